@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the routed MoE FFN step (Q4_0 / Q4_1 experts).
+
+Shared by the tests, the smoke check and the benchmark; used to feed BOTH the
+HIP library and the CPU oracle.  It holds no arithmetic of the method: it only
+draws random tensors and packs random numbers into the GGUF block byte layout.
+
+Workload shapes follow the three diskformer engine pages (Flint: H 2048, 256
+experts top-6, ff 512, shared ff 1024, Q4_1; LFM2.5-24B-A2B: H 2048, 64
+experts top-4 with a selection bias, ff 1536, Q4_0; Ling 3.0 flash: H 2560,
+512 experts in 8 groups, 4 groups kept, top-8, ff 768 + shared 768, weights
+scale 2.5) plus a tiny layer.  Distributions (the pages give none):
+  x ~ N(0, 1) f32;  router ~ N(0, 0.05) f32;  bias ~ N(0, 0.1) f32;
+  Q4 block scales d (and Q4_1 offsets m) ~ U(0.001, 0.02) rounded to f16
+  (round to nearest even);  nibbles i.i.d. uniform over 0..15.
+Every tensor has its own torch.Generator seeded from a hash of
+(master seed, workload, layer, tensor name), so any tensor of any layer can
+be regenerated alone, on the CPU or on the GPU (same generator family per
+device; the oracle always receives copies of the exact tensors the GPU used).
+"""
+import dataclasses
+import hashlib
+
+import torch
+
+Q4_0, Q4_1 = 0, 1
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    hidden: int
+    n_experts: int
+    top_k: int
+    expert_ff: int
+    shared_ff: int = 0
+    qtype: int = Q4_1
+    n_groups: int = 1
+    groups_used: int = 1
+    weights_scale: float = 1.0
+    has_bias: bool = False
+    tokens: int = 1
+    layers: int = 1
+    # distributions
+    router_std: float = 0.05
+    bias_std: float = 0.1
+    scale_lo: float = 0.001
+    scale_hi: float = 0.02
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 256, 8, 2, 128, 0, Q4_1, tokens=1, layers=1),
+    "flint": Workload("flint", 2048, 256, 6, 512, 1024, Q4_1, tokens=1, layers=47),
+    "flint8": Workload("flint8", 2048, 256, 6, 512, 1024, Q4_1, tokens=8, layers=47),
+    "lfm25": Workload("lfm25", 2048, 64, 4, 1536, 0, Q4_0, has_bias=True, tokens=1, layers=38),
+    "ling": Workload("ling", 2560, 512, 8, 768, 768, Q4_1, n_groups=8, groups_used=4, weights_scale=2.5,
+                     has_bias=True, tokens=1, layers=1),
+    "prefill": Workload("prefill", 2048, 256, 6, 512, 1024, Q4_1, tokens=512, layers=1),
+}
+
+
+def seed_for(master, workload, layer, tensor):
+    h = hashlib.blake2b(f"{master}/{workload}/{layer}/{tensor}".encode(), digest_size=8).digest()
+    return int.from_bytes(h, "little") & ((1 << 63) - 1)
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal(shape, std, device, seed):
+    t = torch.randn(shape, generator=_gen(device, seed), device=device, dtype=torch.float32)
+    return t * std if std != 1.0 else t
+
+
+def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24):
+    """n_blocks random GGUF blocks as a uint8 tensor [n_blocks, 18|20].
+
+    Byte layout: f16 d (little endian), for Q4_1 also f16 m, then 16 bytes of
+    nibbles.  d, m ~ U(lo, hi) rounded to f16; nibble bytes uniform 0..255."""
+    bs = BLOCK_BYTES[qtype]
+    out = torch.empty((n_blocks, bs), dtype=torch.uint8, device=device)
+    g = _gen(device, seed)
+    for s in range(0, n_blocks, chunk):
+        n = min(chunk, n_blocks - s)
+        o = out[s:s + n]
+        d = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo).to(torch.float16)
+        o[:, 0:2] = d.view(torch.uint8).view(n, 2)
+        q0 = 2
+        if qtype == Q4_1:
+            m = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo).to(torch.float16)
+            o[:, 2:4] = m.view(torch.uint8).view(n, 2)
+            q0 = 4
+        o[:, q0:] = torch.randint(0, 256, (n, 16), generator=g, device=device, dtype=torch.uint8)
+    return out
+
+
+def expert_tensor(n_experts, rows, cols, qtype, device, seed, wl=None):
+    """E experts of `rows` rows, each a row of cols/32 blocks: uint8 [E, rows, cols/32*bs]."""
+    nb = cols // 32
+    lo, hi = (wl.scale_lo, wl.scale_hi) if wl else (0.001, 0.02)
+    b = q4_blocks(n_experts * rows * nb, qtype, device, seed, lo, hi)
+    return b.view(n_experts, rows, nb * BLOCK_BYTES[qtype])
+
+
+def make_layer(wl, layer=0, device="cpu", master=0):
+    """All weights of one MoE layer of workload `wl`, on `device`."""
+    H, E, F, SF = wl.hidden, wl.n_experts, wl.expert_ff, wl.shared_ff
+    s = lambda name: seed_for(master, wl.name, layer, name)
+    w = {
+        "router_w": normal((E, H), wl.router_std, device, s("router_w")),
+        "bias": normal((E,), wl.bias_std, device, s("bias")) if wl.has_bias else None,
+        "gate_exps": expert_tensor(E, F, H, wl.qtype, device, s("gate_exps"), wl),
+        "up_exps": expert_tensor(E, F, H, wl.qtype, device, s("up_exps"), wl),
+        "down_exps": expert_tensor(E, H, F, wl.qtype, device, s("down_exps"), wl),
+        "gate_sh": None, "up_sh": None, "down_sh": None,
+    }
+    if SF:
+        w["gate_sh"] = expert_tensor(1, SF, H, wl.qtype, device, s("gate_sh"), wl)[0]
+        w["up_sh"] = expert_tensor(1, SF, H, wl.qtype, device, s("up_sh"), wl)[0]
+        w["down_sh"] = expert_tensor(1, H, SF, wl.qtype, device, s("down_sh"), wl)[0]
+    return w
+
+
+def make_x(wl, tokens=None, layer=0, step=0, device="cpu", master=0):
+    """FFN input (already normalised by the caller's RMSNorm): [T, H] ~ N(0, 1)."""
+    T = wl.tokens if tokens is None else tokens
+    return normal((T, wl.hidden), 1.0, device, seed_for(master, wl.name, layer, f"x/{step}/{T}"))
+
+
+def layer_weight_bytes(wl):
+    """Resident bytes of one layer (router + bias + all experts + shared)."""
+    bs = BLOCK_BYTES[wl.qtype]
+    H, E, F, SF = wl.hidden, wl.n_experts, wl.expert_ff, wl.shared_ff
+    per_exp = 3 * F * (H // 32) * bs
+    return E * H * 4 + (E * 4 if wl.has_bias else 0) + E * per_exp + 3 * SF * (H // 32) * bs
+
+
+def to_numpy(w):
+    return {k: (None if v is None else v.detach().cpu().numpy()) for k, v in w.items()}
