@@ -1,0 +1,143 @@
+/*
+ * moe_q4.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts FFN step
+ * with GGUF Q4_0 / Q4_1 experts.
+ *
+ * The layer these calls compute is the MoE FFN of the three diskformer engine
+ * pages (Flint: diskformer 0.5.4->0.6.4 engines/flint_moe_ssd.js, file header;
+ * Ling 3.0 flash: diskformer 0.5.3->0.6.4 engines/ling_moe_ssd.js, file header
+ * and the routeLing / swiglu / moeAccum kernels; LFM2.5: diskformer
+ * 0.5.4->0.6.6 engines/lfm2_moe_ssd.js, file header and the router comment
+ * with TOPK_SIG_BODY and moeAccumB).  For each token t with FFN input x_t
+ * (already RMS-normalised by the caller):
+ *
+ *   l_e   = sum_h Wr[e][h] x_t[h]                    router logits (F32 router)
+ *   p_e   = 1 / (1 + exp(-l_e)),  s_e = p_e + b_e    sigmoid; bias b selects only
+ *   [groups] keep the groups_used groups whose two largest s sum highest
+ *   ids   = the top_k experts by s (lowest index wins ties), in pick order
+ *   w_j   = p_{id_j} / max(sum_j p_{id_j}, wsum_min) * weights_scale
+ *   resid_t += sum_j w_j * FFN_{id_j}(x_t) + FFN_shared(x_t)
+ *   FFN(x) = Wd * (silu(Wg x) * (Wu x)),  silu(g) = g / (1 + exp(-g))
+ *
+ * Numerics.  Router logits accumulate in double and are rounded to f32; the
+ * sigmoid of that f32 logit is evaluated in double and rounded to f32; scores,
+ * group sums, comparisons and weights are f32 as on the pages.  Expert GEMVs
+ * dequantise Q4 in registers and accumulate in f32.  Outputs are bitwise
+ * reproducible run to run (no floating-point atomics).
+ *
+ * Conventions for every call:
+ *   - every pointer is a DEVICE pointer unless stated; all work is enqueued on
+ *     `stream` and the call returns without synchronising;
+ *   - the caller owns every buffer; the library allocates nothing and keeps no
+ *     pointer after returning; calls are reentrant for distinct workspaces;
+ *   - f32 arrays and Q4 tensors must be 16-byte aligned; rows of Q4 tensors
+ *     are whole blocks, consecutive (Q4_1 rows stay 4-byte aligned, Q4_0 rows
+ *     may be 2-byte aligned, which the kernels handle);
+ *   - T = 0 is a no-op returning MOE_OK;
+ *   - on any error nothing is enqueued and moe_last_error() describes it;
+ *     faults of the kernels themselves surface at the caller's next sync.
+ */
+#ifndef MOE_Q4_H
+#define MOE_Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *moe_stream_t; /* a hipStream_t; NULL = default stream */
+
+enum { MOE_Q4_0 = 0, MOE_Q4_1 = 1 };
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* a configuration/shape rule below, or a NULL required pointer */
+  MOE_EALIGN = -2,     /* a pointer is not 16-byte aligned */
+  MOE_EWORKSPACE = -3, /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ELAUNCH = -4     /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Layer shape.  Limits (the pages cap E at 512 and k at 32):
+ *   hidden H:      32 <= H <= 8192, H % 32 == 0
+ *   n_experts E:   1 <= E <= 512
+ *   top_k k:       1 <= k <= min(32, E)
+ *   n_groups G:    1 <= G <= 64, E % G == 0, E/G >= 2 when G > 1
+ *   groups_used:   1 <= Gu <= G, k <= Gu * (E/G); Gu == G means no group limit
+ *   expert_ff F:   32 <= F <= 8192, F % 32 == 0
+ *   shared_ff SF:  0 (no shared expert) or 32 <= SF <= 8192, SF % 32 == 0
+ *   qtype:         MOE_Q4_0 or MOE_Q4_1 (routed and shared experts alike)
+ *   weights_scale: finite, > 0 (1 for Flint and LFM2.5, 2.5 for Ling)
+ *   wsum_min:      finite, > 0 (2^-14 = 6.103515625e-5 on all three pages)   */
+typedef struct {
+  int32_t hidden, n_experts, top_k;
+  int32_t n_groups, groups_used;
+  int32_t expert_ff, shared_ff;
+  int32_t qtype;
+  float weights_scale;
+  float wsum_min;
+} moe_config;
+
+/* Weights of one MoE layer (GGUF tensor names in brackets).  Block tensors
+ * hold Q4 blocks: Q4_1 = 20 bytes (f16 d, f16 m, 16 nibble bytes; value
+ * d*q + m), Q4_0 = 18 bytes (f16 d, 16 nibble bytes; value d*(q-8)); byte i of
+ * the nibbles holds element i (low nibble) and element i+16 (high nibble). */
+typedef struct {
+  const float *router_w;      /* [E][H] f32                          (ffn_gate_inp)     */
+  const float *router_bias;   /* [E] f32, selection only; NULL = none (exp_probs_b)     */
+  const uint8_t *gate_exps;   /* [E][F][H/32] blocks                 (ffn_gate_exps)    */
+  const uint8_t *up_exps;     /* [E][F][H/32] blocks                 (ffn_up_exps)      */
+  const uint8_t *down_exps;   /* [E][H][F/32] blocks                 (ffn_down_exps)    */
+  const uint8_t *gate_shexp;  /* [SF][H/32] blocks, NULL iff SF == 0 (ffn_gate_shexp)   */
+  const uint8_t *up_shexp;    /* [SF][H/32] blocks, NULL iff SF == 0 (ffn_up_shexp)     */
+  const uint8_t *down_shexp;  /* [H][SF/32] blocks, NULL iff SF == 0 (ffn_down_shexp)   */
+} moe_layer_weights;
+
+/* Bytes of device workspace the calls below need for T tokens (16-byte
+ * aligned, contents need not be initialised, not kept between calls).
+ * Returns 0 for an invalid configuration or T < 0. */
+size_t moe_workspace_bytes(const moe_config *cfg, int32_t T);
+
+/* Router scoring and top-k selection for T tokens (the lfm2_moe_ssd.js page's
+ * router comment and TOPK_SIG_BODY; group-limited selection from the
+ * ling_moe_ssd.js page's routeLing).
+ *   x:         [T][H] f32 FFN input (ignored when logits_in != NULL)
+ *   logits_in: NULL = compute logits from router_w and x; else [T][E] f32
+ *              logits used as given (selection-only path)
+ *   ids:       [T][k] int32 out, pick order (descending score, lowest index
+ *              first on ties)
+ *   weights:   [T][k] f32 out, aligned with ids
+ * router_w may be NULL when logits_in is given. */
+int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                    const float *logits_in, int32_t *ids, float *weights, void *workspace,
+                    size_t workspace_bytes, moe_stream_t stream);
+
+/* Expert FFNs for given routing: resid[t] += sum_j weights[t][j] *
+ * FFN_{ids[t][j]}(x_t) + FFN_shared(x_t) (the ling_moe_ssd.js page's swiglu
+ * and moeAccum; the lfm2_moe_ssd.js page's moeAccumB and shared-expert
+ * addInPlace).  ids must be in [0, E) (not checked on the device; out-of-range
+ * ids read out-of-bounds weights).  resid [T][H] f32 in/out, must not alias x.
+ * Small T (decode) runs fused dequant-GEMV kernels; large T (chunked prefill)
+ * groups the (token, pick) pairs by expert and runs per-expert MFMA GEMMs. */
+int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                      const int32_t *ids, const float *weights, float *resid, void *workspace,
+                      size_t workspace_bytes, moe_stream_t stream);
+
+/* The whole step: moe_router_topk then moe_expert_ffn_q4 on the same
+ * workspace.  ids_out / weights_out ([T][k]) are optional (NULL = keep in the
+ * workspace). */
+int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                   float *resid, int32_t *ids_out, float *weights_out, void *workspace,
+                   size_t workspace_bytes, moe_stream_t stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Largest T that takes the decode (GEMV) path; larger T takes the grouped
+ * GEMM path. */
+int32_t moe_decode_max_tokens(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_Q4_H */

@@ -1,0 +1,176 @@
+"""Python binding of libmoe_q4.so: the routed MoE FFN step with Q4_0 / Q4_1
+experts on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+(include/moe_q4.h).  torch supplies device memory (tensor.data_ptr()) and the
+current HIP stream.  There is no fallback: if the built library is missing,
+load_library() raises.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
+
+MOE_Q4_0, MOE_Q4_1 = 0, 1
+WSUM_MIN = 6.103515625e-5  # 2^-14
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+class MoeConfig(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("n_groups", C.c_int32), ("groups_used", C.c_int32),
+                ("expert_ff", C.c_int32), ("shared_ff", C.c_int32), ("qtype", C.c_int32),
+                ("weights_scale", C.c_float), ("wsum_min", C.c_float)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("router_w", "router_bias", "gate_exps", "up_exps", "down_exps",
+                                          "gate_shexp", "up_shexp", "down_shexp")]
+
+
+def load_library(path=LIB_PATH):
+    """Load the built HIP library; raises if it is missing (no CPU fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is not built: run __graft_entry__.build() "
+                                f"(or python sparse_moe_ffn_topk_amd/build.py) first")
+    L = C.CDLL(path)
+    P, S = C.c_void_p, C.c_size_t
+    L.moe_workspace_bytes.restype = S
+    L.moe_workspace_bytes.argtypes = [C.POINTER(MoeConfig), C.c_int32]
+    L.moe_router_topk.restype = C.c_int
+    L.moe_router_topk.argtypes = [C.POINTER(MoeConfig), C.POINTER(LayerWeights), P, C.c_int32, P, P, P, P, S, P]
+    L.moe_expert_ffn_q4.restype = C.c_int
+    L.moe_expert_ffn_q4.argtypes = [C.POINTER(MoeConfig), C.POINTER(LayerWeights), P, C.c_int32, P, P, P, P, S, P]
+    L.moe_layer_step.restype = C.c_int
+    L.moe_layer_step.argtypes = [C.POINTER(MoeConfig), C.POINTER(LayerWeights), P, C.c_int32, P, P, P, P, S, P]
+    L.moe_last_error.restype = C.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_decode_max_tokens.restype = C.c_int32
+    L.moe_decode_max_tokens.argtypes = []
+    _lib = L
+    return L
+
+
+EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
+            "moe_decode_max_tokens")
+
+
+def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,
+                weights_scale=1.0, wsum_min=WSUM_MIN):
+    return MoeConfig(hidden, n_experts, top_k, n_groups, n_groups if groups_used is None else groups_used,
+                     expert_ff, shared_ff, qtype, weights_scale, wsum_min)
+
+
+def config_for(wl):
+    """MoeConfig of a moe_synth.Workload-like object."""
+    return make_config(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
+                       wl.groups_used, wl.weights_scale)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def layer_weights(w):
+    """LayerWeights from a dict of device tensors (keys as moe_synth.make_layer)."""
+    import torch
+    _check(w.get("router_w"), "router_w", torch.float32)
+    _check(w.get("bias"), "bias", torch.float32)
+    for n in ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh"):
+        _check(w.get(n), n, torch.uint8)
+    return LayerWeights(*[None if w.get(n) is None else w[n].data_ptr()
+                          for n in ("router_w", "bias", "gate_exps", "up_exps", "down_exps",
+                                    "gate_sh", "up_sh", "down_sh")])
+
+
+def _raise(rc):
+    if rc != 0:
+        raise MoeError(rc, load_library().moe_last_error().decode())
+
+
+def workspace_bytes(cfg, T):
+    return load_library().moe_workspace_bytes(C.byref(cfg), T)
+
+
+def alloc_workspace(cfg, T, device="cuda"):
+    import torch
+    n = workspace_bytes(cfg, T)
+    if n == 0:
+        raise MoeError(-1, "invalid configuration")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def router_topk(cfg, w, x, logits_in=None, ids=None, weights=None, workspace=None, stream=None, lw=None):
+    import torch
+    T = (logits_in if x is None else x).shape[0]
+    dev = (logits_in if x is None else x).device
+    _check(x, "x", torch.float32)
+    _check(logits_in, "logits_in", torch.float32)
+    if ids is None:
+        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, T, dev)
+    lw = lw if lw is not None else layer_weights(w)
+    _raise(load_library().moe_router_topk(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(logits_in), _ptr(ids),
+                                          _ptr(weights), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return ids, weights
+
+
+def expert_ffn_q4(cfg, w, x, ids, weights, resid, workspace=None, stream=None, lw=None):
+    import torch
+    T = x.shape[0]
+    _check(x, "x", torch.float32)
+    _check(ids, "ids", torch.int32)
+    _check(weights, "weights", torch.float32)
+    _check(resid, "resid", torch.float32)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, T, x.device)
+    lw = lw if lw is not None else layer_weights(w)
+    _raise(load_library().moe_expert_ffn_q4(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(ids), _ptr(weights),
+                                            _ptr(resid), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return resid
+
+
+def layer_step(cfg, w, x, resid, ids_out=None, weights_out=None, workspace=None, stream=None, lw=None):
+    import torch
+    T = x.shape[0]
+    _check(x, "x", torch.float32)
+    _check(resid, "resid", torch.float32)
+    _check(ids_out, "ids_out", torch.int32)
+    _check(weights_out, "weights_out", torch.float32)
+    if workspace is None:
+        workspace = alloc_workspace(cfg, T, x.device)
+    lw = lw if lw is not None else layer_weights(w)
+    _raise(load_library().moe_layer_step(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
+                                         _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return resid

@@ -1,0 +1,235 @@
+// abi.hip -- the C ABI of the MoE step: argument checks, workspace layout and
+// kernel sequencing on the caller's stream.  Nothing here allocates device
+// memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include <string>
+
+#include "../../include/moe_q4.h"
+#include "moe_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+constexpr int kDecodeMaxT = 8;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace regions (byte offsets, each 256-byte aligned).
+struct Layout {
+  size_t logits, ids, wts, act, total;
+};
+
+Layout layout(const moe_config &c, int32_t T) {
+  Layout L;
+  size_t o = 0;
+  L.logits = o;
+  o += up256((size_t)T * c.n_experts * 4);
+  L.ids = o;
+  o += up256((size_t)T * c.top_k * 4);
+  L.wts = o;
+  o += up256((size_t)T * c.top_k * 4);
+  L.act = o;
+  o += up256(((size_t)T * c.top_k * c.expert_ff + (size_t)T * c.shared_ff) * 4);
+  L.total = o;
+  return L;
+}
+
+int check_cfg(const moe_config *c) {
+  if (!c) return fail(MOE_EINVAL, "cfg is NULL");
+  const int H = c->hidden, E = c->n_experts, k = c->top_k, G = c->n_groups, Gu = c->groups_used;
+  if (H < 32 || H > 8192 || H % 32) return fail(MOE_EINVAL, "hidden %d: need 32 <= H <= 8192, H %% 32 == 0", H);
+  if (E < 1 || E > 512) return fail(MOE_EINVAL, "n_experts %d: need 1..512", E);
+  if (k < 1 || k > 32 || k > E) return fail(MOE_EINVAL, "top_k %d: need 1 <= k <= min(32, E=%d)", k, E);
+  if (G < 1 || G > 64 || E % G) return fail(MOE_EINVAL, "n_groups %d: need 1..64 dividing E=%d", G, E);
+  if (G > 1 && E / G < 2) return fail(MOE_EINVAL, "groups of %d experts: need >= 2 per group", E / G);
+  if (Gu < 1 || Gu > G) return fail(MOE_EINVAL, "groups_used %d: need 1..G=%d", Gu, G);
+  if ((long)k > (long)Gu * (E / G)) return fail(MOE_EINVAL, "top_k %d exceeds the experts of %d kept groups", k, Gu);
+  if (c->expert_ff < 32 || c->expert_ff > 8192 || c->expert_ff % 32)
+    return fail(MOE_EINVAL, "expert_ff %d: need 32 <= F <= 8192, F %% 32 == 0", c->expert_ff);
+  if (c->shared_ff != 0 && (c->shared_ff < 32 || c->shared_ff > 8192 || c->shared_ff % 32))
+    return fail(MOE_EINVAL, "shared_ff %d: need 0 or 32 <= SF <= 8192, SF %% 32 == 0", c->shared_ff);
+  if (c->qtype != MOE_Q4_0 && c->qtype != MOE_Q4_1) return fail(MOE_EINVAL, "qtype %d: need 0 or 1", c->qtype);
+  if (!(std::isfinite(c->weights_scale) && c->weights_scale > 0))
+    return fail(MOE_EINVAL, "weights_scale must be finite and > 0");
+  if (!(std::isfinite(c->wsum_min) && c->wsum_min > 0)) return fail(MOE_EINVAL, "wsum_min must be finite and > 0");
+  return MOE_OK;
+}
+
+int check_ptr(const void *p, const char *name, bool required) {
+  if (!p) return required ? fail(MOE_EINVAL, "%s is NULL", name) : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+int check_ws(const moe_config &c, int32_t T, void *ws, size_t bytes) {
+  size_t need = layout(c, T).total;
+  if (!ws) return fail(MOE_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(ws)) return fail(MOE_EALIGN, "workspace is not 16-byte aligned");
+  if (bytes < need) return fail(MOE_EWORKSPACE, "workspace has %zu bytes, need %zu", bytes, need);
+  return MOE_OK;
+}
+
+int check_expert_ptrs(const moe_config &c, const moe_layer_weights *w) {
+  int rc;
+  if ((rc = check_ptr(w->gate_exps, "gate_exps", true))) return rc;
+  if ((rc = check_ptr(w->up_exps, "up_exps", true))) return rc;
+  if ((rc = check_ptr(w->down_exps, "down_exps", true))) return rc;
+  const bool sh = c.shared_ff > 0;
+  if ((rc = check_ptr(w->gate_shexp, "gate_shexp", sh))) return rc;
+  if ((rc = check_ptr(w->up_shexp, "up_shexp", sh))) return rc;
+  if ((rc = check_ptr(w->down_shexp, "down_shexp", sh))) return rc;
+  return MOE_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MOE_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int router_topk_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T,
+                     const float *logits_in, int32_t *ids, float *wts, void *ws, hipStream_t st) {
+  const Layout L = layout(c, T);
+  const float *logits = logits_in;
+  if (!logits_in) {
+    float *lg = (float *)((char *)ws + L.logits);
+    int rc = launched(moe::launch_router_logits(w->router_w, x, c.hidden, c.n_experts, T, lg, st), "router logits");
+    if (rc) return rc;
+    logits = lg;
+  }
+  return launched(moe::launch_select(logits, w->router_bias, T, c.n_experts, c.top_k, c.n_groups, c.groups_used,
+                                     c.weights_scale, c.wsum_min, ids, wts, st),
+                  "top-k select");
+}
+
+int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T,
+                    const int32_t *ids, const float *wts, float *resid, void *ws, hipStream_t st) {
+  const Layout L = layout(c, T);
+  moe::DecodeArgs a;
+  a.qtype = c.qtype;
+  a.T = T;
+  a.H = c.hidden;
+  a.k = c.top_k;
+  a.F = c.expert_ff;
+  a.SF = c.shared_ff;
+  a.x = x;
+  a.ids = ids;
+  a.wts = wts;
+  a.gate_exps = w->gate_exps;
+  a.up_exps = w->up_exps;
+  a.down_exps = w->down_exps;
+  a.gate_sh = w->gate_shexp;
+  a.up_sh = w->up_shexp;
+  a.down_sh = w->down_shexp;
+  a.act = (float *)((char *)ws + L.act);
+  a.resid = resid;
+  return launched(moe::launch_decode_ffn(a, st), "decode expert FFN");
+}
+
+int check_ffn_shape(const moe_config &c) {
+  if (moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) > 65536)
+    return fail(MOE_EINVAL, "top_k*expert_ff + shared_ff = %d exceeds the down kernel's LDS staging (14336)",
+                c.top_k * c.expert_ff + c.shared_ff);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config *cfg, int32_t T) {
+  if (T < 0 || check_cfg(cfg) != MOE_OK) return 0;
+  return layout(*cfg, T).total;
+}
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+int32_t moe_decode_max_tokens(void) { return kDecodeMaxT; }
+
+int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                    const float *logits_in, int32_t *ids, float *weights, void *workspace, size_t workspace_bytes,
+                    moe_stream_t stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if (T == 0) return MOE_OK;
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if ((rc = check_ptr(logits_in, "logits_in", false))) return rc;
+  if (!logits_in) {
+    if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
+    if ((rc = check_ptr(x, "x", true))) return rc;
+  }
+  if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
+  if ((rc = check_ptr(ids, "ids", true))) return rc;
+  if ((rc = check_ptr(weights, "weights", true))) return rc;
+  if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
+  return router_topk_impl(*cfg, w, x, T, logits_in, ids, weights, workspace, (hipStream_t)stream);
+}
+
+int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                      const int32_t *ids, const float *weights, float *resid, void *workspace,
+                      size_t workspace_bytes, moe_stream_t stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if (T == 0) return MOE_OK;
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if ((rc = check_ffn_shape(*cfg))) return rc;
+  if ((rc = check_expert_ptrs(*cfg, w))) return rc;
+  if ((rc = check_ptr(x, "x", true))) return rc;
+  if ((rc = check_ptr(ids, "ids", true))) return rc;
+  if ((rc = check_ptr(weights, "weights", true))) return rc;
+  if ((rc = check_ptr(resid, "resid", true))) return rc;
+  if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
+  if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
+  return expert_ffn_impl(*cfg, w, x, T, ids, weights, resid, workspace, (hipStream_t)stream);
+}
+
+int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T, float *resid,
+                   int32_t *ids_out, float *weights_out, void *workspace, size_t workspace_bytes,
+                   moe_stream_t stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if (T == 0) return MOE_OK;
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  if ((rc = check_ffn_shape(*cfg))) return rc;
+  if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
+  if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
+  if ((rc = check_expert_ptrs(*cfg, w))) return rc;
+  if ((rc = check_ptr(x, "x", true))) return rc;
+  if ((rc = check_ptr(resid, "resid", true))) return rc;
+  if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
+  if ((rc = check_ptr(ids_out, "ids_out", false))) return rc;
+  if ((rc = check_ptr(weights_out, "weights_out", false))) return rc;
+  if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
+  const Layout L = layout(*cfg, T);
+  int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
+  float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = router_topk_impl(*cfg, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
+  return expert_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
+}
+
+}  // extern "C"

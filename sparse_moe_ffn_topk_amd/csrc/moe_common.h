@@ -1,0 +1,141 @@
+// moe_common.h -- device helpers shared by the gfx950 kernels of the MoE step.
+//
+// Q4 blocks (GGUF): Q4_1 = f16 d, f16 m, 16 nibble bytes (20 B, value d*q+m);
+// Q4_0 = f16 d, 16 nibble bytes (18 B, value d*(q-8)).  Nibble byte i holds
+// element i in its low half and element i+16 in its high half (block layout of
+// the diskformer flint_moe_ssd.js page, file header and Q41DOT comment).
+//
+// A block's dot with 32 inputs is d*sum(q x) + m*sum(x) (the same page's
+// q41dot identity); Q4_0 is the case m = -8d.  The per-block input sum is
+// computed once per input vector and kept in LDS beside the inputs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_Q4_0 0
+#define MOE_Q4_1 1
+
+// Dword 3 of a raw buffer resource on gfx9-family parts (gfx950 included):
+// 32-bit data format, no swizzle, no stride; out-of-range loads return 0.
+#define MOE_RSRC_WORD3 0x00020000
+
+namespace moe {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  // Sizes are rounded up to whole dwords: a dword holding the last byte of an
+  // allocation never crosses a page, and Q4_0 loads read 4-byte-aligned words.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)((bytes + 3u) & ~3u),
+                                           MOE_RSRC_WORD3);
+}
+
+template <int QT> struct QBlock;
+
+// Five dwords of a block as loaded: w[0] carries the f16 scale (and offset),
+// the nibble words are extracted by nib().
+struct Raw5 {
+  uint32_t w[5];
+};
+
+template <> struct QBlock<MOE_Q4_1> {
+  static constexpr int bytes = 20;
+  // Block at byte offset `off` (4-byte aligned: rows of 20-byte blocks).
+  static __device__ __forceinline__ Raw5 load(rsrc_t r, uint32_t off) {
+    Raw5 b;
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    b.w[0] = v.x; b.w[1] = v.y; b.w[2] = v.z; b.w[3] = v.w;
+    b.w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 16), 0, 0);
+    return b;
+  }
+  static __device__ __forceinline__ void scales(const Raw5 &b, uint32_t, float &d, float &m) {
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)(b.w[0] & 0xffffu));
+    m = (float)__builtin_bit_cast(_Float16, (uint16_t)(b.w[0] >> 16));
+  }
+  static __device__ __forceinline__ uint32_t nib(const Raw5 &b, uint32_t, int k) { return b.w[1 + k]; }
+};
+
+template <> struct QBlock<MOE_Q4_0> {
+  static constexpr int bytes = 18;
+  // Block at byte offset `off` (2-byte aligned): five dwords from the dword
+  // boundary at or below it, realigned in registers.
+  static __device__ __forceinline__ Raw5 load(rsrc_t r, uint32_t off) {
+    uint32_t a = off & ~3u;
+    Raw5 b;
+    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)a, 0, 0);
+    b.w[0] = v.x; b.w[1] = v.y; b.w[2] = v.z; b.w[3] = v.w;
+    b.w[4] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(a + 16), 0, 0);
+    return b;
+  }
+  static __device__ __forceinline__ void scales(const Raw5 &b, uint32_t off, float &d, float &m) {
+    uint16_t db = (off & 2u) ? (uint16_t)(b.w[0] >> 16) : (uint16_t)(b.w[0] & 0xffffu);
+    d = (float)__builtin_bit_cast(_Float16, db);
+    m = -8.0f * d;
+  }
+  // Nibble word k = block bytes 2+4k .. 5+4k.
+  static __device__ __forceinline__ uint32_t nib(const Raw5 &b, uint32_t off, int k) {
+    return (off & 2u) ? b.w[1 + k] : __builtin_amdgcn_alignbyte(b.w[1 + k], b.w[k], 2);
+  }
+};
+
+// sum over one nibble word's 8 elements of q*x: low nibbles pair with
+// x[4k..4k+3], high nibbles with x[16+4k..16+4k+3].  The high nibbles are
+// masked in place (value 16q) and their partial is scaled by 1/16 at the end.
+__device__ __forceinline__ void nib_word_dot(uint32_t w, const float4 &xl, const float4 &xh, float &lo,
+                                             float &hi) {
+  uint32_t l = w & 0x0F0F0F0Fu, h = w & 0xF0F0F0F0u;
+  lo = __builtin_fmaf((float)(l & 0xff), xl.x, lo);
+  lo = __builtin_fmaf((float)((l >> 8) & 0xff), xl.y, lo);
+  lo = __builtin_fmaf((float)((l >> 16) & 0xff), xl.z, lo);
+  lo = __builtin_fmaf((float)(l >> 24), xl.w, lo);
+  hi = __builtin_fmaf((float)(h & 0xff), xh.x, hi);
+  hi = __builtin_fmaf((float)((h >> 8) & 0xff), xh.y, hi);
+  hi = __builtin_fmaf((float)((h >> 16) & 0xff), xh.z, hi);
+  hi = __builtin_fmaf((float)(h >> 24), xh.w, hi);
+}
+
+// Dot of one loaded block with its 32 inputs xb (LDS) and their sum sx.
+template <int QT>
+__device__ __forceinline__ float block_dot(const Raw5 &b, uint32_t off, const float *xb, float sx) {
+  float d, m;
+  QBlock<QT>::scales(b, off, d, m);
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    float4 xl = *reinterpret_cast<const float4 *>(xb + 4 * k);
+    float4 xh = *reinterpret_cast<const float4 *>(xb + 16 + 4 * k);
+    nib_word_dot(QBlock<QT>::nib(b, off, k), xl, xh, lo, hi);
+  }
+  float q = __builtin_fmaf(hi, 0.0625f, lo);
+  return __builtin_fmaf(d, q, m * sx);
+}
+
+// Same dot with the 32 inputs given as 8 float4 already in registers.
+template <int QT>
+__device__ __forceinline__ float block_dot_regs(const Raw5 &b, uint32_t off, const float4 *x8, float sx) {
+  float d, m;
+  QBlock<QT>::scales(b, off, d, m);
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; k++) nib_word_dot(QBlock<QT>::nib(b, off, k), x8[k], x8[4 + k], lo, hi);
+  float q = __builtin_fmaf(hi, 0.0625f, lo);
+  return __builtin_fmaf(d, q, m * sx);
+}
+
+// LDS layout of an input vector: block b's 32 floats at b*XSTRIDE (36 floats:
+// a 16-byte pad per block spreads a lane group's 128-bit reads over the banks).
+constexpr int XSTRIDE = 36;
+
+// Sum over `width` consecutive lanes (width a power of two <= 64); every lane
+// of the group receives the total.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ double group_sum_d(double v, int width) {
+  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,32 @@
+// moe_launch.h -- host-side launchers of the MoE kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router logits [T][E] f32 from W [E][H] and x [T][H] (f64 accumulation).
+hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
+                                hipStream_t st);
+
+// Scores, optional group limit, top-k, weights; one wave per token.
+hipError_t launch_select(const float *logits, const float *bias, int T, int E, int k, int G, int Gu,
+                         float scale, float wsum_min, int32_t *ids, float *wts, hipStream_t st);
+
+struct DecodeArgs {
+  int qtype, T, H, k, F, SF;
+  const float *x;
+  const int32_t *ids;
+  const float *wts;
+  const uint8_t *gate_exps, *up_exps, *down_exps;
+  const uint8_t *gate_sh, *up_sh, *down_sh;
+  float *act;    // [T*k][F] then [T][SF]
+  float *resid;  // [T][H] in/out
+};
+
+// gate||up + SwiGLU, then down + weighted per-token accumulate.
+hipError_t launch_decode_ffn(const DecodeArgs &a, hipStream_t st);
+size_t decode_down_lds_bytes(int k, int F, int SF);
+
+}  // namespace moe

@@ -1,0 +1,101 @@
+"""Helpers shared by the GPU parity tests: input placement, oracle runs on
+copies of the exact device inputs, and the parity measures.
+
+Tolerance (per token row, on the FFN delta or the composed residual):
+    ||y_gpu - y_oracle||_inf / ||y_oracle||_inf <= 1e-3
+(f32 accumulation on the GPU against the oracle's f64).  Selected expert ids
+must match bit-exact, except where the oracle certifies a near-tie: the two
+disputed experts' f64 selection scores differ by less than TIE_TAU.
+"""
+import numpy as np
+import torch
+
+import moe_synth as S
+import oracle as O
+
+REL_TOL = 1e-3
+TIE_TAU = 1e-6
+
+
+def oracle_cfg(wl):
+    return O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
+                      wl.groups_used, wl.weights_scale)
+
+
+def to_device(w, device="cuda"):
+    return {k: (None if v is None else v.to(device).contiguous()) for k, v in w.items()}
+
+
+def row_rel_err(got, ref):
+    """Per-row max-norm relative error."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return num / np.maximum(den, 1e-300)
+
+
+def scores64(wnp, x_t, bias):
+    l = O.router_logits(wnp["router_w"], x_t)
+    p = 1.0 / (1.0 + np.exp(-l))
+    return p + (0.0 if bias is None else bias.astype(np.float64))
+
+
+def check_ids(wl, wnp, x, ids_gpu, ids_ref):
+    """Return the list of tokens whose ids differ; assert each is a certified near-tie."""
+    bad = []
+    for t in range(ids_ref.shape[0]):
+        if np.array_equal(ids_gpu[t], ids_ref[t]):
+            continue
+        s = scores64(wnp, x[t], wnp.get("bias"))
+        a, b = set(ids_gpu[t].tolist()), set(ids_ref[t].tolist())
+        disputed = sorted(a ^ b) if a != b else [int(i) for i, j in zip(ids_gpu[t], ids_ref[t]) if i != j]
+        gap = max(s[disputed]) - min(s[disputed])
+        assert gap < TIE_TAU, f"token {t}: ids {ids_gpu[t]} vs oracle {ids_ref[t]} (score gap {gap:.3g})"
+        bad.append(t)
+    return bad
+
+
+def oracle_given_routing(wl, wnp, x_t, ids, wts, resid_t=None):
+    """Oracle FFN output of one token for forced ids / weights (used for certified near-ties)."""
+    H, F, SF = wl.hidden, wl.expert_ff, wl.shared_ff
+    out = np.zeros(H) if resid_t is None else resid_t.astype(np.float64).copy()
+    xd = x_t.astype(np.float64)
+    for e, wj in zip(ids, wts):
+        out += float(wj) * O.expert_ffn(wl.qtype, wnp["gate_exps"][e], wnp["up_exps"][e], wnp["down_exps"][e],
+                                        H, F, xd)
+    if SF:
+        out += O.expert_ffn(wl.qtype, wnp["gate_sh"], wnp["up_sh"], wnp["down_sh"], H, SF, xd)
+    return out
+
+
+def run_layer_parity(wl, w_dev, x_dev, resid_dev=None, wnp=None, sample=None):
+    """Run moe_layer_step on the device and the oracle on the same inputs.
+    Returns (max row rel err, n near-ties)."""
+    import sparse_moe_ffn_topk_amd as moe
+    cfg = moe.config_for(wl)
+    T = x_dev.shape[0]
+    resid_in = torch.zeros_like(x_dev) if resid_dev is None else resid_dev.clone()
+    out = resid_in.clone()
+    ids = torch.empty((T, wl.top_k), dtype=torch.int32, device=x_dev.device)
+    wts = torch.empty((T, wl.top_k), dtype=torch.float32, device=x_dev.device)
+    moe.layer_step(cfg, w_dev, x_dev, out, ids, wts)
+    torch.cuda.synchronize()
+    if wnp is None:
+        wnp = S.to_numpy(w_dev)
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    x = x_dev.cpu().numpy()[rows]
+    r = resid_in.cpu().numpy()[rows]
+    ref, ids_ref, w_ref = O.layer(oracle_cfg(wl), wnp, x, r)
+    ids_g = ids.cpu().numpy()[rows]
+    wts_g = wts.cpu().numpy()[rows]
+    got = out.cpu().numpy()[rows]
+    ties = check_ids(wl, wnp, x, ids_g, ids_ref)
+    for t in ties:  # compare outputs under the GPU's own (certified) routing
+        ref[t] = oracle_given_routing(wl, wnp, x[t], ids_g[t], wts_g[t], r[t])
+    ok = [t for t in range(len(rows)) if t not in ties]
+    if ok:
+        assert np.allclose(wts_g[ok], w_ref[ok], rtol=2e-6, atol=1e-7), "routing weights differ"
+    # delta parity: compare FFN contributions, not the residual they ride on
+    err = row_rel_err(got - r, ref - r)
+    return float(err.max()), len(ties)

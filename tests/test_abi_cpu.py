@@ -1,0 +1,110 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the public
+header declares, and rejects invalid arguments before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import sparse_moe_ffn_topk_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.load_library()
+    decl = _declared_symbols()
+    assert set(decl) >= {"moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step",
+                         "moe_last_error"}
+    for n in decl:
+        assert hasattr(L, n), n
+    assert set(moe.EXPORTED) == set(decl)
+
+
+def test_struct_layouts_match_header():
+    assert C.sizeof(moe.MoeConfig) == 10 * 4
+    assert C.sizeof(moe.LayerWeights) == 8 * 8
+
+
+def _cfg(**kw):
+    base = dict(hidden=256, n_experts=8, top_k=2, expert_ff=128)
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(hidden=100), "hidden"), (dict(hidden=0), "hidden"), (dict(hidden=16384), "hidden"),
+    (dict(n_experts=0), "n_experts"), (dict(n_experts=513), "n_experts"),
+    (dict(top_k=0), "top_k"), (dict(top_k=9), "top_k"), (dict(n_experts=64, top_k=33), "top_k"),
+    (dict(n_groups=3), "n_groups"), (dict(n_experts=8, n_groups=8), "groups of"),
+    (dict(n_groups=4, groups_used=5), "groups_used"), (dict(n_groups=4, groups_used=0), "groups_used"),
+    (dict(top_k=5, n_groups=4, groups_used=2), "exceeds"),
+    (dict(expert_ff=100), "expert_ff"), (dict(shared_ff=16), "shared_ff"),
+    (dict(qtype=2), "qtype"), (dict(weights_scale=0.0), "weights_scale"), (dict(wsum_min=-1.0), "wsum_min"),
+])
+def test_invalid_config_rejected(kw, msg):
+    L = moe.load_library()
+    cfg = _cfg(**kw)
+    assert L.moe_workspace_bytes(C.byref(cfg), 1) == 0
+    lw = moe.LayerWeights(*([0x1000] * 8))
+    rc = L.moe_layer_step(C.byref(cfg), C.byref(lw), C.c_void_p(0x1000), 1, C.c_void_p(0x2000), None, None,
+                          C.c_void_p(0x3000), 1 << 30, None)
+    assert rc == -1
+    assert msg in L.moe_last_error().decode()
+
+
+def test_workspace_bytes_grows_with_tokens():
+    L = moe.load_library()
+    cfg = _cfg(shared_ff=64)
+    a, b = L.moe_workspace_bytes(C.byref(cfg), 1), L.moe_workspace_bytes(C.byref(cfg), 8)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    assert L.moe_workspace_bytes(C.byref(cfg), -1) == 0
+
+
+def test_pointer_errors_are_reported_without_launching():
+    L = moe.load_library()
+    cfg = _cfg()
+    ws = L.moe_workspace_bytes(C.byref(cfg), 2)
+    good = [0x10000] * 8
+    good[1] = 0  # no bias
+    good[5] = good[6] = good[7] = 0  # no shared expert
+    lw = moe.LayerWeights(*good)
+    x, r, w = C.c_void_p(0x20000), C.c_void_p(0x30000), C.c_void_p(0x40000)
+    # NULL x
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), None, 2, r, None, None, w, ws, None) == -1
+    # misaligned resid
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), x, 2, C.c_void_p(0x30004), None, None, w, ws, None) == -2
+    # resid aliases x
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), x, 2, x, None, None, w, ws, None) == -1
+    # workspace too small / NULL
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), x, 2, r, None, None, w, ws - 1, None) == -3
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), x, 2, r, None, None, None, ws, None) == -3
+    # shared expert pointers missing when shared_ff > 0
+    cfg2 = _cfg(shared_ff=64)
+    ws2 = L.moe_workspace_bytes(C.byref(cfg2), 2)
+    assert L.moe_layer_step(C.byref(cfg2), C.byref(lw), x, 2, r, None, None, w, ws2, None) == -1
+    assert "gate_shexp" in L.moe_last_error().decode()
+    # T = 0 is a no-op that succeeds without a workspace
+    assert L.moe_layer_step(C.byref(cfg), C.byref(lw), x, 0, r, None, None, None, 0, None) == 0
+    assert L.moe_last_error().decode() == ""
+    # negative T
+    assert L.moe_router_topk(C.byref(cfg), C.byref(lw), x, -1, None, w, w, w, ws, None) == -1
+
+
+def test_decode_down_staging_limit_reported():
+    L = moe.load_library()
+    cfg = moe.make_config(1024, 64, 32, 512)  # k*F = 16384 > 14336
+    lw = moe.LayerWeights(*([0x10000] * 5 + [0] * 3))
+    rc = L.moe_expert_ffn_q4(C.byref(cfg), C.byref(lw), C.c_void_p(0x20000), 1, C.c_void_p(0x20000),
+                             C.c_void_p(0x20000), C.c_void_p(0x30000), C.c_void_p(0x40000), 1 << 30, None)
+    assert rc == -1 and "LDS" in L.moe_last_error().decode()

@@ -1,0 +1,197 @@
+"""GPU parity of the HIP path (called through the C ABI) against the f64 oracle.
+
+Each case prints what names it before the GPU work so a failing run can be
+traced from its output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as S
+import oracle as O
+from moe_testlib import REL_TOL, oracle_cfg, row_rel_err, run_layer_parity, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _layer(wl, seed=0, tokens=None, step=0):
+    w = S.make_layer(wl, layer=seed, device="cpu")
+    x = S.make_x(wl, tokens=tokens, layer=seed, step=step, device="cpu")
+    return w, x
+
+
+# ----------------------------------------------------------- selection only --
+
+SEL_CASES = {
+    "tiny": dict(E=8, k=2),
+    "flint": dict(E=256, k=6),
+    "lfm25": dict(E=64, k=4, bias=True),
+    "ling": dict(E=512, k=8, G=8, Gu=4, bias=True, scale=2.5),
+    "k_eq_E": dict(E=16, k=16),
+    "groups_all_used": dict(E=128, k=8, G=8, Gu=8),
+    "max": dict(E=512, k=32, G=64, Gu=7, bias=True),
+    "odd_E": dict(E=97, k=5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEL_CASES))
+def test_select_from_given_logits_bit_exact(gpu, name):
+    moe = gpu
+    c = SEL_CASES[name]
+    E, k, G, Gu = c["E"], c["k"], c.get("G", 1), c.get("Gu", c.get("G", 1))
+    T = 37
+    _say("select", name, f"E={E} k={k} G={G} Gu={Gu} T={T}")
+    g = torch.Generator().manual_seed(1000 + E + k)
+    logits = (torch.randn((T, E), generator=g) * 2.5).float()
+    logits[3] = 0.7  # a token with all-equal logits: pure index tie-break
+    logits[4, : E // 2] = -30.0  # part of the table deep in the clamp region
+    logits[5] = -30.0  # every sigmoid tiny: the weight-sum clamp applies
+    bias = (torch.randn(E, generator=g) * 0.1).float() if c.get("bias") else None
+    cfg = moe.make_config(64, E, k, 32, n_groups=G, groups_used=Gu, weights_scale=c.get("scale", 1.0))
+    w = {"router_w": None, "bias": None if bias is None else bias.cuda()}
+    ids, wts = moe.router_topk(cfg, w, None, logits_in=logits.cuda())
+    ids, wts = ids.cpu().numpy(), wts.cpu().numpy()
+    ocfg = O.make_cfg(64, E, k, 32, n_groups=G, groups_used=Gu, weights_scale=c.get("scale", 1.0))
+    for t in range(T):
+        rid, rw = O.route(ocfg, logits[t].numpy(), bias=None if bias is None else bias.numpy())
+        assert list(ids[t]) == list(rid), f"token {t}"
+        assert np.allclose(wts[t], rw, rtol=2e-6, atol=0), f"token {t}"
+
+
+def test_select_clamp_and_scale_exact(gpu):
+    moe = gpu
+    _say("select clamp ling")
+    logits = torch.full((2, 512), -30.0)
+    cfg = moe.make_config(64, 512, 8, 32, n_groups=8, groups_used=4, weights_scale=2.5)
+    ids, wts = moe.router_topk(cfg, {"router_w": None, "bias": None}, None, logits_in=logits.cuda())
+    assert ids.cpu().tolist() == [list(range(8))] * 2
+    p32 = np.float32(1.0 / (1.0 + np.exp(30.0)))
+    want = np.float32(p32 / np.float32(2.0 ** -14) * np.float32(2.5))
+    assert np.all(wts.cpu().numpy() == want)
+
+
+# ------------------------------------------------------------- whole layer --
+
+LAYER_CASES = ["tiny", "flint", "flint8", "lfm25", "ling"]
+
+
+@pytest.mark.parametrize("name", LAYER_CASES)
+@pytest.mark.parametrize("composed", [False, True])
+def test_layer_step_parity(gpu, name, composed):
+    wl = S.WORKLOADS[name]
+    T = wl.tokens
+    _say("layer", name, f"T={T} composed={composed}")
+    w, x = _layer(wl, seed=3)
+    wd, xd = to_device(w), x.cuda()
+    resid = xd.clone() if composed else None
+    err, ties = run_layer_parity(wl, wd, xd, resid, wnp=S.to_numpy(w))
+    print(f"[result] {name} composed={composed} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 13, 40])
+def test_layer_token_counts_ragged(gpu, T):
+    wl = S.Workload("ragged", 96 * 2, 24, 3, 160, 96, S.Q4_1, has_bias=True)
+    _say("ragged T", T)
+    w, x = _layer(wl, seed=T, tokens=T)
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("H,F,SF", [(96, 96, 0), (96, 160, 96), (288, 32, 64), (2080, 224, 0)])
+def test_layer_q4_0_unaligned_rows(gpu, H, F, SF):
+    # odd block counts give Q4_0 rows at 2-byte alignment
+    wl = S.Workload("q40odd", H, 16, 3, F, SF, S.Q4_0, has_bias=True)
+    _say("q4_0 odd rows", H, F, SF)
+    w, x = _layer(wl, seed=H + F, tokens=3)
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    assert err <= REL_TOL
+
+
+def test_layer_single_expert_and_k_equals_E(gpu):
+    for E, k in ((1, 1), (6, 6)):
+        wl = S.Workload("kE", 128, E, k, 64, 32, S.Q4_1)
+        _say("k=E", E)
+        w, x = _layer(wl, seed=E, tokens=4)
+        err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+        assert err <= REL_TOL
+
+
+def test_layer_all_tokens_on_one_expert(gpu):
+    wl = S.Workload("one", 256, 32, 2, 64, 0, S.Q4_1, has_bias=True)
+    _say("all tokens on one expert")
+    w, x = _layer(wl, seed=9, tokens=8)
+    w["bias"] = torch.zeros(32)
+    w["bias"][[5, 17]] = 10.0  # bias forces experts 5 and 17 for every token
+    wd = to_device(w)
+    err, _ = run_layer_parity(wl, wd, x.cuda(), wnp=S.to_numpy(w))
+    assert err <= REL_TOL
+
+
+def test_layer_large_shape(gpu):
+    # the ABI maxima for H and E with every group kept by a limit
+    wl = S.Workload("big", 8192, 512, 32, 64, 128, S.Q4_1, n_groups=64, groups_used=8, weights_scale=1.5,
+                    has_bias=True)
+    _say("large H=8192 E=512 k=32")
+    w, x = _layer(wl, seed=1, tokens=2)
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    assert err <= REL_TOL
+
+
+def test_expert_ffn_zero_offsets_give_exact_zero(gpu):
+    # Q4_0 blocks with every nibble 8 contribute exactly zero, bitwise on the GPU too
+    moe = gpu
+    wl = S.Workload("zero", 256, 8, 2, 64, 64, S.Q4_0)
+    _say("q4_0 midpoint nibbles")
+    w, x = _layer(wl, seed=2, tokens=3)
+    for n in ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh"):
+        w[n].view(-1, 18)[:, 2:] = 0x88
+    wd, xd = to_device(w), x.cuda()
+    resid = torch.randn(3, 256, device="cuda")
+    out = resid.clone()
+    moe.layer_step(moe.config_for(wl), wd, xd, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, resid)
+
+
+def test_determinism_and_token_independence(gpu):
+    moe = gpu
+    wl = S.WORKLOADS["flint8"]
+    _say("determinism flint8")
+    w, x = _layer(wl, seed=4)
+    wd, xd = to_device(w), x.cuda()
+    cfg = moe.config_for(wl)
+    outs = []
+    for _ in range(2):
+        o = torch.zeros_like(xd)
+        moe.layer_step(cfg, wd, xd, o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for t in range(xd.shape[0]):
+        o1 = torch.zeros_like(xd[t:t + 1])
+        moe.layer_step(cfg, wd, xd[t:t + 1].contiguous(), o1)
+        torch.cuda.synchronize()
+        err = row_rel_err(o1.cpu().numpy(), outs[0][t:t + 1].cpu().numpy())
+        assert err.max() <= 1e-6
+
+
+def test_split_calls_equal_layer_step(gpu):
+    moe = gpu
+    wl = S.WORKLOADS["ling"]
+    _say("router_topk + expert_ffn_q4 == layer_step")
+    w, x = _layer(wl, seed=5)
+    wd, xd = to_device(w), x.cuda()
+    cfg = moe.config_for(wl)
+    a = torch.zeros_like(xd)
+    ids, wts = torch.empty((1, 8), dtype=torch.int32, device="cuda"), torch.empty((1, 8), device="cuda")
+    moe.layer_step(cfg, wd, xd, a, ids, wts)
+    ids2, wts2 = moe.router_topk(cfg, wd, xd)
+    b = torch.zeros_like(xd)
+    moe.expert_ffn_q4(cfg, wd, xd, ids2, wts2, b)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(wts, wts2) and torch.equal(a, b)
