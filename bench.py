@@ -1,0 +1,229 @@
+#!/usr/bin/env python
+"""Benchmark of the routed MoE FFN step (Q4 experts) on one MI355X.
+
+Default workload: the Flint-shaped decode stack -- H 2048, 256 experts top-6
+by sigmoid, SwiGLU experts ff 512 plus an always-on shared expert ff 1024, all
+Q4_1, batch 1, 47 distinct MoE layers resident in HBM (23.9 GB).  One step =
+one decode token through all 47 layers: router logits, top-k, gate||up +
+SwiGLU, down + weighted residual accumulate, per layer, in layer order on one
+stream (each layer's expert reads start after the previous layer finished).
+
+Inputs are synthetic and seeded (moe_synth): x ~ N(0,1) fresh per layer, 16
+pre-generated steps cycled; router N(0, 0.05); Q4 scales U(0.001, 0.02) in f16;
+uniform nibbles.  Weights are generated directly on the GPU.
+
+Timing: each of the 16 step variants is captured once as a HIP graph; W
+warm-up replays, then K timed replays between two synchronisations.  The
+dominant kernel (gate||up + SwiGLU) is then timed launch by launch with HIP
+events on its own stream (library kernel timer, eager launches) to give the
+roofline line.  The CPU baseline times the f64 oracle on a bounded sample.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer decode tokens/s + achieved weight-stream GB/s (% of HBM peak), 1 GPU"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for fn in ("moe_common.h", "ffn_decode.hip"):
+        with open(os.path.join(ROOT, "sparse_moe_ffn_topk_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic per launch of the dominant kernel from committed rocprofv3 counter runs,
+    only if they were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"gateup_swiglu_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="flint", choices=["flint", "flint8", "lfm25", "ling", "tiny"])
+    ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timer", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              f"the multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth as S
+    import sparse_moe_ffn_topk_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.load_library()
+    dev = "cuda"
+    wl = S.WORKLOADS[args.workload]
+    L, T, nS = wl.layers, wl.tokens, args.slots
+    if wl.name == "ling":
+        L = 28  # one layer's distinct shape; 28 generated copies exceed the 256 MB MALL 4x over
+    cfg = moe.config_for(wl)
+    bs = S.BLOCK_BYTES[wl.qtype]
+    per_expert = 3 * wl.expert_ff * (wl.hidden // 32) * bs
+    shared_bytes = 3 * wl.shared_ff * (wl.hidden // 32) * bs
+    router_bytes = wl.n_experts * wl.hidden * 4 + (wl.n_experts * 4 if wl.has_bias else 0)
+
+    t0 = time.time()
+    log(f"workload {wl.name}: H={wl.hidden} E={wl.n_experts} k={wl.top_k} F={wl.expert_ff} SF={wl.shared_ff} "
+        f"qtype=Q4_{wl.qtype} T={T} layers={L}; generating weights on the GPU")
+    layers, lws = [], []
+    for l in range(L):
+        w = S.make_layer(wl, layer=l, device=dev)
+        layers.append(w)
+        lws.append(moe.layer_weights(w))
+        if l % 8 == 7:
+            log(f"  {l + 1}/{L} layers generated")
+    torch.cuda.synchronize()
+    resident = sum(sum(t.numel() * t.element_size() for t in w.values() if t is not None) for w in layers)
+    log(f"weights resident: {resident / 1e9:.2f} GB in {time.time() - t0:.1f}s")
+
+    xs = [[S.make_x(wl, T, layer=l, step=s, device=dev) for l in range(L)] for s in range(nS)]
+    resid = torch.zeros((T, wl.hidden), dtype=torch.float32, device=dev)
+    ws = moe.alloc_workspace(cfg, T, dev)
+    ids = [[torch.empty((T, wl.top_k), dtype=torch.int32, device=dev) for _ in range(L)] for _ in range(nS)]
+    wts = [[torch.empty((T, wl.top_k), dtype=torch.float32, device=dev) for _ in range(L)] for _ in range(nS)]
+
+    def step(s):
+        for l in range(L):
+            moe.layer_step(cfg, None, xs[s][l], resid, ids[s][l], wts[s][l], ws, lw=lws[l])
+
+    # eager pass over every variant (loads code objects, fills ids for the byte model)
+    for s in range(nS):
+        step(s)
+    torch.cuda.synchronize()
+    graphs = []
+    for s in range(nS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(s)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    log(f"captured {nS} graphs of {L} layer steps ({4 * L} kernels each)")
+
+    # algorithmic weight bytes per step variant: router + bias + distinct picked experts + shared
+    distinct = np.zeros((nS, L))
+    for s in range(nS):
+        for l in range(L):
+            distinct[s, l] = len(np.unique(ids[s][l].cpu().numpy()))
+    step_bytes = [float(L * (router_bytes + shared_bytes) + distinct[s].sum() * per_expert) for s in range(nS)]
+
+    for i in range(args.warmup):
+        graphs[i % nS].replay()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        graphs[i % nS].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    mean_bytes = sum(step_bytes[i % nS] for i in range(args.steps)) / args.steps
+    tok_s = T / (ms_step / 1e3)
+    gbps = mean_bytes / (ms_step / 1e3) / 1e9
+    log(f"timed: {ms_step * 1e3:.1f} us/step ({ms_step * 1e3 / L:.2f} us/layer), {tok_s:.1f} tok/s, "
+        f"{gbps:.1f} GB/s of weights ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s); wall {wall:.3f}s")
+
+    # per-kernel durations, launch by launch, HIP events on the launch stream (eager)
+    kstats = {}
+    if not args.no_kernel_timer:
+        nk = min(20, max(4, args.steps // 10))
+        for name, kid in (("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT),
+                          ("gateup_swiglu", moe.KERNEL_GATEUP), ("down_accum", moe.KERNEL_DOWN)):
+            with moe.KernelTimer(kid, nk * L) as kt:
+                for i in range(nk):
+                    step(i % nS)
+            kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us}
+        log("kernel means (us): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
+
+    roofline = None
+    if "gateup_swiglu" in kstats:
+        # algorithmic bytes of one gate||up launch: distinct picked experts' gate and up rows, the shared
+        # expert's gate and up rows, x read once per token, act written once
+        gu_expert = 2 * wl.expert_ff * (wl.hidden // 32) * bs
+        gu_shared = 2 * wl.shared_ff * (wl.hidden // 32) * bs
+        nk = kstats["gateup_swiglu"]["launches"] // L
+        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(nk)]))
+        act_bytes = T * (wl.top_k * wl.expert_ff + wl.shared_ff) * 4 + T * wl.hidden * 4
+        per_launch = d_mean * gu_expert + gu_shared + act_bytes
+        ach = per_launch / (kstats["gateup_swiglu"]["mean_us"] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_gateup_swiglu", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": load_traffic(wl.name),
+                    "algorithmic_bytes_per_launch": int(per_launch),
+                    "mean_launch_us": round(kstats["gateup_swiglu"]["mean_us"], 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        nl = min(3, L)
+        host = [S.to_numpy(layers[l]) for l in range(nl)]
+        xh = [xs[0][l].cpu().numpy() for l in range(nl)]
+        ocfg = O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
+                          wl.groups_used, wl.weights_scale)
+        log(f"cpu baseline: f64 oracle, 1 thread, ~{args.cpu_seconds:.0f}s")
+        n, c0 = 0, time.perf_counter()
+        while n < nl or time.perf_counter() - c0 < args.cpu_seconds:
+            O.layer(ocfg, host[n % nl], xh[n % nl])
+            n += 1
+        per_layer = (time.perf_counter() - c0) / n
+        cpu = {"value": round(T / (per_layer * L), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} oracle layer-steps (T={T}) cycling {nl} of the {L} generated layers, "
+                         f"{per_layer * 1e3:.1f} ms each, scaled to the {L}-layer stack"}
+        log(f"cpu baseline: {per_layer * 1e3:.1f} ms per layer-step -> {cpu['value']} tok/s")
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}_T{T}_{L}layers", "hidden": wl.hidden, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "expert_ff": wl.expert_ff, "shared_ff": wl.shared_ff,
+                   "qtype": f"Q4_{wl.qtype}", "tokens": T, "layers": L, "global_batch": T,
+                   "parallelism": "single-gpu"},
+        "weight_stream_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "us_per_layer": round(ms_step * 1e3 / L, 3), "tok_s_per_layer": round(tok_s * L, 1),
+        "weight_bytes_per_step": int(mean_bytes), "kernels_us": {k: round(v["mean_us"], 3) for k, v in kstats.items()},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -137,6 +137,22 @@ const char *moe_last_error(void);
  * GEMM path. */
 int32_t moe_decode_max_tokens(void);
 
+/* Diagnostics: time launches of one kernel with HIP events recorded on the
+ * stream each launch goes to (process-wide, not thread-safe; for benchmarks).
+ * moe_kernel_timer_begin creates `capacity` event pairs and arms the timer
+ * for `kernel`; every later launch of that kernel is bracketed until the
+ * capacity is used.  moe_kernel_timer_end waits for the recorded events,
+ * returns the number of timed launches in *count and the sum of their
+ * durations in *total_ms, and releases the events. */
+enum {
+  MOE_KERNEL_ROUTER = 1,  /* router logits                              */
+  MOE_KERNEL_SELECT = 2,  /* scores, group limit, top-k, weights         */
+  MOE_KERNEL_GATEUP = 3,  /* gate||up GEMV + SwiGLU (decode)             */
+  MOE_KERNEL_DOWN = 4     /* down GEMV + weighted accumulate (decode)    */
+};
+int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
+int moe_kernel_timer_end(int32_t *count, double *total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,12 +58,17 @@ def load_library(path=LIB_PATH):
     L.moe_last_error.argtypes = []
     L.moe_decode_max_tokens.restype = C.c_int32
     L.moe_decode_max_tokens.argtypes = []
+    L.moe_kernel_timer_begin.restype = C.c_int
+    L.moe_kernel_timer_begin.argtypes = [C.c_int32, C.c_int32]
+    L.moe_kernel_timer_end.restype = C.c_int
+    L.moe_kernel_timer_end.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_double)]
     _lib = L
     return L
 
 
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
-            "moe_decode_max_tokens")
+            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end")
+KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
 
 
 def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,
@@ -174,3 +179,26 @@ def layer_step(cfg, w, x, resid, ids_out=None, weights_out=None, workspace=None,
     _raise(load_library().moe_layer_step(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
                                          _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return resid
+
+
+class KernelTimer:
+    """Times every launch of one kernel with HIP events on its own stream (diagnostics)."""
+
+    def __init__(self, kernel, capacity):
+        self.kernel, self.capacity = kernel, capacity
+
+    def __enter__(self):
+        _raise(load_library().moe_kernel_timer_begin(self.kernel, self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        n, ms = C.c_int32(0), C.c_double(0.0)
+        rc = load_library().moe_kernel_timer_end(C.byref(n), C.byref(ms))
+        self.count, self.total_ms = n.value, ms.value
+        if exc[0] is None:
+            _raise(rc)
+        return False
+
+    @property
+    def mean_us(self):
+        return 1000.0 * self.total_ms / max(self.count, 1)

@@ -120,8 +120,10 @@ int router_topk_impl(const moe_config &c, const moe_layer_weights *w, const floa
                   "top-k select");
 }
 
-int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T,
-                    const int32_t *ids, const float *wts, float *resid, void *ws, hipStream_t st) {
+// Expert FFNs.  With logits != NULL (decode path of moe_layer_step) the
+// gate||up kernel routes each token itself and writes ids / wts.
+int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, int32_t *ids,
+                    float *wts, const float *logits, float *resid, void *ws, hipStream_t st) {
   const Layout L = layout(c, T);
   moe::DecodeArgs a;
   a.qtype = c.qtype;
@@ -133,6 +135,9 @@ int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float
   a.x = x;
   a.ids = ids;
   a.wts = wts;
+  a.logits = logits;
+  a.bias = w->router_bias;
+  a.sel = moe::SelParams{c.n_experts, c.top_k, c.n_groups, c.groups_used, c.weights_scale, c.wsum_min};
   a.gate_exps = w->gate_exps;
   a.up_exps = w->up_exps;
   a.down_exps = w->down_exps;
@@ -144,6 +149,12 @@ int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float
   return launched(moe::launch_decode_ffn(a, st), "decode expert FFN");
 }
 
+int check_tokens(const moe_config &c, int32_t T) {
+  if ((long)T * (c.top_k + 1) > 65535)
+    return fail(MOE_EINVAL, "T*(top_k+1) = %ld exceeds 65535 (split the tokens into chunks)", (long)T * (c.top_k + 1));
+  return MOE_OK;
+}
+
 int check_ffn_shape(const moe_config &c) {
   if (moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) > 65536)
     return fail(MOE_EINVAL, "top_k*expert_ff + shared_ff = %d exceeds the down kernel's LDS staging (14336)",
@@ -151,9 +162,69 @@ int check_ffn_shape(const moe_config &c) {
   return MOE_OK;
 }
 
+// ---- kernel timer (diagnostics) ----
+struct Timer {
+  int kernel = 0, capacity = 0, count = 0;
+  hipEvent_t *start = nullptr, *stop = nullptr;
+} g_timer;
+
 }  // namespace
 
+namespace moe {
+void timer_before(int id, hipStream_t st) {
+  if (g_timer.kernel == id && g_timer.count < g_timer.capacity) (void)hipEventRecord(g_timer.start[g_timer.count], st);
+}
+void timer_after(int id, hipStream_t st) {
+  if (g_timer.kernel == id && g_timer.count < g_timer.capacity) (void)hipEventRecord(g_timer.stop[g_timer.count++], st);
+}
+}  // namespace moe
+
 extern "C" {
+
+int moe_kernel_timer_end(int32_t *count, double *total_ms);
+
+int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
+  g_err.clear();
+  if (g_timer.kernel) moe_kernel_timer_end(nullptr, nullptr);
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_DOWN || capacity < 1 || capacity > (1 << 20))
+    return fail(MOE_EINVAL, "kernel timer: bad kernel %d or capacity %d", kernel, capacity);
+  g_timer.start = new hipEvent_t[capacity];
+  g_timer.stop = new hipEvent_t[capacity];
+  for (int i = 0; i < capacity; i++) {
+    if (hipEventCreate(&g_timer.start[i]) != hipSuccess || hipEventCreate(&g_timer.stop[i]) != hipSuccess) {
+      g_timer.capacity = i;
+      moe_kernel_timer_end(nullptr, nullptr);
+      return fail(MOE_ELAUNCH, "kernel timer: hipEventCreate failed");
+    }
+  }
+  g_timer.kernel = kernel;
+  g_timer.capacity = capacity;
+  g_timer.count = 0;
+  return MOE_OK;
+}
+
+int moe_kernel_timer_end(int32_t *count, double *total_ms) {
+  double total = 0.0;
+  int n = g_timer.count, rc = MOE_OK;
+  for (int i = 0; i < n; i++) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_timer.stop[i]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_timer.start[i], g_timer.stop[i]) != hipSuccess)
+      rc = fail(MOE_ELAUNCH, "kernel timer: event %d not measurable", i);
+    total += ms;
+  }
+  for (int i = 0; i < g_timer.capacity; i++) {
+    (void)hipEventDestroy(g_timer.start[i]);
+    (void)hipEventDestroy(g_timer.stop[i]);
+  }
+  delete[] g_timer.start;
+  delete[] g_timer.stop;
+  g_timer = Timer();
+  if (count) *count = n;
+  if (total_ms) *total_ms = total;
+  return rc;
+}
+
 
 size_t moe_workspace_bytes(const moe_config *cfg, int32_t T) {
   if (T < 0 || check_cfg(cfg) != MOE_OK) return 0;
@@ -195,6 +266,7 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_ffn_shape(*cfg))) return rc;
+  if ((rc = check_tokens(*cfg, T))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
   if ((rc = check_ptr(ids, "ids", true))) return rc;
@@ -202,7 +274,8 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if ((rc = check_ptr(resid, "resid", true))) return rc;
   if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
-  return expert_ffn_impl(*cfg, w, x, T, ids, weights, resid, workspace, (hipStream_t)stream);
+  return expert_ffn_impl(*cfg, w, x, T, const_cast<int32_t *>(ids), const_cast<float *>(weights), nullptr, resid,
+                         workspace, (hipStream_t)stream);
 }
 
 int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T, float *resid,
@@ -215,6 +288,7 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_ffn_shape(*cfg))) return rc;
+  if ((rc = check_tokens(*cfg, T))) return rc;
   if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
   if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
@@ -228,8 +302,16 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
   float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
   hipStream_t st = (hipStream_t)stream;
+  if (T <= kDecodeMaxT) {
+    // decode: router logits, then the gate||up kernel routes in its prologue
+    float *lg = (float *)((char *)workspace + L.logits);
+    if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st),
+                       "router logits")))
+      return rc;
+    return expert_ffn_impl(*cfg, w, x, T, ids, wts, lg, resid, workspace, st);
+  }
   if ((rc = router_topk_impl(*cfg, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
-  return expert_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
+  return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
 }
 
 }  // extern "C"

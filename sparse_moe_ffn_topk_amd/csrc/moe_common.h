@@ -127,15 +127,47 @@ __device__ __forceinline__ float block_dot_regs(const Raw5 &b, uint32_t off, con
 // a 16-byte pad per block spreads a lane group's 128-bit reads over the banks).
 constexpr int XSTRIDE = 36;
 
-// Sum over `width` consecutive lanes (width a power of two <= 64); every lane
-// of the group receives the total.
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
+// DPP lane moves (gfx9 encodings): row_shr:n moves each lane's value n lanes
+// up within its row of 16; with bound_ctrl the first n lanes read 0.
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, true);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (long long)(unsigned)lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __builtin_bit_cast(long long, v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __builtin_bit_cast(double, ((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 16):
+// the LAST lane of each group (lane % W == W-1) receives the group total.
+template <int W>
+__device__ __forceinline__ float group_sum_last(float v) {
+  if constexpr (W >= 2) v += dpp_f<DPP_ROW_SHR1>(v);
+  if constexpr (W >= 4) v += dpp_f<DPP_ROW_SHR2>(v);
+  if constexpr (W >= 8) v += dpp_f<DPP_ROW_SHR4>(v);
+  if constexpr (W >= 16) v += dpp_f<DPP_ROW_SHR8>(v);
   return v;
 }
-__device__ __forceinline__ double group_sum_d(double v, int width) {
-  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+
+// Sum of a double over the whole wave (row sums, then the four rows in a
+// fixed order); the result is uniform.
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<DPP_ROW_SHR1>(v);
+  v += dpp_d<DPP_ROW_SHR2>(v);
+  v += dpp_d<DPP_ROW_SHR4>(v);
+  v += dpp_d<DPP_ROW_SHR8>(v);
+  return (readlane_d(v, 15) + readlane_d(v, 31)) + (readlane_d(v, 47) + readlane_d(v, 63));
 }
 
 }  // namespace moe

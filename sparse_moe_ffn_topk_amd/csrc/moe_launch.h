@@ -14,19 +14,34 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
 hipError_t launch_select(const float *logits, const float *bias, int T, int E, int k, int G, int Gu,
                          float scale, float wsum_min, int32_t *ids, float *wts, hipStream_t st);
 
+// Routing parameters: experts, top-k, groups, groups kept, weights scale,
+// clamp on the picked-sigmoid sum.
+struct SelParams {
+  int E, k, G, Gu;
+  float scale, wsum_min;
+};
+
 struct DecodeArgs {
   int qtype, T, H, k, F, SF;
   const float *x;
-  const int32_t *ids;
-  const float *wts;
+  int32_t *ids;     // [T][k]: written by the gate||up kernel when logits != NULL, else read
+  float *wts;       // [T][k]: likewise
+  const float *logits;  // [T][E] router logits to route in-kernel, or NULL
+  const float *bias;    // selection bias or NULL
+  SelParams sel;
   const uint8_t *gate_exps, *up_exps, *down_exps;
   const uint8_t *gate_sh, *up_sh, *down_sh;
-  float *act;    // [T*k][F] then [T][SF]
+  float *act;    // per token: [k][F] routed rows, then [SF] shared
   float *resid;  // [T][H] in/out
 };
 
 // gate||up + SwiGLU, then down + weighted per-token accumulate.
 hipError_t launch_decode_ffn(const DecodeArgs &a, hipStream_t st);
 size_t decode_down_lds_bytes(int k, int F, int SF);
+
+// Kernel timer hooks (diagnostics): bracket one launch of kernel `id` with
+// events on `st` when the timer is armed for it.
+void timer_before(int id, hipStream_t st);
+void timer_after(int id, hipStream_t st);
 
 }  // namespace moe
