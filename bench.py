@@ -64,7 +64,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="flint", choices=["flint", "flint8", "lfm25", "ling", "tiny"])
+    ap.add_argument("--workload", default="flint", choices=["flint", "flint8", "lfm25", "ling", "tiny", "prefill"])
     ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -90,7 +90,9 @@ def main():
     wl = S.WORKLOADS[args.workload]
     L, T, nS = wl.layers, wl.tokens, args.slots
     if wl.name == "ling":
-        L = 28  # one layer's distinct shape; 28 generated copies exceed the 256 MB MALL 4x over
+        L = 28  # 28 generated copies of the one layer shape exceed the 256 MB MALL 4x over
+    if wl.name == "prefill":
+        L = 4   # 4 generated layers cycled (509 MB each touched per chunk)
     cfg = moe.config_for(wl)
     bs = S.BLOCK_BYTES[wl.qtype]
     per_expert = 3 * wl.expert_ff * (wl.hidden // 32) * bs
@@ -164,10 +166,15 @@ def main():
 
     # per-kernel durations, launch by launch, HIP events on the launch stream (eager)
     kstats = {}
+    grouped = T > moe.load_library().moe_decode_max_tokens()
     if not args.no_kernel_timer:
         nk = min(20, max(4, args.steps // 10))
-        for name, kid in (("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT),
-                          ("gateup_swiglu", moe.KERNEL_GATEUP), ("down_accum", moe.KERNEL_DOWN)):
+        kernels = ((("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT), ("sort", moe.KERNEL_SORT),
+                    ("group_gateup", moe.KERNEL_GROUP_GATEUP), ("group_down", moe.KERNEL_GROUP_DOWN),
+                    ("combine", moe.KERNEL_COMBINE)) if grouped else
+                   (("router", moe.KERNEL_ROUTER), ("gateup_swiglu", moe.KERNEL_GATEUP),
+                    ("down_accum", moe.KERNEL_DOWN)))
+        for name, kid in kernels:
             with moe.KernelTimer(kid, nk * L) as kt:
                 for i in range(nk):
                     step(i % nS)
@@ -175,6 +182,23 @@ def main():
         log("kernel means (us): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
 
     roofline = None
+    if "group_gateup" in kstats:
+        # grouped gate||up: every distinct expert's gate and up rows once per chunk, the shared expert's,
+        # x read, act written; 2*T*k*F*H*2 + 2*T*SF*H*2 useful MFMA flops alongside
+        gu_expert = 2 * wl.expert_ff * (wl.hidden // 32) * bs
+        gu_shared = 2 * wl.shared_ff * (wl.hidden // 32) * bs
+        nk = kstats["group_gateup"]["launches"] // L
+        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(nk)]))
+        act_bytes = T * (wl.top_k * wl.expert_ff + wl.shared_ff) * 4 + T * wl.hidden * 4
+        per_launch = d_mean * gu_expert + gu_shared + act_bytes
+        us = kstats["group_gateup"]["mean_us"]
+        ach = per_launch / (us * 1e-6) / 1e9
+        flops = 2.0 * 2 * T * (wl.top_k * wl.expert_ff + wl.shared_ff) * wl.hidden
+        roofline = {"bound": "hbm", "kernel": "k_group_gemm<GATEUP>", "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": load_traffic(wl.name), "algorithmic_bytes_per_launch": int(per_launch),
+                    "mean_launch_us": round(us, 3),
+                    "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 2), "mfma_peak_tflops_f16": 2500.0}
     if "gateup_swiglu" in kstats:
         # algorithmic bytes of one gate||up launch: distinct picked experts' gate and up rows, the shared
         # expert's gate and up rows, x read once per token, act written once

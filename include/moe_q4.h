@@ -148,7 +148,11 @@ enum {
   MOE_KERNEL_ROUTER = 1,  /* router logits                              */
   MOE_KERNEL_SELECT = 2,  /* scores, group limit, top-k, weights         */
   MOE_KERNEL_GATEUP = 3,  /* gate||up GEMV + SwiGLU (decode)             */
-  MOE_KERNEL_DOWN = 4     /* down GEMV + weighted accumulate (decode)    */
+  MOE_KERNEL_DOWN = 4,    /* down GEMV + weighted accumulate (decode)    */
+  MOE_KERNEL_SORT = 5,    /* pairs grouped by expert (grouped path)      */
+  MOE_KERNEL_GROUP_GATEUP = 6, /* grouped gate||up MFMA GEMM + SwiGLU     */
+  MOE_KERNEL_GROUP_DOWN = 7,   /* grouped down MFMA GEMM, weighted        */
+  MOE_KERNEL_COMBINE = 8       /* per-token sum into the residual         */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
 int moe_kernel_timer_end(int32_t *count, double *total_ms);

@@ -69,6 +69,7 @@ def load_library(path=LIB_PATH):
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
             "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end")
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
+KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE = 5, 6, 7, 8
 
 
 def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,

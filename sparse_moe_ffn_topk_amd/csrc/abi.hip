@@ -33,22 +33,41 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace regions (byte offsets, each 256-byte aligned).
+// Workspace regions (byte offsets, each 256-byte aligned).  Decode (T <= 8)
+// uses logits/ids/wts/act; the grouped path works on chunks of at most
+// PREFILL_CHUNK tokens and adds the sort results and its act and Y rows.
 struct Layout {
-  size_t logits, ids, wts, act, total;
+  size_t logits, ids, wts, act, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, total;
 };
 
 Layout layout(const moe_config &c, int32_t T) {
   Layout L;
+  const size_t k = c.top_k, E = c.n_experts, F = c.expert_ff, SF = c.shared_ff, H = c.hidden;
+  const size_t Tc = T < moe::PREFILL_CHUNK ? (size_t)T : (size_t)moe::PREFILL_CHUNK;
   size_t o = 0;
-  L.logits = o;
-  o += up256((size_t)T * c.n_experts * 4);
-  L.ids = o;
-  o += up256((size_t)T * c.top_k * 4);
-  L.wts = o;
-  o += up256((size_t)T * c.top_k * 4);
-  L.act = o;
-  o += up256(((size_t)T * c.top_k * c.expert_ff + (size_t)T * c.shared_ff) * 4);
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  L.logits = take((size_t)T * E * 4);
+  L.ids = take((size_t)T * k * 4);
+  L.wts = take((size_t)T * k * 4);
+  L.act = take(((size_t)T * k * F + (size_t)T * SF) * 4);
+  const bool grouped = T > kDecodeMaxT || moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) > 65536;
+  if (grouped) {
+    L.offsets = take((E + 1) * 4);
+    L.pos = take(Tc * k * 4);
+    L.perm = take(Tc * k * 4);
+    L.tiles = take(((Tc * k + 15) / 16 + E) * 2 * 4);
+    L.ntiles = take(4);
+    L.pact = take(Tc * k * F * 4);
+    L.pact_sh = take(Tc * SF * 4);
+    L.Y = take(Tc * k * H * 4);
+    L.Ysh = take(Tc * H * 4);
+  } else {
+    L.offsets = L.pos = L.perm = L.tiles = L.ntiles = L.pact = L.pact_sh = L.Y = L.Ysh = 0;
+  }
   L.total = o;
   return L;
 }
@@ -149,18 +168,49 @@ int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float
   return launched(moe::launch_decode_ffn(a, st), "decode expert FFN");
 }
 
-int check_tokens(const moe_config &c, int32_t T) {
-  if ((long)T * (c.top_k + 1) > 65535)
-    return fail(MOE_EINVAL, "T*(top_k+1) = %ld exceeds 65535 (split the tokens into chunks)", (long)T * (c.top_k + 1));
+// Grouped (prefill) expert FFNs, chunk by chunk of at most PREFILL_CHUNK tokens.
+int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, const int32_t *ids,
+                     const float *wts, float *resid, void *ws, hipStream_t st) {
+  const Layout L = layout(c, T);
+  char *b = (char *)ws;
+  for (int32_t t0 = 0; t0 < T; t0 += moe::PREFILL_CHUNK) {
+    const int32_t Tc = T - t0 < moe::PREFILL_CHUNK ? T - t0 : moe::PREFILL_CHUNK;
+    moe::PrefillArgs p;
+    p.qtype = c.qtype;
+    p.T = Tc;
+    p.H = c.hidden;
+    p.k = c.top_k;
+    p.F = c.expert_ff;
+    p.SF = c.shared_ff;
+    p.E = c.n_experts;
+    p.x = x + (size_t)t0 * c.hidden;
+    p.ids = ids + (size_t)t0 * c.top_k;
+    p.wts = wts + (size_t)t0 * c.top_k;
+    p.gate_exps = w->gate_exps;
+    p.up_exps = w->up_exps;
+    p.down_exps = w->down_exps;
+    p.gate_sh = w->gate_shexp;
+    p.up_sh = w->up_shexp;
+    p.down_sh = w->down_shexp;
+    p.offsets = (int32_t *)(b + L.offsets);
+    p.pos = (int32_t *)(b + L.pos);
+    p.perm = (int32_t *)(b + L.perm);
+    p.tiles = (int32_t *)(b + L.tiles);
+    p.ntiles = (int32_t *)(b + L.ntiles);
+    p.act = (float *)(b + L.pact);
+    p.act_sh = (float *)(b + L.pact_sh);
+    p.Y = (float *)(b + L.Y);
+    p.Ysh = (float *)(b + L.Ysh);
+    p.resid = resid + (size_t)t0 * c.hidden;
+    int rc = launched(moe::launch_prefill_ffn(p, st), "grouped expert FFN");
+    if (rc) return rc;
+  }
   return MOE_OK;
 }
 
-int check_ffn_shape(const moe_config &c) {
-  if (moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) > 65536)
-    return fail(MOE_EINVAL, "top_k*expert_ff + shared_ff = %d exceeds the down kernel's LDS staging (14336)",
-                c.top_k * c.expert_ff + c.shared_ff);
-  return MOE_OK;
-}
+// Decode kernels stage a token's whole act row in LDS; configurations whose
+// row does not fit take the grouped path at any T.
+bool decode_fits(const moe_config &c) { return moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) <= 65536; }
 
 // ---- kernel timer (diagnostics) ----
 struct Timer {
@@ -186,7 +236,7 @@ int moe_kernel_timer_end(int32_t *count, double *total_ms);
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
   g_err.clear();
   if (g_timer.kernel) moe_kernel_timer_end(nullptr, nullptr);
-  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_DOWN || capacity < 1 || capacity > (1 << 20))
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_COMBINE || capacity < 1 || capacity > (1 << 20))
     return fail(MOE_EINVAL, "kernel timer: bad kernel %d or capacity %d", kernel, capacity);
   g_timer.start = new hipEvent_t[capacity];
   g_timer.stop = new hipEvent_t[capacity];
@@ -265,8 +315,6 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
-  if ((rc = check_ffn_shape(*cfg))) return rc;
-  if ((rc = check_tokens(*cfg, T))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
   if ((rc = check_ptr(ids, "ids", true))) return rc;
@@ -274,6 +322,8 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if ((rc = check_ptr(resid, "resid", true))) return rc;
   if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
+  if (T > kDecodeMaxT || !decode_fits(*cfg))
+    return prefill_ffn_impl(*cfg, w, x, T, ids, weights, resid, workspace, (hipStream_t)stream);
   return expert_ffn_impl(*cfg, w, x, T, const_cast<int32_t *>(ids), const_cast<float *>(weights), nullptr, resid,
                          workspace, (hipStream_t)stream);
 }
@@ -287,8 +337,6 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
-  if ((rc = check_ffn_shape(*cfg))) return rc;
-  if ((rc = check_tokens(*cfg, T))) return rc;
   if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
   if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
@@ -302,7 +350,7 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
   float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
   hipStream_t st = (hipStream_t)stream;
-  if (T <= kDecodeMaxT) {
+  if (T <= kDecodeMaxT && decode_fits(*cfg)) {
     // decode: router logits, then the gate||up kernel routes in its prologue
     float *lg = (float *)((char *)workspace + L.logits);
     if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st),
@@ -311,6 +359,7 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
     return expert_ffn_impl(*cfg, w, x, T, ids, wts, lg, resid, workspace, st);
   }
   if ((rc = router_topk_impl(*cfg, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
+  if (T > kDecodeMaxT || !decode_fits(*cfg)) return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
   return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
 }
 

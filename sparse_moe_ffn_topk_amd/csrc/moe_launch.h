@@ -39,6 +39,24 @@ struct DecodeArgs {
 hipError_t launch_decode_ffn(const DecodeArgs &a, hipStream_t st);
 size_t decode_down_lds_bytes(int k, int F, int SF);
 
+// Many tokens (chunked prefill, T <= PREFILL_CHUNK): sort the pairs by expert,
+// grouped MFMA GEMMs, combine.
+constexpr int PREFILL_CHUNK = 512;
+struct PrefillArgs {
+  int qtype, T, H, k, F, SF, E;
+  const float *x;          // [T][H]
+  const int32_t *ids;      // [T][k]
+  const float *wts;        // [T][k]
+  const uint8_t *gate_exps, *up_exps, *down_exps;
+  const uint8_t *gate_sh, *up_sh, *down_sh;
+  int32_t *offsets, *pos, *perm, *tiles, *ntiles;  // sort results
+  float *act, *act_sh;     // [T*k][F] sorted, [T][SF]
+  float *Y, *Ysh;          // [T*k][H] sorted and weighted, [T][H]
+  float *resid;            // [T][H] in/out
+};
+hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
+size_t prefill_sort_lds_bytes(int T, int E);
+
 // Kernel timer hooks (diagnostics): bracket one launch of kernel `id` with
 // events on `st` when the timer is armed for it.
 void timer_before(int id, hipStream_t st);

@@ -1,0 +1,424 @@
+// prefill.hip -- expert FFNs for many tokens (chunked prefill): the (token,
+// pick) pairs are grouped by expert and every expert runs as a small dense
+// GEMM on the MFMA units (gfx950, v_mfma_f32_16x16x32_f16).
+//
+// What is computed is the same MoE FFN as the decode path (swiglu, moeAccum
+// and moeAccumB of the diskformer ling_moe_ssd.js / lfm2_moe_ssd.js pages):
+//   act[p][f] = silu(g) * u,  g = Wg_e x_t,  u = Wu_e x_t     (pair p = (t, j))
+//   resid[t][h] += sum_j w_tj * (Wd_e act_p)[h] + shared(x_t)[h]
+// The pages run one GEMV per (token, pick) pair with no grouping; grouping
+// the pairs by expert is this library's design, so every expert's weights
+// are read once per chunk.
+//
+// Steps:
+//  1. k_sort_by_expert (one block): a stable counting sort of the pairs by
+//     expert, tokens ascending within an expert: per-expert token bit sets,
+//     popcount prefixes, an exclusive scan -> offsets, pos[p], perm[pos], and
+//     the list of 16-token tiles of every expert.
+//  2. k_group_gemm<GATEUP>: per (tile, 256-row slice): g and u for 16 tokens
+//     x 256 rows, SwiGLU in registers, act rows written in sorted order; the
+//     shared expert runs as extra tiles over all tokens.
+//  3. k_group_gemm<DOWN>: Y[pos] = w_p * (Wd_e act_pos), shared Ysh[t].
+//  4. k_combine: resid[t] += sum_j Y[pos(t, j)] + Ysh[t], fixed order: no
+//     atomics, bitwise reproducible.
+//
+// Numerics of the GEMM: a Q4 block's nibbles q are exact in f16, so each
+// block's MFMA partial sum_k q_k x_k is exact up to f32 accumulation once x
+// is split as x = hi + lo (two f16, about 22 significant bits); the block's
+// f32 scale d and offset term m * sum_k x_k are applied per block in f32
+// (value d*q + m; Q4_0 is m = -8d).  The nibbles enter the MFMA as exact f16
+// values: a mask-or builds the f16 1024 + q, a packed f16 subtract removes
+// the 1024.
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ sort --
+
+// One block of 1024 threads; T <= PREFILL_CHUNK, E <= 512.
+// bits[e][w]: bit t%32 of word t/32 set when token t picked e.
+__global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ ids, int T, int k, int E,
+                                                         int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
+                                                         int32_t *__restrict__ perm, int32_t *__restrict__ tiles,
+                                                         int32_t *__restrict__ ntiles) {
+  extern __shared__ uint32_t lds[];
+  const int W = (T + 31) >> 5;
+  uint32_t *bits = lds;                       // [E][W]
+  uint16_t *pre = (uint16_t *)(lds + E * W);  // [E][W] exclusive popcount prefix
+  __shared__ int cnt[512], off[513], toff[513];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * W; i += 1024) bits[i] = 0u;
+  __syncthreads();
+  const int np = T * k;
+  for (int p = tid; p < np; p += 1024) {
+    const int e = ids[p], t = p / k;
+    atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  if (tid < E) {
+    int c = 0;
+    for (int w = 0; w < W; w++) {
+      pre[tid * W + w] = (uint16_t)c;
+      c += __popc(bits[tid * W + w]);
+    }
+    cnt[tid] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, to = 0;
+    for (int e = 0; e < E; e++) {
+      off[e] = o;
+      toff[e] = to;
+      o += cnt[e];
+      to += (cnt[e] + 15) >> 4;
+    }
+    off[E] = o;
+    toff[E] = to;
+    *ntiles = to;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+  if (tid < E) {
+    const int nt = (cnt[tid] + 15) >> 4;
+    for (int i = 0; i < nt; i++) {
+      tiles[2 * (toff[tid] + i)] = tid;
+      tiles[2 * (toff[tid] + i) + 1] = 16 * i;
+    }
+  }
+  for (int p = tid; p < np; p += 1024) {
+    const int e = ids[p], t = p / k;
+    const uint32_t wbits = bits[e * W + (t >> 5)];
+    const int r = pre[e * W + (t >> 5)] + __popc(wbits & ((1u << (t & 31)) - 1u));
+    const int q = off[e] + r;
+    pos[p] = q;
+    perm[q] = p;
+  }
+}
+
+// ------------------------------------------------------------- grouped GEMM --
+
+// Q4 block pieces a lane needs for one MFMA B operand: the f16 scale and
+// offset (as f32) and 8 nibble bytes -- bytes 0..7 or 8..15 of the block's 16.
+template <int QT> struct QPart;
+template <> struct QPart<MOE_Q4_1> {
+  static constexpr int bytes = 20;
+  static __device__ __forceinline__ void load(rsrc_t r, uint32_t off, int half, uint32_t &dm, u32x2 &nb) {
+    dm = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    nb = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 4 + 8 * half), 0, 0);
+  }
+  static __device__ __forceinline__ void scales(uint32_t dm, uint32_t, float &d, float &m) {
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm & 0xffffu));
+    m = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm >> 16));
+  }
+};
+template <> struct QPart<MOE_Q4_0> {
+  static constexpr int bytes = 18;
+  // The block starts 2-byte aligned: load 3 aligned dwords covering the 8
+  // nibble bytes and realign them; the scale comes from the dword holding it.
+  static __device__ __forceinline__ void load(rsrc_t r, uint32_t off, int half, uint32_t &dm, u32x2 &nb) {
+    dm = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off & ~3u), 0, 0);
+    const uint32_t s = off + 2 + 8 * half, a = s & ~3u;
+    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, (int)a, 0, 0);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(a + 8), 0, 0);
+    const uint32_t l0 = lo.x, l1 = lo.y;
+    if (s & 2u) {
+      nb.x = __builtin_amdgcn_alignbyte(l1, l0, 2);
+      nb.y = __builtin_amdgcn_alignbyte(hi, l1, 2);
+    } else {
+      nb.x = l0;
+      nb.y = l1;
+    }
+  }
+  static __device__ __forceinline__ void scales(uint32_t dm, uint32_t off, float &d, float &m) {
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((off & 2u) ? (dm >> 16) : (dm & 0xffffu)));
+    m = -8.0f * d;
+  }
+};
+
+// 8 nibbles of 8 bytes (low halves, or high halves if hi) as exact f16 q,
+// in the order k = 0,2,1,3,4,6,5,7 of the bytes (two mask-ors per dword).
+__device__ __forceinline__ half8 nibbles_f16(u32x2 nb, bool hi) {
+  uint32_t w0 = nb.x, w1 = nb.y;
+  if (hi) {
+    w0 >>= 4;
+    w1 >>= 4;
+  }
+  const uint32_t a = (w0 & 0x000F000Fu) | 0x64006400u, b = ((w0 >> 8) & 0x000F000Fu) | 0x64006400u;
+  const uint32_t c = (w1 & 0x000F000Fu) | 0x64006400u, d = ((w1 >> 8) & 0x000F000Fu) | 0x64006400u;
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = {a, b, c, d};
+  // (1024 + q) - 1024 = q, exact in f16
+  return __builtin_bit_cast(half8, v) - (half8)(_Float16)1024.0f;
+}
+// Position, within a lane's 8 A values, of byte j of its 8 nibble bytes
+// (matches nibbles_f16's order 0,2,1,3,4,6,5,7).
+__device__ __forceinline__ int kperm(int j) { return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1); }
+
+enum { GG_GATEUP = 0, GG_DOWN = 1 };
+
+struct GemmArgs {
+  int T, k, H, F, SF, E;
+  const float *x;            // [T][H]
+  const float *act;          // sorted act [T*k][F]
+  const float *act_sh;       // [T][SF]
+  const float *wts;          // [T*k]
+  const int32_t *offsets, *perm, *tiles, *ntiles;
+  const uint8_t *w0, *w1;    // gate, up (GATEUP) or down (DOWN): routed experts
+  const uint8_t *s0, *s1;    // same for the shared expert
+  float *out;                // GATEUP: sorted act; DOWN: Y [T*k][H]
+  float *out_sh;             // GATEUP: act_sh; DOWN: Ysh [T][H]
+  int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
+};
+
+constexpr int KC = 8;           // Q4 blocks (x 32 k) of A staged per chunk
+constexpr int KCH = KC * 32;    // k values per chunk
+
+// grid.x: routed tiles (16 tokens of one expert) then shared tiles (16 tokens);
+// grid.y: slices of 256 output rows; 4 waves x 64 rows (4 MFMA tiles of 16).
+template <int QT, int MODE>
+__global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
+  constexpr int BS = QPart<QT>::bytes;
+  constexpr int NM = MODE == GG_GATEUP ? 2 : 1;  // weight matrices
+  __shared__ _Float16 ahi[16][KCH + 8], alo[16][KCH + 8];
+  __shared__ float asum[16][KC];
+  __shared__ int rowid[16];  // A row per tile token (-1: none)
+  __shared__ int outid[16];  // output row per tile token
+  __shared__ float outw[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bx = blockIdx.x;
+  const bool shared = bx >= a.max_routed_tiles;
+  int e = 0, ntok, K, R;
+  const uint8_t *m0p, *m1p;
+  if (!shared) {
+    if (bx >= *a.ntiles) return;
+    e = a.tiles[2 * bx];
+    const int first = a.offsets[e] + a.tiles[2 * bx + 1];
+    ntok = min(16, a.offsets[e + 1] - first);
+    K = MODE == GG_GATEUP ? a.H : a.F;
+    R = MODE == GG_GATEUP ? a.F : a.H;
+    const size_t mat = (size_t)R * (K / 32) * BS;
+    m0p = a.w0 + (size_t)e * mat;
+    m1p = MODE == GG_GATEUP ? a.w1 + (size_t)e * mat : nullptr;
+    if (tid < 16) {
+      const int q = first + tid;
+      const bool ok = tid < ntok;
+      rowid[tid] = ok ? (MODE == GG_GATEUP ? a.perm[q] / a.k : q) : -1;
+      outid[tid] = ok ? q : -1;
+      outw[tid] = ok && MODE == GG_DOWN ? a.wts[a.perm[q]] : 1.f;
+    }
+  } else {
+    const int t0 = 16 * (bx - a.max_routed_tiles);
+    ntok = min(16, a.T - t0);
+    K = MODE == GG_GATEUP ? a.H : a.SF;
+    R = MODE == GG_GATEUP ? a.SF : a.H;
+    m0p = a.s0;
+    m1p = a.s1;
+    if (tid < 16) {
+      const bool ok = tid < ntok;
+      rowid[tid] = ok ? t0 + tid : -1;
+      outid[tid] = ok ? t0 + tid : -1;
+      outw[tid] = 1.f;
+    }
+  }
+  const int r0 = blockIdx.y * 256;
+  if (r0 >= R) return;
+  const int nbK = K / 32;
+  const uint32_t mbytes = (uint32_t)((size_t)R * nbK * BS);
+  const rsrc_t rw0 = make_rsrc(m0p, mbytes);
+  const rsrc_t rw1 = NM == 2 ? make_rsrc(m1p, mbytes) : rw0;
+  const float *arows = MODE == GG_GATEUP ? a.x : (shared ? a.act_sh : a.act);
+  const int astride = K;
+
+  // lane roles in the MFMA: token m = lane%16 (A) / column n = lane%16 (B),
+  // k-octet kq = lane/16; D rows (tokens) 4*kq + i, column n
+  const int n = lane & 15, kq = lane >> 4;
+  const int half = kq & 1;       // nibble bytes 0..7 or 8..15
+  const bool hin = kq >= 2;      // high nibbles (k + 16)
+  f32x4 acc[NM][4];
+#pragma unroll
+  for (int mt = 0; mt < NM; mt++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rbase = r0 + wave * 64;
+
+  __syncthreads();
+  for (int kc = 0; kc < nbK; kc += KC) {
+    // stage A: 16 tokens x KCH k values as f16 hi + lo, in the lanes' k order,
+    // plus each token's per-block sums
+    {
+      const int m = tid >> 4, seg = tid & 15;  // 16 threads per token, 16 k each
+      const int kb = kc * 32 + seg * 16;
+      const int row = rowid[m];
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (row >= 0 && kb + i < K) f = *reinterpret_cast<const float4 *>(arows + (size_t)row * astride + kb + i);
+        v[i] = f.x;
+        v[i + 1] = f.y;
+        v[i + 2] = f.z;
+        v[i + 3] = f.w;
+      }
+      // k within the block: kk = seg%2*16 + i; the lane holding it has
+      // kq = (kk%16)/8 + 2*(kk/16) and slot kperm(kk%8)
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int kk = (seg & 1) * 16 + i;              // k within the Q4 block
+        const int blk = seg >> 1;                        // block within the chunk
+        const int q8 = ((kk & 15) >> 3) + 2 * (kk >> 4); // k-octet of the lane
+        const int col = blk * 32 + q8 * 8 + kperm(kk & 7);
+        const _Float16 h = (_Float16)v[i];
+        ahi[m][col] = h;
+        alo[m][col] = (_Float16)(v[i] - (float)h);
+        s += v[i];
+      }
+      s += __shfl_xor(s, 1, 64);  // the two threads of one block
+      if ((seg & 1) == 0) asum[m][seg >> 1] = s;
+    }
+    __syncthreads();
+    for (int b = 0; b < KC && kc + b < nbK; b++) {
+      const int bk = kc + b;
+      const half8 xh = *reinterpret_cast<const half8 *>(&ahi[n][b * 32 + kq * 8]);
+      const half8 xl = *reinterpret_cast<const half8 *>(&alo[n][b * 32 + kq * 8]);
+      float sx[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) sx[i] = asum[4 * kq + i][b];
+#pragma unroll
+      for (int mt = 0; mt < NM; mt++) {
+        const rsrc_t rw = mt == 0 ? rw0 : rw1;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int row = rbase + 16 * c + n;
+          const uint32_t off = row < R ? (uint32_t)(row * nbK + bk) * BS : 0x7ffffff0u;
+          uint32_t dm;
+          u32x2 nb;
+          QPart<QT>::load(rw, off, half, dm, nb);
+          float d, m;
+          QPart<QT>::scales(dm, off, d, m);
+          const half8 q = nibbles_f16(nb, hin);
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, q, z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, q, z, 0, 0, 0);
+          // block value: d * sum(q x) + m * sum(x); the column (row) of D is
+          // this lane's n, its tokens 4*kq + i
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[mt][c][i] = __builtin_fmaf(d, z[i], __builtin_fmaf(m, sx[i], acc[mt][c][i]));
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: this lane holds D[token 4*kq + i][row rbase + 16c + n]
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int row = rbase + 16 * c + n;
+    if (row >= R) continue;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int m = 4 * kq + i;
+      const int o = outid[m];
+      if (o < 0) continue;
+      float v;
+      if (MODE == GG_GATEUP) {
+        const float g = acc[0][c][i], u = acc[NM - 1][c][i];
+        v = g / (1.0f + __expf(-g)) * u;
+      } else {
+        v = outw[m] * acc[0][c][i];
+      }
+      float *dst = shared ? a.out_sh : a.out;
+      dst[(size_t)o * R + row] = v;
+    }
+  }
+}
+
+// resid[t][h] += sum_j Y[pos(t, j)][h] + Ysh[t][h]
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, const float *__restrict__ Ysh,
+                                                 const int32_t *__restrict__ pos, int T, int k, int H,
+                                                 float *__restrict__ resid) {
+  const int t = blockIdx.y, h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= H) return;
+  float acc = 0.f;
+  for (int j = 0; j < k; j++) acc += Y[(size_t)pos[t * k + j] * H + h];
+  if (Ysh) acc += Ysh[(size_t)t * H + h];
+  resid[(size_t)t * H + h] += acc;
+}
+
+// ---------------------------------------------------------------- launch --
+
+size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * (4 + 2); }
+
+hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
+  const int T = p.T, k = p.k, E = p.E;
+  const size_t lds = prefill_sort_lds_bytes(T, E);
+  timer_before(5, st);
+  k_sort_by_expert<<<1, 1024, lds, st>>>(p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
+  timer_after(5, st);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GemmArgs g{};
+  g.T = T;
+  g.k = k;
+  g.H = p.H;
+  g.F = p.F;
+  g.SF = p.SF;
+  g.E = E;
+  g.x = p.x;
+  g.act = p.act;
+  g.act_sh = p.act_sh;
+  g.wts = p.wts;
+  g.offsets = p.offsets;
+  g.perm = p.perm;
+  g.tiles = p.tiles;
+  g.ntiles = p.ntiles;
+  g.max_routed_tiles = (T * k + 15) / 16 + E;
+  const int shtiles = p.SF > 0 ? (T + 15) / 16 : 0;
+  // gate || up
+  g.w0 = p.gate_exps;
+  g.w1 = p.up_exps;
+  g.s0 = p.gate_sh;
+  g.s1 = p.up_sh;
+  g.out = p.act;
+  g.out_sh = p.act_sh;
+  {
+    const int rows = p.F > p.SF ? p.F : p.SF;
+    dim3 grid(g.max_routed_tiles + shtiles, (rows + 255) / 256);
+    timer_before(6, st);
+    if (p.qtype == MOE_Q4_1)
+      k_group_gemm<MOE_Q4_1, GG_GATEUP><<<grid, 256, 0, st>>>(g);
+    else
+      k_group_gemm<MOE_Q4_0, GG_GATEUP><<<grid, 256, 0, st>>>(g);
+    timer_after(6, st);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // down, weighted
+  g.w0 = p.down_exps;
+  g.w1 = nullptr;
+  g.s0 = p.down_sh;
+  g.s1 = nullptr;
+  g.out = p.Y;
+  g.out_sh = p.Ysh;
+  {
+    dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
+    timer_before(7, st);
+    if (p.qtype == MOE_Q4_1)
+      k_group_gemm<MOE_Q4_1, GG_DOWN><<<grid, 256, 0, st>>>(g);
+    else
+      k_group_gemm<MOE_Q4_0, GG_DOWN><<<grid, 256, 0, st>>>(g);
+    timer_after(7, st);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  timer_before(8, st);
+  k_combine<<<dim3((p.H + 255) / 256, T), 256, 0, st>>>(p.Y, p.SF > 0 ? p.Ysh : nullptr, p.pos, T, k, p.H, p.resid);
+  timer_after(8, st);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -101,10 +101,13 @@ def test_pointer_errors_are_reported_without_launching():
     assert L.moe_router_topk(C.byref(cfg), C.byref(lw), x, -1, None, w, w, w, ws, None) == -1
 
 
-def test_decode_down_staging_limit_reported():
+def test_wide_configs_take_the_grouped_path_workspace():
+    # k*F + SF beyond the decode kernels' LDS staging: such shapes run the
+    # grouped path at any T, so even T = 1 reserves its regions
     L = moe.load_library()
-    cfg = moe.make_config(1024, 64, 32, 512)  # k*F = 16384 > 14336
-    lw = moe.LayerWeights(*([0x10000] * 5 + [0] * 3))
-    rc = L.moe_expert_ffn_q4(C.byref(cfg), C.byref(lw), C.c_void_p(0x20000), 1, C.c_void_p(0x20000),
-                             C.c_void_p(0x20000), C.c_void_p(0x30000), C.c_void_p(0x40000), 1 << 30, None)
-    assert rc == -1 and "LDS" in L.moe_last_error().decode()
+    wide = moe.make_config(1024, 64, 32, 512)
+    narrow = moe.make_config(1024, 64, 4, 512)
+    assert L.moe_workspace_bytes(C.byref(wide), 1) > 0
+    assert L.moe_workspace_bytes(C.byref(narrow), 1) > 0
+    # many tokens: the grouped path's chunked regions
+    assert L.moe_workspace_bytes(C.byref(narrow), 4096) > L.moe_workspace_bytes(C.byref(narrow), 8)

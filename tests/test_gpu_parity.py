@@ -93,7 +93,30 @@ def test_layer_step_parity(gpu, name, composed):
     assert err <= REL_TOL
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 13, 40])
+def test_layer_prefill_chunk(gpu):
+    # 512 tokens through one Flint-shaped layer (grouped MFMA path); the oracle
+    # checks a spread sample of tokens (tokens are independent)
+    wl = S.WORKLOADS["prefill"]
+    _say("layer prefill T=512 (sampled oracle rows)")
+    w, x = _layer(wl, seed=7)
+    sample = list(range(0, 512, 11)) + [511]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
+    print(f"[result] prefill max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("T", [600, 1100])
+def test_layer_prefill_multi_chunk(gpu, T):
+    # more tokens than one chunk: the chunks run one after another
+    wl = S.Workload("chunks", 256, 16, 3, 64, 96, S.Q4_1, has_bias=True)
+    _say("prefill chunks T", T)
+    w, x = _layer(wl, seed=T, tokens=T)
+    sample = list(range(0, T, 37)) + [T - 1]
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w), sample=sample)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13, 40])
 def test_layer_token_counts_ragged(gpu, T):
     wl = S.Workload("ragged", 96 * 2, 24, 3, 160, 96, S.Q4_1, has_bias=True)
     _say("ragged T", T)
@@ -102,12 +125,13 @@ def test_layer_token_counts_ragged(gpu, T):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("T", [3, 20])
 @pytest.mark.parametrize("H,F,SF", [(96, 96, 0), (96, 160, 96), (288, 32, 64), (2080, 224, 0)])
-def test_layer_q4_0_unaligned_rows(gpu, H, F, SF):
-    # odd block counts give Q4_0 rows at 2-byte alignment
+def test_layer_q4_0_unaligned_rows(gpu, H, F, SF, T):
+    # odd block counts give Q4_0 rows at 2-byte alignment (T=3 decode, T=20 grouped)
     wl = S.Workload("q40odd", H, 16, 3, F, SF, S.Q4_0, has_bias=True)
-    _say("q4_0 odd rows", H, F, SF)
-    w, x = _layer(wl, seed=H + F, tokens=3)
+    _say("q4_0 odd rows", H, F, SF, "T", T)
+    w, x = _layer(wl, seed=H + F, tokens=T)
     err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
     assert err <= REL_TOL
 
