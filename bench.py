@@ -69,6 +69,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true")
+    ap.add_argument("--mode", default="eager", choices=["eager", "graph"],
+                    help="eager: one native moe_stack_step call per step (dominant kernel timed with HIP events "
+                         "during the timed steps); graph: each step variant replayed as a captured HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 device-to-device copies of 1 GiB (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -87,6 +92,14 @@ def main():
         sys.exit(1)
     moe.load_library()
     dev = "cuda"
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * 4, "copies": 8}), flush=True)
+        return
     wl = S.WORKLOADS[args.workload]
     L, T, nS = wl.layers, wl.tokens, args.slots
     if wl.name == "ling":
@@ -116,46 +129,60 @@ def main():
     xs = [[S.make_x(wl, T, layer=l, step=s, device=dev) for l in range(L)] for s in range(nS)]
     resid = torch.zeros((T, wl.hidden), dtype=torch.float32, device=dev)
     ws = moe.alloc_workspace(cfg, T, dev)
-    ids = [[torch.empty((T, wl.top_k), dtype=torch.int32, device=dev) for _ in range(L)] for _ in range(nS)]
-    wts = [[torch.empty((T, wl.top_k), dtype=torch.float32, device=dev) for _ in range(L)] for _ in range(nS)]
+    ids = [torch.empty((L, T, wl.top_k), dtype=torch.int32, device=dev) for _ in range(nS)]
+    wts = [torch.empty((L, T, wl.top_k), dtype=torch.float32, device=dev) for _ in range(nS)]
+    stacks = [moe.Stack(cfg, layers, xs[s], resid, ids[s], wts[s], ws) for s in range(nS)]
 
-    def step(s):
-        for l in range(L):
-            moe.layer_step(cfg, None, xs[s][l], resid, ids[s][l], wts[s][l], ws, lw=lws[l])
-
-    # eager pass over every variant (loads code objects, fills ids for the byte model)
+    # one pass over every input variant (loads code objects, fills ids for the byte model)
     for s in range(nS):
-        step(s)
+        stacks[s].step()
     torch.cuda.synchronize()
     graphs = []
-    for s in range(nS):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(s)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    log(f"captured {nS} graphs of {L} layer steps ({4 * L} kernels each)")
+    if args.mode == "graph":
+        for s in range(nS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                stacks[s].step()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        log(f"captured {nS} graphs of {L} layer steps")
+
+    def run(i):
+        if graphs:
+            graphs[i % nS].replay()
+        else:
+            stacks[i % nS].step()
 
     # algorithmic weight bytes per step variant: router + bias + distinct picked experts + shared
     distinct = np.zeros((nS, L))
     for s in range(nS):
+        h = ids[s].cpu().numpy()
         for l in range(L):
-            distinct[s, l] = len(np.unique(ids[s][l].cpu().numpy()))
+            distinct[s, l] = len(np.unique(h[l]))
     step_bytes = [float(L * (router_bytes + shared_bytes) + distinct[s].sum() * per_expert) for s in range(nS)]
 
+    grouped = T > moe.load_library().moe_decode_max_tokens()
+    dominant = (moe.KERNEL_GROUP_GATEUP, "group_gateup") if grouped else (moe.KERNEL_GATEUP, "gateup_swiglu")
     for i in range(args.warmup):
-        graphs[i % nS].replay()
+        run(i)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps ({args.mode})")
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # eager mode: the dominant kernel is bracketed by HIP events on its stream during the timed steps
+    timer = moe.KernelTimer(dominant[0], args.steps * L) if (args.mode == "eager" and not args.no_kernel_timer) \
+        else None
+    if timer:
+        timer.__enter__()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        graphs[i % nS].replay()
+        run(i)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if timer:
+        timer.__exit__(None, None, None)
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     mean_bytes = sum(step_bytes[i % nS] for i in range(args.steps)) / args.steps
@@ -164,20 +191,19 @@ def main():
     log(f"timed: {ms_step * 1e3:.1f} us/step ({ms_step * 1e3 / L:.2f} us/layer), {tok_s:.1f} tok/s, "
         f"{gbps:.1f} GB/s of weights ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s); wall {wall:.3f}s")
 
-    # per-kernel durations, launch by launch, HIP events on the launch stream (eager)
+    # the other kernels' durations: a separate pass per kernel, same eager steps
     kstats = {}
-    grouped = T > moe.load_library().moe_decode_max_tokens()
-    if not args.no_kernel_timer:
+    if timer:
+        kstats[dominant[1]] = {"launches": timer.count, "mean_us": timer.mean_us}
+    if not args.no_kernel_timer and args.mode == "eager":
         nk = min(20, max(4, args.steps // 10))
-        kernels = ((("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT), ("sort", moe.KERNEL_SORT),
-                    ("group_gateup", moe.KERNEL_GROUP_GATEUP), ("group_down", moe.KERNEL_GROUP_DOWN),
-                    ("combine", moe.KERNEL_COMBINE)) if grouped else
-                   (("router", moe.KERNEL_ROUTER), ("gateup_swiglu", moe.KERNEL_GATEUP),
-                    ("down_accum", moe.KERNEL_DOWN)))
-        for name, kid in kernels:
+        others = ((("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT), ("sort", moe.KERNEL_SORT),
+                   ("group_down", moe.KERNEL_GROUP_DOWN), ("combine", moe.KERNEL_COMBINE)) if grouped else
+                  (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN)))
+        for name, kid in others:
             with moe.KernelTimer(kid, nk * L) as kt:
                 for i in range(nk):
-                    step(i % nS)
+                    run(i)
             kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us}
         log("kernel means (us): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
 
@@ -187,8 +213,7 @@ def main():
         # x read, act written; 2*T*k*F*H*2 + 2*T*SF*H*2 useful MFMA flops alongside
         gu_expert = 2 * wl.expert_ff * (wl.hidden // 32) * bs
         gu_shared = 2 * wl.shared_ff * (wl.hidden // 32) * bs
-        nk = kstats["group_gateup"]["launches"] // L
-        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(nk)]))
+        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(args.steps)]))
         act_bytes = T * (wl.top_k * wl.expert_ff + wl.shared_ff) * 4 + T * wl.hidden * 4
         per_launch = d_mean * gu_expert + gu_shared + act_bytes
         us = kstats["group_gateup"]["mean_us"]
@@ -204,8 +229,7 @@ def main():
         # expert's gate and up rows, x read once per token, act written once
         gu_expert = 2 * wl.expert_ff * (wl.hidden // 32) * bs
         gu_shared = 2 * wl.shared_ff * (wl.hidden // 32) * bs
-        nk = kstats["gateup_swiglu"]["launches"] // L
-        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(nk)]))
+        d_mean = float(np.mean([distinct[i % nS].mean() for i in range(args.steps)]))
         act_bytes = T * (wl.top_k * wl.expert_ff + wl.shared_ff) * 4 + T * wl.hidden * 4
         per_launch = d_mean * gu_expert + gu_shared + act_bytes
         ach = per_launch / (kstats["gateup_swiglu"]["mean_us"] * 1e-6) / 1e9

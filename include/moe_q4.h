@@ -29,7 +29,8 @@
  *     `stream` and the call returns without synchronising;
  *   - the caller owns every buffer; the library allocates nothing and keeps no
  *     pointer after returning; calls are reentrant for distinct workspaces;
- *   - f32 arrays and Q4 tensors must be 16-byte aligned; rows of Q4 tensors
+ *   - x, resid, router_w, logits_in, the workspace and the Q4 tensors must be
+ *     16-byte aligned; ids, routing weights and the bias 4-byte aligned; rows of Q4 tensors
  *     are whole blocks, consecutive (Q4_1 rows stay 4-byte aligned, Q4_0 rows
  *     may be 2-byte aligned, which the kernels handle);
  *   - T = 0 is a no-op returning MOE_OK;
@@ -128,6 +129,17 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
  * workspace). */
 int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
                    float *resid, int32_t *ids_out, float *weights_out, void *workspace,
+                   size_t workspace_bytes, moe_stream_t stream);
+
+/* L MoE layers of one shape run in order on one stream, each a
+ * moe_layer_step: layer l reads x[l] and adds its FFN output to the shared
+ * residual, so layer l+1's expert reads start only after layer l finished.
+ *   layers:      host array of L weight sets
+ *   x:           host array of L device pointers, each [T][H] f32
+ *   ids_out / weights_out: [L][T][k] or NULL
+ * The workspace is reused by every layer (moe_workspace_bytes(cfg, T)). */
+int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32_t L, const float *const *x,
+                   int32_t T, float *resid, int32_t *ids_out, float *weights_out, void *workspace,
                    size_t workspace_bytes, moe_stream_t stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */

@@ -58,6 +58,9 @@ def load_library(path=LIB_PATH):
     L.moe_last_error.argtypes = []
     L.moe_decode_max_tokens.restype = C.c_int32
     L.moe_decode_max_tokens.argtypes = []
+    L.moe_stack_step.restype = C.c_int
+    L.moe_stack_step.argtypes = [C.POINTER(MoeConfig), C.POINTER(LayerWeights), C.c_int32, C.POINTER(C.c_void_p),
+                                 C.c_int32, P, P, P, P, S, P]
     L.moe_kernel_timer_begin.restype = C.c_int
     L.moe_kernel_timer_begin.argtypes = [C.c_int32, C.c_int32]
     L.moe_kernel_timer_end.restype = C.c_int
@@ -67,7 +70,7 @@ def load_library(path=LIB_PATH):
 
 
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
-            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end")
+            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step")
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
 KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE = 5, 6, 7, 8
 
@@ -180,6 +183,24 @@ def layer_step(cfg, w, x, resid, ids_out=None, weights_out=None, workspace=None,
     _raise(load_library().moe_layer_step(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
                                          _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(stream)))
     return resid
+
+
+class Stack:
+    """L layers of one shape run in order by moe_stack_step (one native call per step)."""
+
+    def __init__(self, cfg, layers, xs, resid, ids=None, wts=None, workspace=None):
+        self.cfg, self.L, self.resid = cfg, len(layers), resid
+        self.lws = (LayerWeights * self.L)(*[layer_weights(w) for w in layers])
+        self.xs = (C.c_void_p * self.L)(*[x.data_ptr() for x in xs])
+        self.T = xs[0].shape[0]
+        self.ids, self.wts = ids, wts
+        self.ws = workspace if workspace is not None else alloc_workspace(cfg, self.T, resid.device)
+        self._keep = (layers, xs)
+
+    def step(self, stream=None):
+        _raise(load_library().moe_stack_step(C.byref(self.cfg), self.lws, self.L, self.xs, self.T, _ptr(self.resid),
+                                             _ptr(self.ids), _ptr(self.wts), _ptr(self.ws), self.ws.numel(),
+                                             _stream(stream)))
 
 
 class KernelTimer:

@@ -98,6 +98,12 @@ int check_ptr(const void *p, const char *name, bool required) {
   if (!aligned16(p)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name);
   return MOE_OK;
 }
+// ids, routing weights and the bias are read and written element by element
+int check_ptr4(const void *p, const char *name, bool required) {
+  if (!p) return required ? fail(MOE_EINVAL, "%s is NULL", name) : MOE_OK;
+  if ((uintptr_t)p & 3u) return fail(MOE_EALIGN, "%s is not 4-byte aligned", name);
+  return MOE_OK;
+}
 
 int check_ws(const moe_config &c, int32_t T, void *ws, size_t bytes) {
   size_t need = layout(c, T).total;
@@ -221,11 +227,13 @@ struct Timer {
 }  // namespace
 
 namespace moe {
-void timer_before(int id, hipStream_t st) {
-  if (g_timer.kernel == id && g_timer.count < g_timer.capacity) (void)hipEventRecord(g_timer.start[g_timer.count], st);
-}
-void timer_after(int id, hipStream_t st) {
-  if (g_timer.kernel == id && g_timer.count < g_timer.capacity) (void)hipEventRecord(g_timer.stop[g_timer.count++], st);
+TimerSlot timer_slot(int id) {
+  TimerSlot t;
+  if (g_timer.kernel == id && g_timer.count < g_timer.capacity) {
+    t.start = g_timer.start[g_timer.count];
+    t.stop = g_timer.stop[g_timer.count++];
+  }
+  return t;
 }
 }  // namespace moe
 
@@ -299,9 +307,9 @@ int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const flo
     if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
     if ((rc = check_ptr(x, "x", true))) return rc;
   }
-  if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
-  if ((rc = check_ptr(ids, "ids", true))) return rc;
-  if ((rc = check_ptr(weights, "weights", true))) return rc;
+  if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
+  if ((rc = check_ptr4(ids, "ids", true))) return rc;
+  if ((rc = check_ptr4(weights, "weights", true))) return rc;
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
   return router_topk_impl(*cfg, w, x, T, logits_in, ids, weights, workspace, (hipStream_t)stream);
 }
@@ -317,8 +325,8 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
-  if ((rc = check_ptr(ids, "ids", true))) return rc;
-  if ((rc = check_ptr(weights, "weights", true))) return rc;
+  if ((rc = check_ptr4(ids, "ids", true))) return rc;
+  if ((rc = check_ptr4(weights, "weights", true))) return rc;
   if ((rc = check_ptr(resid, "resid", true))) return rc;
   if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
@@ -338,13 +346,13 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
-  if ((rc = check_ptr(w->router_bias, "router_bias", false))) return rc;
+  if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
   if ((rc = check_ptr(resid, "resid", true))) return rc;
   if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
-  if ((rc = check_ptr(ids_out, "ids_out", false))) return rc;
-  if ((rc = check_ptr(weights_out, "weights_out", false))) return rc;
+  if ((rc = check_ptr4(ids_out, "ids_out", false))) return rc;
+  if ((rc = check_ptr4(weights_out, "weights_out", false))) return rc;
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
   const Layout L = layout(*cfg, T);
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
@@ -361,6 +369,26 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if ((rc = router_topk_impl(*cfg, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
   if (T > kDecodeMaxT || !decode_fits(*cfg)) return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
   return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
+}
+
+int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32_t L, const float *const *x,
+                   int32_t T, float *resid, int32_t *ids_out, float *weights_out, void *workspace,
+                   size_t workspace_bytes, moe_stream_t stream) {
+  g_err.clear();
+  if (L < 0) return fail(MOE_EINVAL, "L %d < 0", L);
+  if (L > 0 && (!layers || !x)) return fail(MOE_EINVAL, "layers or x is NULL");
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  const size_t per = (size_t)T * cfg->top_k;
+  for (int32_t l = 0; l < L; l++) {
+    rc = moe_layer_step(cfg, &layers[l], x[l], T, resid, ids_out ? ids_out + l * per : nullptr,
+                        weights_out ? weights_out + l * per : nullptr, workspace, workspace_bytes, stream);
+    if (rc) {
+      std::string m = g_err;
+      return fail(rc, "layer %d: %s", l, m.c_str());
+    }
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

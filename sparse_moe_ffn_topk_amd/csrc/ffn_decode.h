@@ -264,14 +264,13 @@ static inline int xr_for(int n) {  // float4s per thread to stage n floats with 
 
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  k_gateup_swiglu<QT, LPR, XR><<<grid, 256, lds, st>>>(a.x, a.ids, a.wts, a.logits, a.bias, a.sel, a.T, a.H, a.k,
-                                                         a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh,
-                                                         a.act);
+  MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
+             a.bias, a.sel, a.T, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.act);
 }
 template <int QT, int LPR, int XR>
 static void down_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  k_down_accum<QT, LPR, XR><<<grid, 256, lds, st>>>(a.act, a.ids, a.wts, a.T, a.H, a.k, a.F, a.SF, a.down_exps,
-                                                      a.down_sh, a.resid);
+  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, (const float *)a.act,
+             (const int32_t *)a.ids, (const float *)a.wts, a.T, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid);
 }
 
 #define MOE_XR_SWITCH(FN, QT, LPR)                  \

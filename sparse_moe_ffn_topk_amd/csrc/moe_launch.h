@@ -1,5 +1,6 @@
 // moe_launch.h -- host-side launchers of the MoE kernels (internal).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -57,9 +58,20 @@ struct PrefillArgs {
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
 size_t prefill_sort_lds_bytes(int T, int E);
 
-// Kernel timer hooks (diagnostics): bracket one launch of kernel `id` with
-// events on `st` when the timer is armed for it.
-void timer_before(int id, hipStream_t st);
-void timer_after(int id, hipStream_t st);
+// Kernel timer (diagnostics): when armed for kernel `id`, timer_slot() hands
+// out the next (start, stop) event pair, which the launch attaches to the
+// kernel's own dispatch (hipExtLaunchKernelGGL), so the events time exactly
+// that kernel's execution on its stream; otherwise both are NULL.
+struct TimerSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+TimerSlot timer_slot(int id);
+
+// Launch KERNEL (parenthesise template names) with the timer's events for ID.
+#define MOE_LAUNCH(ID, KERNEL, GRID, BLOCK, LDS, ST, ...)                                                 \
+  do {                                                                                                   \
+    const ::moe::TimerSlot ts_ = ::moe::timer_slot(ID);                                                  \
+    hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, ts_.start, ts_.stop, 0, __VA_ARGS__);            \
+  } while (0)
 
 }  // namespace moe

@@ -358,9 +358,8 @@ size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32)
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
   const size_t lds = prefill_sort_lds_bytes(T, E);
-  timer_before(5, st);
-  k_sort_by_expert<<<1, 1024, lds, st>>>(p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
-  timer_after(5, st);
+  MOE_LAUNCH(5, k_sort_by_expert, dim3(1), dim3(1024), (uint32_t)lds, st, p.ids, T, k, E, p.offsets, p.pos, p.perm,
+             p.tiles, p.ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   GemmArgs g{};
@@ -390,12 +389,10 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   {
     const int rows = p.F > p.SF ? p.F : p.SF;
     dim3 grid(g.max_routed_tiles + shtiles, (rows + 255) / 256);
-    timer_before(6, st);
     if (p.qtype == MOE_Q4_1)
-      k_group_gemm<MOE_Q4_1, GG_GATEUP><<<grid, 256, 0, st>>>(g);
+      MOE_LAUNCH(6, (k_group_gemm<MOE_Q4_1, GG_GATEUP>), grid, dim3(256), 0u, st, g);
     else
-      k_group_gemm<MOE_Q4_0, GG_GATEUP><<<grid, 256, 0, st>>>(g);
-    timer_after(6, st);
+      MOE_LAUNCH(6, (k_group_gemm<MOE_Q4_0, GG_GATEUP>), grid, dim3(256), 0u, st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // down, weighted
@@ -407,17 +404,14 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   g.out_sh = p.Ysh;
   {
     dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
-    timer_before(7, st);
     if (p.qtype == MOE_Q4_1)
-      k_group_gemm<MOE_Q4_1, GG_DOWN><<<grid, 256, 0, st>>>(g);
+      MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_1, GG_DOWN>), grid, dim3(256), 0u, st, g);
     else
-      k_group_gemm<MOE_Q4_0, GG_DOWN><<<grid, 256, 0, st>>>(g);
-    timer_after(7, st);
+      MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_0, GG_DOWN>), grid, dim3(256), 0u, st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  timer_before(8, st);
-  k_combine<<<dim3((p.H + 255) / 256, T), 256, 0, st>>>(p.Y, p.SF > 0 ? p.Ysh : nullptr, p.pos, T, k, p.H, p.resid);
-  timer_after(8, st);
+  MOE_LAUNCH(8, k_combine, dim3((p.H + 255) / 256, T), dim3(256), 0u, st, (const float *)p.Y,
+             (const float *)(p.SF > 0 ? p.Ysh : nullptr), (const int32_t *)p.pos, T, k, p.H, p.resid);
   return hipGetLastError();
 }
 

@@ -112,31 +112,27 @@ __global__ __launch_bounds__(256) void k_select(const float *__restrict__ logits
 
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
                                 hipStream_t st) {
-  timer_before(1, st);
   if (T <= 8) {
     dim3 grid(E);
     if (T == 1)
-      k_router_rows<1><<<grid, 64, 0, st>>>(W, x, H, E, T, logits);
+      MOE_LAUNCH(1, (k_router_rows<1>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
     else if (T <= 2)
-      k_router_rows<2><<<grid, 64, 0, st>>>(W, x, H, E, T, logits);
+      MOE_LAUNCH(1, (k_router_rows<2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
     else if (T <= 4)
-      k_router_rows<4><<<grid, 64, 0, st>>>(W, x, H, E, T, logits);
+      MOE_LAUNCH(1, (k_router_rows<4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
     else
-      k_router_rows<8><<<grid, 64, 0, st>>>(W, x, H, E, T, logits);
+      MOE_LAUNCH(1, (k_router_rows<8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
   } else {
     dim3 grid((E + 15) / 16, (T + 15) / 16);
-    k_router_tiled<<<grid, 256, 0, st>>>(W, x, H, E, T, logits);
+    MOE_LAUNCH(1, k_router_tiled, grid, dim3(256), 0u, st, W, x, H, E, T, logits);
   }
-  timer_after(1, st);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const float *logits, const float *bias, int T, int E, int k, int G, int Gu,
                          float scale, float wsum_min, int32_t *ids, float *wts, hipStream_t st) {
   const SelParams P{E, k, G, Gu, scale, wsum_min};
-  timer_before(2, st);
-  k_select<<<dim3(T), 256, 0, st>>>(logits, bias, T, P, ids, wts);
-  timer_after(2, st);
+  MOE_LAUNCH(2, k_select, dim3(T), dim3(256), 0u, st, logits, bias, T, P, ids, wts);
   return hipGetLastError();
 }
 
