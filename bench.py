@@ -12,11 +12,13 @@ Inputs are synthetic and seeded (moe_synth): x ~ N(0,1) fresh per layer, 16
 pre-generated steps cycled; router N(0, 0.05); Q4 scales U(0.001, 0.02) in f16;
 uniform nibbles.  Weights are generated directly on the GPU.
 
-Timing: each of the 16 step variants is captured once as a HIP graph; W
-warm-up replays, then K timed replays between two synchronisations.  The
-dominant kernel (gate||up + SwiGLU) is then timed launch by launch with HIP
-events on its own stream (library kernel timer, eager launches) to give the
-roofline line.  The CPU baseline times the f64 oracle on a bounded sample.
+Timing: each of the 16 step variants (one native moe_stack_step call) is
+captured once as a HIP graph; W warm-up replays, then K timed replays between
+two synchronisations give the headline.  A second timed region of eager native
+steps measures kernel durations: the library attaches HIP start/stop events to
+every dispatch of the kernel under test, on its stream; the dominant kernel
+(gate||up + SwiGLU) gives the roofline line.  The CPU baseline times the f64
+oracle on a bounded sample.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -40,7 +42,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for fn in ("moe_common.h", "ffn_decode.hip"):
+    for fn in ("moe_common.h", "select_block.h", "ffn_decode.h", "ffn_decode_q41.hip"):
         with open(os.path.join(ROOT, "sparse_moe_ffn_topk_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -69,9 +71,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timer", action="store_true")
-    ap.add_argument("--mode", default="eager", choices=["eager", "graph"],
-                    help="eager: one native moe_stack_step call per step (dominant kernel timed with HIP events "
-                         "during the timed steps); graph: each step variant replayed as a captured HIP graph")
+    ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
+                    help="graph: each step variant (one native moe_stack_step call) replayed as a captured HIP "
+                         "graph; eager: the native call itself, launched step by step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device-to-device copies of 1 GiB (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -168,11 +170,6 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done; timing {args.steps} steps ({args.mode})")
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # eager mode: the dominant kernel is bracketed by HIP events on its stream during the timed steps
-    timer = moe.KernelTimer(dominant[0], args.steps * L) if (args.mode == "eager" and not args.no_kernel_timer) \
-        else None
-    if timer:
-        timer.__enter__()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
@@ -181,8 +178,6 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    if timer:
-        timer.__exit__(None, None, None)
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
     mean_bytes = sum(step_bytes[i % nS] for i in range(args.steps)) / args.steps
@@ -191,21 +186,23 @@ def main():
     log(f"timed: {ms_step * 1e3:.1f} us/step ({ms_step * 1e3 / L:.2f} us/layer), {tok_s:.1f} tok/s, "
         f"{gbps:.1f} GB/s of weights ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s); wall {wall:.3f}s")
 
-    # the other kernels' durations: a separate pass per kernel, same eager steps
+    # Kernel durations: a second timed region of eager native steps in which the
+    # library attaches HIP start/stop events to every dispatch of one kernel (on
+    # the stream it is launched on); events recorded inside a captured graph are
+    # not measurable, so graph replays cannot carry them.
     kstats = {}
-    if timer:
-        kstats[dominant[1]] = {"launches": timer.count, "mean_us": timer.mean_us}
-    if not args.no_kernel_timer and args.mode == "eager":
-        nk = min(20, max(4, args.steps // 10))
+    if not args.no_kernel_timer:
+        nk = min(args.steps, 60)
         others = ((("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT), ("sort", moe.KERNEL_SORT),
                    ("group_down", moe.KERNEL_GROUP_DOWN), ("combine", moe.KERNEL_COMBINE)) if grouped else
                   (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN)))
-        for name, kid in others:
+        for name, kid in ((dominant[1], dominant[0]),) + others:
             with moe.KernelTimer(kid, nk * L) as kt:
                 for i in range(nk):
-                    run(i)
+                    stacks[i % nS].step()
+                torch.cuda.synchronize()
             kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us}
-        log("kernel means (us): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
+        log("kernel means (us, eager dispatches): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
 
     roofline = None
     if "group_gateup" in kstats:
