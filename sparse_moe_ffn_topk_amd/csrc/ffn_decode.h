@@ -36,30 +36,30 @@ constexpr uint32_t OOB = 0x7ffffff0u;
 
 // Input staging in two halves so its loads are issued before the weight
 // loads and its LDS writes happen after them.  stage_load() reads the n floats
-// of src into registers (XR float4 per thread; loads past n return zeros);
-// stage_store() writes them as blocks of 32 (stride XSTRIDE) and each block's
-// sum to sx[].  n % 32 == 0, n <= 1024 * XR.
+// of src into registers (XR float4 per thread of NT; loads past n return
+// zeros); stage_store() writes them as blocks of 32 (stride XSTRIDE) and each
+// block's sum to sx[].  n % 32 == 0, n <= 4 * NT * XR.
 template <int XR>
 struct Stage {
   float4 v[XR];
 };
-template <int XR>
+template <int NT, int XR>
 __device__ __forceinline__ void stage_load(Stage<XR> &st, const float *src, int n) {
   const rsrc_t r = make_rsrc(src, (uint32_t)n * 4u);
 #pragma unroll
   for (int i = 0; i < XR; i++) {
     // (element-wise: __builtin_bit_cast of an ext-vector element reads element 0 with this compiler)
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((threadIdx.x + 256 * i) * 16), 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((threadIdx.x + NT * i) * 16), 0, 0);
     const uint32_t a0 = v.x, a1 = v.y, a2 = v.z, a3 = v.w;
     st.v[i] = make_float4(__uint_as_float(a0), __uint_as_float(a1), __uint_as_float(a2), __uint_as_float(a3));
   }
 }
-template <int XR>
+template <int NT, int XR>
 __device__ __forceinline__ void stage_store(const Stage<XR> &st, int n, float *xs, float *sx) {
   const int n4 = n >> 2;
 #pragma unroll
   for (int i = 0; i < XR; i++) {
-    const int q = threadIdx.x + 256 * i;
+    const int q = threadIdx.x + NT * i;
     const int b = q >> 3, c = q & 7;
     const float4 v = st.v[i];
     if (q < n4) *reinterpret_cast<float4 *>(xs + b * XSTRIDE + 4 * c) = v;
@@ -71,81 +71,89 @@ __device__ __forceinline__ void stage_store(const Stage<XR> &st, int n, float *x
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// grid.x: row tiles of 256/LPR rows; grid.y: pair p (T*k routed, then T shared).
+// grid.x: NB blocks per token; grid.y: token t.  A wave task is RW = 64/LPR
+// rows (one per lane group) of a gate/up matrix pair.  Token t's tasks are the
+// shared expert's rows first, then pick j's rows for j = 0..k-1; task u runs
+// on wave u / NB of block u % NB.  So the first waves of every block stream
+// shared rows, whose loads are issued before routing, and the routed waves
+// issue theirs as soon as the block has routed the token.
 // act row of token t: its k routed rows of F, then the shared row of SF.
-// With logits != NULL the routed blocks first route their token with the whole
-// block (select_block) while their x loads are in flight; block (0, t*k+k-1)
-// writes the token's ids and weights.  Otherwise ids are read from `ids`.
+// With logits != NULL every block routes its token (select_load/select_rank)
+// and block (0, t) writes the token's ids and weights; otherwise ids are read.
 template <int QT, int LPR, int XR>
 __global__ __launch_bounds__(256) void k_gateup_swiglu(
     const float *__restrict__ x, int32_t *__restrict__ ids, float *__restrict__ wts,
-    const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int T, int H, int k, int F,
-    int SF, const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
+    const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int H, int k, int F, int SF,
+    const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
     const uint8_t *__restrict__ gate_sh, const uint8_t *__restrict__ up_sh, float *__restrict__ act) {
   extern __shared__ float smem[];
+  __shared__ SelShared sh;
   constexpr int BS = QBlock<QT>::bytes;
-  constexpr int ROWS = 256 / LPR;
+  constexpr int RW = 64 / LPR;
   const int nbH = H >> 5;
-  const int p = blockIdx.y;
-  const int nroute = T * k;
-  const size_t arow = (size_t)k * F + SF;
-  const bool routed = p < nroute;
-  const int t = routed ? p / k : p - nroute;
-  const int rows = routed ? F : SF;
-  const int f0 = blockIdx.x * ROWS;
-  if (f0 >= rows) return;
+  const int t = blockIdx.y, NB = gridDim.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, gi = lane / LPR, li = lane % LPR;
+  const int nsw = (SF + RW - 1) / RW, nfw = (F + RW - 1) / RW;
+  const int u = wave * NB + blockIdx.x;
+  const bool is_sh = u < nsw;
+  const bool wlive = u < nsw + k * nfw;
+  const int j = is_sh ? 0 : min((u - nsw) / nfw, k - 1);
+  const int row = (is_sh ? u : u - nsw - j * nfw) * RW + gi;
+  const bool live = wlive && row < (is_sh ? SF : F);
+  const uint32_t rowbytes = (uint32_t)nbH * BS;
+  const uint32_t rowoff = live ? (uint32_t)row * rowbytes : 0u;
+  float *out = act + (size_t)t * ((size_t)k * F + SF) + (is_sh ? (size_t)k * F : (size_t)j * F);
 
+  // input, then router inputs, then (shared waves) weights: in-order retirement
+  // lets routing wait for the first two only
   Stage<XR> xst;
+  stage_load<256, XR>(xst, x + (size_t)t * H, H);
+  SelIn in{};
   int e = 0;
-  if (routed && logits) {
-    // route the token with the whole block; x is already in flight
-    __shared__ SelShared sh;
-    stage_load(xst, x + (size_t)t * H, H);
-    const int j = p - t * k;
-    const bool writer = j == k - 1 && blockIdx.x == 0;
-    select_block(logits + (size_t)t * P.E, bias, P, sh, writer ? wts + (size_t)t * k : nullptr);
-    e = sh.pick[j];
-    if (writer && threadIdx.x < k) ids[(size_t)t * k + threadIdx.x] = sh.pick[threadIdx.x];
-  } else {
-    if (routed) e = ids[p];
-    stage_load(xst, x + (size_t)t * H, H);  // input first: its loads retire first
-  }
-  const uint8_t *gbase, *ubase;
-  float *out;
-  if (routed) {
-    const size_t mat = (size_t)F * nbH * BS;
-    gbase = gate_exps + (size_t)e * mat;
-    ubase = up_exps + (size_t)e * mat;
-    out = act + (size_t)t * arow + (size_t)(p - t * k) * F;
-  } else {
-    gbase = gate_sh;
-    ubase = up_sh;
-    out = act + (size_t)t * arow + (size_t)k * F;
-  }
+  if (logits)
+    select_load(logits + (size_t)t * P.E, bias, P, in);
+  else if (!is_sh && wlive)
+    e = ids[(size_t)t * k + j];
 
-  const int gi = threadIdx.x / LPR, li = threadIdx.x % LPR;
-  const int f = f0 + gi;
-  const bool live = f < rows;
-  const uint32_t mbytes = (uint32_t)((size_t)rows * nbH * BS);
-  const rsrc_t rg = make_rsrc(gbase, mbytes), ru = make_rsrc(ubase, mbytes);
-  const uint32_t rowoff = (uint32_t)f * nbH * BS;
   const int nch = (nbH / LPR + NCH - 1) / NCH;  // LPR divides nbH
-
   Raw5 ga[NCH], ua[NCH], gb[NCH], ub[NCH];
+  rsrc_t rg = make_rsrc(gate_sh, (uint32_t)SF * rowbytes), ru = make_rsrc(up_sh, (uint32_t)SF * rowbytes);
   auto offset = [&](int c, int i) {
     const int b = li + LPR * (c * NCH + i);
     return (live && b < nbH) ? rowoff + (uint32_t)b * BS : OOB;
   };
-  auto load = [&](Raw5 *G, Raw5 *U, int c) {
+  // early: every wave issues the same loads (routed waves at the out-of-range
+  // offset, which moves no data), so each wave has the same count in flight and
+  // routing waits for exactly its own inputs
+  auto load = [&](Raw5 *G, Raw5 *U, int c, bool early) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const uint32_t off = offset(c, i);
+      const uint32_t off = (early && !is_sh) ? OOB : offset(c, i);
       G[i] = QBlock<QT>::load(rg, off);
       U[i] = QBlock<QT>::load(ru, off);
     }
   };
+  load(ga, ua, 0, true);
+  load(gb, ub, 1, true);  // (past the row end: out of range, no data moves)
+  if (logits) {
+    const bool writer = blockIdx.x == 0;
+    select_rank(in, P, sh, writer ? wts + (size_t)t * k : nullptr);
+    if (writer && threadIdx.x < k) ids[(size_t)t * k + threadIdx.x] = sh.pick[threadIdx.x];
+    e = __builtin_amdgcn_readfirstlane(sh.pick[j]);
+  }
   float *xs = smem, *sx = smem + nbH * XSTRIDE;
-  float g = 0.f, u = 0.f;
+  stage_store<256, XR>(xst, H, xs, sx);
+  if (!is_sh) {
+    const size_t mat = (size_t)F * rowbytes;
+    rg = make_rsrc(gate_exps + (size_t)e * mat, (uint32_t)mat);
+    ru = make_rsrc(up_exps + (size_t)e * mat, (uint32_t)mat);
+    load(ga, ua, 0, false);
+    if (nch > 1) load(gb, ub, 1, false);
+  }
+  __syncthreads();
+
+  float g = 0.f, v = 0.f;
   auto compute = [&](const Raw5 *G, const Raw5 *U, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
@@ -154,38 +162,35 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
       const float *xb = xs + b * XSTRIDE;
       const float s = sx[b];
       g += block_dot<QT>(G[i], off, xb, s);
-      u += block_dot<QT>(U[i], off, xb, s);
+      v += block_dot<QT>(U[i], off, xb, s);
     }
   };
-
-  load(ga, ua, 0);
-  if (nch > 1) load(gb, ub, 1);
-  stage_store(xst, H, xs, sx);
-  __syncthreads();
   for (int c = 0; c < nch; c += 2) {
     compute(ga, ua, c);
-    if (c + 2 < nch) load(ga, ua, c + 2);
+    if (c + 2 < nch) load(ga, ua, c + 2, false);
     if (c + 1 < nch) {
       compute(gb, ub, c + 1);
-      if (c + 3 < nch) load(gb, ub, c + 3);
+      if (c + 3 < nch) load(gb, ub, c + 3, false);
     }
   }
   g = group_sum_last<LPR>(g);
-  u = group_sum_last<LPR>(u);
-  if (li == LPR - 1 && live) out[f] = silu_mul(g, u);
+  v = group_sum_last<LPR>(v);
+  if (li == LPR - 1 && live) out[row] = silu_mul(g, v);
 }
 
-// grid.x: tiles of 256/LPR outputs h; grid.y: token t.  Each lane walks a flat
-// list of (pick j, block) tasks -- the token's k routed rows h, then the shared
-// row h -- two register chunks at a time.
-template <int QT, int LPR, int XR>
-__global__ __launch_bounds__(256) void k_down_accum(
-    const float *__restrict__ act, const int32_t *__restrict__ ids, const float *__restrict__ wts, int T,
-    int H, int k, int F, int SF, const uint8_t *__restrict__ down_exps, const uint8_t *__restrict__ down_sh,
+// grid.x: tiles of NT/LPR outputs h; grid.y: token t.  Each lane walks a flat
+// list of (row, block) tasks -- the shared row h first (its loads need no
+// routing and go out at once), then the token's k routed rows h -- two
+// register chunks at a time.  The token's ids and weights are fetched into
+// lanes 0..k-1 ahead of everything else.
+template <int QT, int LPR, int XR, int NT>
+__global__ __launch_bounds__(NT) void k_down_accum(
+    const float *__restrict__ act, const int32_t *__restrict__ ids, const float *__restrict__ wts, int H, int k,
+    int F, int SF, const uint8_t *__restrict__ down_exps, const uint8_t *__restrict__ down_sh,
     float *__restrict__ resid) {
   extern __shared__ float smem[];
   constexpr int BS = QBlock<QT>::bytes;
-  constexpr int ROWS = 256 / LPR;
+  constexpr int ROWS = NT / LPR;
   const int t = blockIdx.y;
   const int nbF = F >> 5, nbS = SF >> 5;
   const int nbAll = k * nbF + nbS;
@@ -194,22 +199,25 @@ __global__ __launch_bounds__(256) void k_down_accum(
   const int h = blockIdx.x * ROWS + gi;
   const bool live = h < H;
   const int bplF = nbF / LPR, bplS = nbS / LPR;  // LPR divides both
-  const int nqF = k * bplF, nq = nqF + bplS;
+  const int nq = bplS + k * bplF;
   const int nch = (nq + NCH - 1) / NCH;
   const size_t mat = (size_t)H * nbF * BS;
   const uint32_t rowF = (uint32_t)h * nbF * BS;
   const uint32_t rowS = (uint32_t)h * nbS * BS;
-  const int32_t *tid_ids = ids + (size_t)t * k;
-  const float *tw = wts + (size_t)t * k;
 
+  const uint32_t lane = threadIdx.x & 63;
+  const rsrc_t rid = make_rsrc(ids + (size_t)t * k, (uint32_t)k * 4u);
+  const rsrc_t rwt = make_rsrc(wts + (size_t)t * k, (uint32_t)k * 4u);
+  const int id_v = (int)__builtin_amdgcn_raw_buffer_load_b32(rid, (int)(lane * 4u), 0, 0);
+  const float wt_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rwt, (int)(lane * 4u), 0, 0));
   Stage<XR> ast;  // the token's act row: its k routed rows, then the shared row
-  stage_load(ast, act + (size_t)t * (k * F + SF), k * F + SF);
+  stage_load<NT, XR>(ast, act + (size_t)t * (k * F + SF), k * F + SF);
 
-  // task q: routed pick j = q / bplF (block li + LPR*(q % bplF)), then the shared row
-  auto pick = [&](int q) { return q < nqF ? q / bplF : k; };
-  auto block = [&](int q, int j) { return li + LPR * (q < nqF ? q - j * bplF : q - nqF); };
+  // task q: the shared row (j = k) for q < bplS, then pick j = (q - bplS) / bplF
+  auto pick = [&](int q) { return q < bplS ? k : (q - bplS) / bplF; };
+  auto block = [&](int q, int j) { return li + LPR * (q < bplS ? q : q - bplS - j * bplF); };
   auto rsrc_for = [&](int j) {
-    return j < k ? make_rsrc(down_exps + (size_t)tid_ids[j] * mat, (uint32_t)mat)
+    return j < k ? make_rsrc(down_exps + (size_t)__builtin_amdgcn_readlane(id_v, j) * mat, (uint32_t)mat)
                  : make_rsrc(down_sh, (uint32_t)((size_t)H * nbS * BS));
   };
   auto offset = [&](int q, int j) {
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256) void k_down_accum(
   auto load = [&](Raw5 *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int q = c * NCH + i, j = pick(q);
+      const int q = c * NCH + i, j = min(pick(q), k);
       W[i] = QBlock<QT>::load(rsrc_for(j), offset(q, j));
     }
   };
@@ -227,16 +235,17 @@ __global__ __launch_bounds__(256) void k_down_accum(
   auto compute = [&](const Raw5 *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
-      const int q = c * NCH + i, j = pick(q);
+      const int q = c * NCH + i, j = min(pick(q), k);
       const int ab = min(j * nbF + block(q, j), nbAll - 1);  // staged act block (shared row after routed)
       const float d = block_dot<QT>(W[i], offset(q, j), xs + ab * XSTRIDE, sx[ab]);
-      acc = __builtin_fmaf(j < k ? tw[min(j, k - 1)] : 1.0f, d, acc);
+      const int wbits = j < k ? __builtin_amdgcn_readlane(__float_as_int(wt_v), j) : __float_as_int(1.0f);
+      acc = __builtin_fmaf(__int_as_float(wbits), d, acc);
     }
   };
 
   load(A, 0);
   if (nch > 1) load(B, 1);
-  stage_store(ast, k * F + SF, xs, sx);
+  stage_store<NT, XR>(ast, k * F + SF, xs, sx);
   __syncthreads();
   for (int c = 0; c < nch; c += 2) {
     compute(A, c);
@@ -256,8 +265,8 @@ static inline int lanes_for(int nb) {
   int l = nb & -nb;  // largest power of two dividing nb
   return l > 16 ? 16 : l;
 }
-static inline int xr_for(int n) {  // float4s per thread to stage n floats with 256 threads
-  int need = (n / 4 + 255) / 256, xr = 1;
+static inline int xr_for(int n, int nt) {  // float4s per thread to stage n floats with nt threads
+  int need = (n / 4 + nt - 1) / nt, xr = 1;
   while (xr < need) xr <<= 1;
   return xr;
 }
@@ -265,12 +274,20 @@ static inline int xr_for(int n) {  // float4s per thread to stage n floats with 
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
-             a.bias, a.sel, a.T, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.act);
+             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.act);
+}
+template <int QT, int LPR, int XR, int NT>
+static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT>), grid, dim3(NT), (uint32_t)lds, st, (const float *)a.act,
+             (const int32_t *)a.ids, (const float *)a.wts, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid);
 }
 template <int QT, int LPR, int XR>
-static void down_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, (const float *)a.act,
-             (const int32_t *)a.ids, (const float *)a.wts, a.T, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid);
+static void down_launch_128(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  down_launch_nt<QT, LPR, XR, 128>(a, grid, lds, st);
+}
+template <int QT, int LPR, int XR>
+static void down_launch_256(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  down_launch_nt<QT, LPR, XR, 256>(a, grid, lds, st);
 }
 
 #define MOE_XR_SWITCH(FN, QT, LPR)                  \
@@ -294,25 +311,34 @@ template <int QT>
 static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
   const int nbH = a.H / 32;
   const int lpr = lanes_for(nbH);
-  const int rows = 256 / lpr;
-  const int maxrows = a.F > a.SF ? a.F : a.SF;
-  const dim3 grid((maxrows + rows - 1) / rows, a.T * a.k + (a.SF > 0 ? a.T : 0));
+  const int rw = 64 / lpr;  // rows per wave task
+  const int tasks = (a.SF + rw - 1) / rw + a.k * ((a.F + rw - 1) / rw);
+  const dim3 grid((tasks + 3) / 4, a.T);
   const size_t lds = (size_t)nbH * (XSTRIDE + 1) * sizeof(float);
-  const int xr = xr_for(a.H);
+  const int xr = xr_for(a.H, 256);
   MOE_LPR_SWITCH(gateup_launch, QT)
   return hipGetLastError();
 }
 
+// Down blocks of 256 threads, or of 128 where that leaves fewer than 256
+// blocks (so the launch covers the 256 CUs) and the act row still stages in
+// 16 float4 per thread.
 template <int QT>
 static hipError_t down_q(const DecodeArgs &a, hipStream_t st) {
   const int nbF = a.F / 32, nbS = a.SF / 32;
   int lpr = lanes_for(nbF);
   if (nbS > 0 && lanes_for(nbS) < lpr) lpr = lanes_for(nbS);
-  const int rows = 256 / lpr;
-  const dim3 grid((a.H + rows - 1) / rows, a.T);
   const size_t lds = (size_t)(a.k * nbF + nbS) * (XSTRIDE + 1) * sizeof(float);
-  const int xr = xr_for(a.k * a.F + a.SF);
-  MOE_LPR_SWITCH(down_launch, QT)
+  const int n = a.k * a.F + a.SF;
+  const bool wide = (size_t)((a.H + 256 / lpr - 1) / (256 / lpr)) * a.T >= 256 || n > 4 * 128 * 16;
+  const int nt = wide ? 256 : 128;
+  const dim3 grid((a.H + nt / lpr - 1) / (nt / lpr), a.T);
+  const int xr = xr_for(n, nt);
+  if (wide) {
+    MOE_LPR_SWITCH(down_launch_256, QT)
+  } else {
+    MOE_LPR_SWITCH(down_launch_128, QT)
+  }
   return hipGetLastError();
 }
 

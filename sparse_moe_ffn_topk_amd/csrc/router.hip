@@ -8,12 +8,13 @@
 // page: router comment and TOPK_SIG_BODY; ling_moe_ssd.js page: routeLing).
 //
 // MI355X design:
-//  * logits: each wave owns one router row (decode) and streams it with
-//    16-byte loads; products and sums in f64 (full-rate on gfx950), one
-//    rounding to f32 at the end.  Large T uses an LDS-tiled f64 kernel.
-//  * selection: one wave per token; expert e sits in lane e%64, slot e/64, so
-//    every comparison is in registers and every reduction is a 6-step
-//    butterfly -- no LDS, no barriers.
+//  * logits: each wave owns one router row (T <= 8) and streams it with
+//    16-byte buffer loads, all issued before the first product; products and
+//    sums in f64 (full-rate on gfx950), one rounding to f32 at the end.  Larger
+//    T uses an LDS-tiled f64 kernel.
+//  * selection: one 256-thread block per token ranks the experts (a score's
+//    rank is the number of experts that beat it), which gives the k argmax
+//    rounds' picks at once.
 #include "moe_common.h"
 #include "moe_launch.h"
 #include "select_block.h"
@@ -23,39 +24,44 @@ namespace moe {
 // ---------------------------------------------------------------- logits --
 
 // T <= 8 tokens: one 64-thread block per router row e; logits[t][e].  A lane
-// holds up to RCH float4 of the row in registers (all loads in flight at once),
-// then runs the tokens over them; products and sums in f64.
-constexpr int RCH = 16;
-template <int TT>
+// takes NC 16-byte chunks of the row per pass and, per token, the matching NC
+// chunks of x; every load of a pass is issued before the first product (buffer
+// loads with an out-of-range offset past the row end read zeros, so there are
+// no branches between them).  Products and sums in f64, one f32 rounding.
+constexpr uint32_t ROUTER_OOB = 0x7ffffff0u;
+template <int TT, int NC>
 __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
                                                     int H, int E, int T, float *__restrict__ logits) {
   const int e = blockIdx.x, lane = threadIdx.x;
-  const float4 *w4 = reinterpret_cast<const float4 *>(W + (size_t)e * H);
-  const int n4 = H >> 2;
-  double acc[TT];
+  const uint32_t rowbytes = (uint32_t)H * 4u;
+  const rsrc_t rw = make_rsrc(W + (size_t)e * H, rowbytes);
+  const rsrc_t rx = make_rsrc(x, (uint32_t)T * rowbytes);
+  double acc[TT][2];
 #pragma unroll
-  for (int t = 0; t < TT; t++) acc[t] = 0.0;
-  for (int c0 = 0; c0 < n4; c0 += 64 * RCH) {
-    float4 w[RCH];
+  for (int t = 0; t < TT; t++) acc[t][0] = acc[t][1] = 0.0;
+  for (uint32_t c0 = 0; c0 < rowbytes; c0 += 1024u * NC) {
+    uint32_t off[NC];
+    u32x4 w[NC];
 #pragma unroll
-    for (int i = 0; i < RCH; i++) {
-      const int c = c0 + lane + 64 * i;
-      w[i] = c < n4 ? w4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < NC; i++) {
+      const uint32_t o = c0 + 16u * (uint32_t)(lane + 64 * i);
+      off[i] = o < rowbytes ? o : ROUTER_OOB;
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off[i], 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < TT; t++) {
       if (t < T) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+        u32x4 v[NC];
 #pragma unroll
-        for (int i = 0; i < RCH; i++) {
-          const int c = c0 + lane + 64 * i;
-          if (c < n4) {
-            const float4 v = x4[c];
-            acc[t] = __builtin_fma((double)w[i].x, (double)v.x, acc[t]);
-            acc[t] = __builtin_fma((double)w[i].y, (double)v.y, acc[t]);
-            acc[t] = __builtin_fma((double)w[i].z, (double)v.z, acc[t]);
-            acc[t] = __builtin_fma((double)w[i].w, (double)v.w, acc[t]);
-          }
+        for (int i = 0; i < NC; i++)
+          v[i] = __builtin_amdgcn_raw_buffer_load_b128(
+              rx, (int)(off[i] == ROUTER_OOB ? ROUTER_OOB : (uint32_t)t * rowbytes + off[i]), 0, 0);
+#pragma unroll
+        for (int i = 0; i < NC; i++) {
+          acc[t][0] = __builtin_fma((double)__uint_as_float(w[i][0]), (double)__uint_as_float(v[i][0]), acc[t][0]);
+          acc[t][1] = __builtin_fma((double)__uint_as_float(w[i][1]), (double)__uint_as_float(v[i][1]), acc[t][1]);
+          acc[t][0] = __builtin_fma((double)__uint_as_float(w[i][2]), (double)__uint_as_float(v[i][2]), acc[t][0]);
+          acc[t][1] = __builtin_fma((double)__uint_as_float(w[i][3]), (double)__uint_as_float(v[i][3]), acc[t][1]);
         }
       }
     }
@@ -63,7 +69,7 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
 #pragma unroll
   for (int t = 0; t < TT; t++) {
     if (t < T) {
-      const double s = wave_sum_d(acc[t]);
+      const double s = wave_sum_d(acc[t][0] + acc[t][1]);
       if (lane == 0) logits[(size_t)t * E + e] = (float)s;
     }
   }
@@ -113,15 +119,32 @@ __global__ __launch_bounds__(256) void k_select(const float *__restrict__ logits
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
                                 hipStream_t st) {
   if (T <= 8) {
-    dim3 grid(E);
+    // Chunks per lane and pass: the whole row in one pass up to H = 4096.
+    const int n16 = (H + 3) / 4;
+    const int nc = (n16 + 63) / 64;
+    const dim3 grid(E);
+#define MOE_ROUTER_ROWS(TT)                                                                              \
+  do {                                                                                                   \
+    if (nc <= 2)                                                                                         \
+      MOE_LAUNCH(1, (k_router_rows<TT, 2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+    else if (nc <= 4)                                                                                    \
+      MOE_LAUNCH(1, (k_router_rows<TT, 4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+    else if (nc <= 8)                                                                                    \
+      MOE_LAUNCH(1, (k_router_rows<TT, 8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+    else if (nc <= 12)                                                                                   \
+      MOE_LAUNCH(1, (k_router_rows<TT, 12>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);             \
+    else                                                                                                 \
+      MOE_LAUNCH(1, (k_router_rows<TT, 16>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);             \
+  } while (0)
     if (T == 1)
-      MOE_LAUNCH(1, (k_router_rows<1>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
+      MOE_ROUTER_ROWS(1);
     else if (T <= 2)
-      MOE_LAUNCH(1, (k_router_rows<2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
+      MOE_ROUTER_ROWS(2);
     else if (T <= 4)
-      MOE_LAUNCH(1, (k_router_rows<4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
+      MOE_ROUTER_ROWS(4);
     else
-      MOE_LAUNCH(1, (k_router_rows<8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);
+      MOE_ROUTER_ROWS(8);
+#undef MOE_ROUTER_ROWS
   } else {
     dim3 grid((E + 15) / 16, (T + 15) / 16);
     MOE_LAUNCH(1, k_router_tiled, grid, dim3(256), 0u, st, W, x, H, E, T, logits);

@@ -14,11 +14,14 @@
 // rounds is fixed by ranks: expert e is pick number
 //   rank(e) = #{e' : s(e') > s(e), or s(e') == s(e) and e' < e}
 // whenever rank(e) < k.  Here the threads rank experts in parallel, in two
-// stages: each wave ranks the experts of its own segment (64 of every 256)
-// and keeps its k best as candidates; the candidates (at most 4k) are then
-// ranked against each other.  Every global top-k expert is a candidate of its
-// segment, and every expert that beats it is one too, so the candidate ranks
-// are the exact pick positions.  Kept groups use the same rank rule.
+// stages: each wave finds the k best experts of its own segment (64 of every
+// 256) -- after dropping, in registers, every expert that k others of its
+// 16-lane row already beat -- and keeps them as candidates; the candidates
+// (at most 4k) are then ranked against each other.  Every global top-k expert
+// is a candidate of its segment, and every expert that beats it is one too,
+// so the candidate ranks are the exact pick positions.  Experts are compared
+// through 64-bit keys (sel_key) whose unsigned order is the beats order, so a
+// comparison is one integer compare.  Kept groups use the same rank rule.
 //
 // The sigmoid of the f32 logit is evaluated in double and rounded once to
 // f32, so equal f32 logits always give equal scores.
@@ -31,118 +34,225 @@ namespace moe {
 constexpr float NEG = -3.402823466e38f;  // below every score
 constexpr int SEL_MAX_E = 512, SEL_MAX_K = 32, SEL_MAX_G = 64;
 
-struct SelShared {
-  float s[SEL_MAX_E];  // selection scores (NEG: padding or dropped group)
-  float p[SEL_MAX_E];  // sigmoids
+struct alignas(16) SelShared {
+  unsigned long long sk[4][128];         // per wave: keys of its stage-1 survivors
+  float s[SEL_MAX_E];                    // selection scores
+  float p[SEL_MAX_E];                    // sigmoids
   float gs[SEL_MAX_G];
   int kept[SEL_MAX_G];
-  float cs[4 * SEL_MAX_K];  // candidates: score and expert
-  int ce[4 * SEL_MAX_K];
+  unsigned long long ck[4 * SEL_MAX_K];  // candidate keys (0: empty slot)
   int pick[SEL_MAX_K];
   float pp[SEL_MAX_K];
 };
 
+// Ranking key: a beats b (higher score, or equal score and lower index) exactly
+// when key(a) > key(b) as unsigned integers.  High word: the score's bits mapped
+// so that unsigned order is float order (scores are never NaN; -0 is folded to
+// +0 first, as float comparison treats them equal); low word: ~expert, so of
+// two equal scores the lower index has the larger key.  Every real key is
+// nonzero (the high word of any non-NaN float is).
+__device__ __forceinline__ unsigned long long sel_key(float s, int e) {
+  const uint32_t b = __float_as_uint(s + 0.0f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)~e;
+}
+
+// Number of the other 15 lanes of this lane's 16-lane row holding a larger h
+// (DPP row rotations: register traffic only).
+template <int N>
+__device__ __forceinline__ int row_count_above(uint32_t h) {
+  if constexpr (N == 0) {
+    return 0;
+  } else {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0x120 + N, 0xF, 0xF, false);  // row_ror:N
+    return (int)(o > h) + row_count_above<N - 1>(h);
+  }
+}
+
 // a beats b: higher score, or equal score and lower index
 __device__ __forceinline__ int beats(float sa, int ea, float sb, int eb) { return sa > sb || (sa == sb && ea < eb); }
 
-// Route one token with the whole block (blockDim.x == 256; every thread must
-// call it).  On return (after a barrier) sh.pick[0..k) holds the experts in
-// pick order and sh.pp[0..k) their sigmoids; if w_out is given, threads
-// 0..k-1 write the k weights to it.
-__device__ __forceinline__ void select_block(const float *__restrict__ l, const float *__restrict__ bias,
-                                             const SelParams &P, SelShared &sh, float *__restrict__ w_out) {
+// One token's router inputs for thread tid: experts tid and tid + 256.
+struct SelIn {
+  float l[2], b[2];
+};
+
+// Issue the loads of the logits (and bias) the calling thread ranks; split
+// from select_rank() so a caller can put other loads behind them and still
+// wait for these first (vector loads retire in order).  Experts past E read
+// as 0 (buffer loads past the range return zeros).
+__device__ __forceinline__ void select_load(const float *__restrict__ l, const float *__restrict__ bias,
+                                            const SelParams &P, SelIn &in) {
+  const uint32_t tid = threadIdx.x;
+  const rsrc_t rl = make_rsrc(l, (uint32_t)P.E * 4u);
+#pragma unroll
+  for (int r = 0; r < 2; r++) in.l[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (int)((tid + 256u * r) * 4u), 0, 0));
+  if (bias) {
+    const rsrc_t rb = make_rsrc(bias, (uint32_t)P.E * 4u);
+#pragma unroll
+    for (int r = 0; r < 2; r++) in.b[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)((tid + 256u * r) * 4u), 0, 0));
+  } else {
+    in.b[0] = in.b[1] = 0.f;
+  }
+}
+
+// Top-2 of the PG scores held by each aligned run of PG lanes (PG a power of
+// two <= 64), as a multiset (an equal value counts as the second); every lane
+// of the run gets the pair.
+__device__ __forceinline__ void run_top2(float &a, float &b, int PG) {
+  for (int m = PG >> 1; m >= 1; m >>= 1) {
+    const float a2 = __shfl_xor(a, m, 64), b2 = __shfl_xor(b, m, 64);
+    const float lo = fminf(a, a2);
+    a = fmaxf(a, a2);
+    b = fmaxf(lo, fmaxf(b, b2));
+  }
+}
+
+// Route one token with the whole block from inputs loaded by select_load()
+// (blockDim.x == 256; every thread must call it).  On return (after a
+// barrier) sh.pick[0..k) holds the experts in pick order and sh.pp[0..k) their
+// sigmoids; if w_out is given, threads 0..k-1 write the k weights to it.
+__device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P, SelShared &sh,
+                                            float *__restrict__ w_out) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int R = (P.E + 255) >> 8;  // experts per thread (1 or 2)
-  for (int r = 0; r < R; r++) {
+  float sv[2];
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
     const int e = tid + 256 * r;
     float p = 0.f, s = NEG;
     if (e < P.E) {
-      p = (float)(1.0 / (1.0 + exp(-(double)l[e])));
-      s = p + (bias ? bias[e] : 0.f);
+      p = (float)(1.0 / (1.0 + exp(-(double)in.l[r])));
+      s = p + in.b[r];
     }
-    sh.s[e] = s;
-    sh.p[e] = p;
+    sv[r] = s;
+    if (r < R) {
+      sh.s[e] = s;
+      sh.p[e] = p;
+    }
   }
-  if (tid < 4 * SEL_MAX_K) {
-    sh.cs[tid] = NEG;
-    sh.ce[tid] = 0x7fffffff;
-  }
-  __syncthreads();
+  if (tid < 4 * SEL_MAX_K) sh.ck[tid] = 0ull;
 
   if (P.Gu < P.G) {
     const int PG = P.E / P.G;
-    if (tid < P.G) {
-      // the group's two largest scores, an equal value counting as the second
-      float a = NEG, b = NEG;
-      for (int e = tid * PG; e < (tid + 1) * PG; e++) {
-        const float v = sh.s[e];
-        if (v > a) {
-          b = a;
-          a = v;
-        } else if (v > b) {
-          b = v;
+    if (PG <= 64 && (PG & (PG - 1)) == 0) {
+      // a group is an aligned run of PG lanes of one wave: butterfly top-2
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        if (r < R) {
+          float a = sv[r], b = NEG;
+          run_top2(a, b, PG);
+          const int e = tid + 256 * r;
+          if (e < P.E && (e & (PG - 1)) == 0) sh.gs[e / PG] = a + b;
         }
       }
-      sh.gs[tid] = a + b;
+      __syncthreads();
+    } else {
+      __syncthreads();
+      if (tid < P.G) {
+        float a = NEG, b = NEG;
+        for (int e = tid * PG; e < (tid + 1) * PG; e++) {
+          const float v = sh.s[e];
+          const float lo = fminf(a, v);
+          a = fmaxf(a, v);
+          b = fmaxf(b, lo);
+        }
+        sh.gs[tid] = a + b;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (tid < P.G) {
       const float mine = sh.gs[tid];
       int rank = 0;
+#pragma unroll 8
       for (int g = 0; g < P.G; g++) rank += beats(sh.gs[g], g, mine, tid);
       sh.kept[tid] = rank < P.Gu;
     }
     __syncthreads();
-    for (int r = 0; r < R; r++) {
-      const int e = tid + 256 * r;
-      if (e < P.E && !sh.kept[e / PG]) sh.s[e] = NEG;
-    }
-    __syncthreads();
+  }
+  // keys; padding experts and dropped groups get 0, which beats nothing
+  unsigned long long kr[2];
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const int e = tid + 256 * r;
+    const bool real = r < R && e < P.E && (P.Gu >= P.G || sh.kept[e / (P.E / P.G)]);
+    kr[r] = real ? sel_key(sv[r], e) : 0ull;
   }
 
-  // stage 1: rank within the wave's segment {64*wave + i + 256*r}
-  for (int r = 0; r < R; r++) {
-    const int e = tid + 256 * r;
-    if (e < P.E) {
-      const float mine = sh.s[e];
+  // stage 1: the k best of the wave's segment {64*wave + i + 256*r}.
+  // (a) an expert with k or more strictly larger score words in its 16-lane
+  // row has k experts beating it and is dropped; (b) the survivors' keys are
+  // compacted per wave; (c) each survivor is ranked among them.  Everything
+  // that beats a top-k expert of the segment survives (a), so the survivor
+  // ranks below k are its exact ranks in the segment.
+  const int lane = tid & 63;
+  bool surv[2];
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const int above = row_count_above<15>((uint32_t)(kr[r] >> 32));  // every lane takes part
+    surv[r] = kr[r] != 0ull && above < P.k;
+  }
+  int ns = 0;
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    const unsigned long long m = __ballot(surv[r]);
+    if (surv[r]) {
+      const int pos = ns + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      sh.sk[wave][pos] = kr[r];
+    }
+    ns += __popcll(m);
+  }
+  if (lane == 0 && (ns & 1)) sh.sk[wave][ns] = 0ull;  // pad to pairs
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 2; r++) {
+    if (surv[r]) {
+      const unsigned long long mine = kr[r];
       int rank = 0;
-      for (int r2 = 0; r2 < R; r2++) {
-        const int e0 = 256 * r2 + 64 * wave;
-        const float *seg = sh.s + e0;
-#pragma unroll 4
-        for (int i = 0; i < 64; i += 4) {
-          const float4 v = *reinterpret_cast<const float4 *>(seg + i);
-          rank += beats(v.x, e0 + i, mine, e) + beats(v.y, e0 + i + 1, mine, e) + beats(v.z, e0 + i + 2, mine, e) +
-                  beats(v.w, e0 + i + 3, mine, e);
-        }
+      for (int c = 0; c < ns; c += 2) {
+        const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(&sh.sk[wave][c]);
+        rank += (v.x > mine) + (v.y > mine);
       }
-      if (rank < P.k) {
-        sh.cs[wave * P.k + rank] = mine;
-        sh.ce[wave * P.k + rank] = e;
-      }
+      if (rank < P.k) sh.ck[wave * P.k + rank] = mine;
     }
   }
   __syncthreads();
 
-  // stage 2: rank among the candidates
+  // stage 2: rank among the candidates (4k slots; a dropped expert's key and
+  // an empty slot are 0 and are never picked: k <= the kept experts)
   const int C = 4 * P.k;
-  if (tid < C && sh.ce[tid] != 0x7fffffff) {
-    const float mine = sh.cs[tid];
-    const int e = sh.ce[tid];
-    int rank = 0;
-    for (int c = 0; c < C; c++) rank += beats(sh.cs[c], sh.ce[c], mine, e);
-    if (rank < P.k) {
-      sh.pick[rank] = e;
-      sh.pp[rank] = sh.p[e];
+  if (tid < C) {
+    const unsigned long long mine = sh.ck[tid];
+    if (mine != 0ull) {
+      int rank = 0;
+#pragma unroll 4
+      for (int c = 0; c < C; c += 2) {
+        const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(sh.ck + c);
+        rank += (v.x > mine) + (v.y > mine);
+      }
+      if (rank < P.k) {
+        const int e = (int)~(uint32_t)mine;
+        sh.pick[rank] = e;
+        sh.pp[rank] = sh.p[e];
+      }
     }
   }
   __syncthreads();
   if (w_out && tid < P.k) {
     float wsum = 0.f;
+#pragma unroll 8
     for (int j = 0; j < P.k; j++) wsum += sh.pp[j];  // f32, pick order
     wsum = fmaxf(wsum, P.wsum_min);
     w_out[tid] = sh.pp[tid] / wsum * P.scale;
   }
+}
+
+// select_load() then select_rank().
+__device__ __forceinline__ void select_block(const float *__restrict__ l, const float *__restrict__ bias,
+                                             const SelParams &P, SelShared &sh, float *__restrict__ w_out) {
+  SelIn in;
+  select_load(l, bias, P, in);
+  select_rank(in, P, sh, w_out);
 }
 
 }  // namespace moe
