@@ -85,6 +85,10 @@ template <> struct QBlock<MOE_Q4_0> {
 __device__ __forceinline__ void nib_word_dot(uint32_t w, const float4 &xl, const float4 &xh, float &lo,
                                              float &hi) {
   uint32_t l = w & 0x0F0F0F0Fu, h = w & 0xF0F0F0F0u;
+  // hide the masks' known bits from the compiler so that each byte converts
+  // with one v_cvt_f32_ubyteN (it otherwise extracts with v_bfe first)
+  asm("" : "+v"(l));
+  asm("" : "+v"(h));
   lo = __builtin_fmaf((float)(l & 0xff), xl.x, lo);
   lo = __builtin_fmaf((float)((l >> 8) & 0xff), xl.y, lo);
   lo = __builtin_fmaf((float)((l >> 16) & 0xff), xl.z, lo);

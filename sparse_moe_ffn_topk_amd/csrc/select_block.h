@@ -35,7 +35,7 @@ constexpr float NEG = -3.402823466e38f;  // below every score
 constexpr int SEL_MAX_E = 512, SEL_MAX_K = 32, SEL_MAX_G = 64;
 
 struct alignas(16) SelShared {
-  unsigned long long sk[4][128];         // per wave: keys of its stage-1 survivors
+  unsigned long long sk[4][136];         // per wave: keys of its stage-1 survivors (zero-padded to 8)
   float s[SEL_MAX_E];                    // selection scores
   float p[SEL_MAX_E];                    // sigmoids
   float gs[SEL_MAX_G];
@@ -189,8 +189,11 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
   bool surv[2];
 #pragma unroll
   for (int r = 0; r < 2; r++) {
-    const int above = row_count_above<15>((uint32_t)(kr[r] >> 32));  // every lane takes part
-    surv[r] = kr[r] != 0ull && above < P.k;
+    surv[r] = false;
+    if (r < R) {  // (uniform) every lane takes part in the row moves
+      const int above = row_count_above<15>((uint32_t)(kr[r] >> 32));
+      surv[r] = kr[r] != 0ull && above < P.k;
+    }
   }
   int ns = 0;
 #pragma unroll
@@ -202,16 +205,18 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
     }
     ns += __popcll(m);
   }
-  if (lane == 0 && (ns & 1)) sh.sk[wave][ns] = 0ull;  // pad to pairs
+  if (lane < 8 && ns + lane < ((ns + 7) & ~7)) sh.sk[wave][ns + lane] = 0ull;  // pad to 8
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < 2; r++) {
     if (surv[r]) {
       const unsigned long long mine = kr[r];
       int rank = 0;
-      for (int c = 0; c < ns; c += 2) {
-        const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(&sh.sk[wave][c]);
-        rank += (v.x > mine) + (v.y > mine);
+      for (int c = 0; c < ns; c += 8) {  // four reads in flight per step
+        const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(&sh.sk[wave][c]);
+        const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
+        rank += (v0.x > mine) + (v0.y > mine) + (v1.x > mine) + (v1.y > mine) + (v2.x > mine) + (v2.y > mine) +
+                (v3.x > mine) + (v3.y > mine);
       }
       if (rank < P.k) sh.ck[wave * P.k + rank] = mine;
     }
@@ -225,10 +230,11 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
     const unsigned long long mine = sh.ck[tid];
     if (mine != 0ull) {
       int rank = 0;
-#pragma unroll 4
-      for (int c = 0; c < C; c += 2) {
-        const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(sh.ck + c);
-        rank += (v.x > mine) + (v.y > mine);
+      for (int c = 0; c < C; c += 8) {  // slots past C are 0; C <= 4 * SEL_MAX_K, a multiple of 8
+        const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(sh.ck + c);
+        const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
+        rank += (v0.x > mine) + (v0.y > mine) + (v1.x > mine) + (v1.y > mine) + (v2.x > mine) + (v2.y > mine) +
+                (v3.x > mine) + (v3.y > mine);
       }
       if (rank < P.k) {
         const int e = (int)~(uint32_t)mine;
