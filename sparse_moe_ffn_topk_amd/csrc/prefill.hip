@@ -175,17 +175,101 @@ struct GemmArgs {
   int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
 };
 
-constexpr int KC = 8;           // Q4 blocks (x 32 k) of A staged per chunk
-constexpr int KCH = KC * 32;    // k values per chunk
+// K is walked in chunks of KB Q4 blocks.  Per chunk a block stages, in LDS,
+// the raw bytes of its 256 weight rows (BROW bytes each: 4 x 20, or 4 x 18
+// plus 2 bytes of alignment slack) read with contiguous 16-byte loads, and
+// its 16 tokens' inputs as f16 hi + lo in the MFMA lanes' k order.
+constexpr int KB = 4;
+constexpr int BROW = 80;
+constexpr int BRW = BROW / 4;          // dwords per staged row
+constexpr int APAD = KB * 32 + 8;      // f16 per staged input row (16-byte pad)
+
+// A chunk: 16 threads per token, 8 consecutive k each.
+struct AStage {
+  float v[8];
+};
+// (buffer loads: past the row, or for no row, they read zeros -- no branches,
+// so the loads stay in order behind the weight loads)
+__device__ __forceinline__ void a_load(AStage &st, const float *arows, int astride, int K, int row, int kc) {
+  const int seg = threadIdx.x & 15;
+  const uint32_t kb = (uint32_t)(kc * 32 + seg * 8);
+  const rsrc_t r = make_rsrc(arows + (size_t)(row >= 0 ? row : 0) * astride, (uint32_t)K * 4u);
+#pragma unroll
+  for (int i = 0; i < 8; i += 4) {
+    const uint32_t off = (row >= 0 && kb + i < (uint32_t)K) ? (kb + i) * 4u : 0x7ffffff0u;
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    const uint32_t a0 = v.x, a1 = v.y, a2 = v.z, a3 = v.w;
+    st.v[i] = __uint_as_float(a0);
+    st.v[i + 1] = __uint_as_float(a1);
+    st.v[i + 2] = __uint_as_float(a2);
+    st.v[i + 3] = __uint_as_float(a3);
+  }
+}
+// k within the block kk = (seg%4)*8 + i; the lane holding it has k-octet
+// (kk%16)/8 + 2*(kk/16) and slot kperm(kk%8).  asum[block][token].
+__device__ __forceinline__ void a_store(const AStage &st, _Float16 (*ahi)[APAD], _Float16 (*alo)[APAD],
+                                        float (*asum)[16]) {
+  const int m = threadIdx.x >> 4, seg = threadIdx.x & 15;
+  const int blk = seg >> 2;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int kk = (seg & 3) * 8 + i;
+    const int q8 = ((kk & 15) >> 3) + 2 * (kk >> 4);
+    const int col = blk * 32 + q8 * 8 + kperm(kk & 7);
+    const _Float16 h = (_Float16)st.v[i];
+    ahi[m][col] = h;
+    alo[m][col] = (_Float16)(st.v[i] - (float)h);
+    s += st.v[i];
+  }
+  s += __shfl_xor(s, 1, 64);  // the four threads of one block
+  s += __shfl_xor(s, 2, 64);
+  if ((seg & 3) == 0) asum[blk][m] = s;
+}
+
+// Scale, offset and the lane's 8 nibble bytes of block jb of a staged row
+// (w: the row's BRW dwords; o0: byte offset of block 0 in them).
+template <int QT> struct QStaged;
+template <> struct QStaged<MOE_Q4_1> {
+  static __device__ __forceinline__ void get(const uint32_t *w, int, int jb, int half, float &d, float &m,
+                                             u32x2 &nb) {
+    const uint32_t dm = w[5 * jb];
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm & 0xffffu));
+    m = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm >> 16));
+    nb.x = w[5 * jb + 1 + 2 * half];
+    nb.y = w[5 * jb + 2 + 2 * half];
+  }
+};
+template <> struct QStaged<MOE_Q4_0> {
+  static __device__ __forceinline__ void get(const uint32_t *w, int o0, int jb, int half, float &d, float &m,
+                                             u32x2 &nb) {
+    const int o = o0 + 18 * jb;  // even
+    const uint32_t dw = w[o >> 2];
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((o & 2) ? (dw >> 16) : (dw & 0xffffu)));
+    m = -8.0f * d;
+    const int s = o + 2 + 8 * half, a = s >> 2;
+    const uint32_t w0 = w[a], w1 = w[a + 1], w2 = w[a + 2];
+    if (s & 2) {
+      nb.x = __builtin_amdgcn_alignbyte(w1, w0, 2);
+      nb.y = __builtin_amdgcn_alignbyte(w2, w1, 2);
+    } else {
+      nb.x = w0;
+      nb.y = w1;
+    }
+  }
+};
 
 // grid.x: routed tiles (16 tokens of one expert) then shared tiles (16 tokens);
 // grid.y: slices of 256 output rows; 4 waves x 64 rows (4 MFMA tiles of 16).
+// Each chunk: registers -> LDS, barrier, issue the next chunk's loads, MFMAs
+// from LDS, barrier.  Blocks past K get d = m = 0 (their inputs are 0 too).
 template <int QT, int MODE>
 __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   constexpr int BS = QPart<QT>::bytes;
   constexpr int NM = MODE == GG_GATEUP ? 2 : 1;  // weight matrices
-  __shared__ _Float16 ahi[16][KCH + 8], alo[16][KCH + 8];
-  __shared__ float asum[16][KC];
+  __shared__ __attribute__((aligned(16))) uint32_t bst[NM][256][BRW];
+  __shared__ __attribute__((aligned(16))) _Float16 ahi[16][APAD], alo[16][APAD];
+  __shared__ __attribute__((aligned(16))) float asum[KB][16];
   __shared__ int rowid[16];  // A row per tile token (-1: none)
   __shared__ int outid[16];  // output row per tile token
   __shared__ float outw[16];
@@ -229,11 +313,38 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   const int r0 = blockIdx.y * 256;
   if (r0 >= R) return;
   const int nbK = K / 32;
-  const uint32_t mbytes = (uint32_t)((size_t)R * nbK * BS);
+  const uint32_t rowbytes = (uint32_t)nbK * BS;
+  const uint32_t mbytes = (uint32_t)((size_t)R * rowbytes);
   const rsrc_t rw0 = make_rsrc(m0p, mbytes);
   const rsrc_t rw1 = NM == 2 ? make_rsrc(m1p, mbytes) : rw0;
   const float *arows = MODE == GG_GATEUP ? a.x : (shared ? a.act_sh : a.act);
   const int astride = K;
+
+  // weight pieces of this thread: p = tid + 256 i (i < 5) -> row p / 5, 16 bytes p % 5
+  u32x4 breg[NM][5];
+  auto b_issue = [&](int kc) {
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) {
+#pragma unroll
+      for (int i = 0; i < 5; i++) {
+        const int p = tid + 256 * i, row = p / 5, j = p - 5 * row;
+        const int grow = r0 + row;
+        const uint32_t seg = (uint32_t)grow * rowbytes + (uint32_t)kc * BS;
+        const uint32_t off = (grow < R && kc < nbK) ? (seg & ~3u) + 16u * j : 0x7ffffff0u;
+        breg[mt][i] = __builtin_amdgcn_raw_buffer_load_b128(mt == 0 ? rw0 : rw1, (int)off, 0, 0);
+      }
+    }
+  };
+  auto b_store = [&]() {
+#pragma unroll
+    for (int mt = 0; mt < NM; mt++) {
+#pragma unroll
+      for (int i = 0; i < 5; i++) {
+        const int p = tid + 256 * i, row = p / 5, j = p - 5 * row;
+        *reinterpret_cast<u32x4 *>(&bst[mt][row][4 * j]) = breg[mt][i];
+      }
+    }
+  };
 
   // lane roles in the MFMA: token m = lane%16 (A) / column n = lane%16 (B),
   // k-octet kq = lane/16; D rows (tokens) 4*kq + i, column n
@@ -245,63 +356,41 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   for (int mt = 0; mt < NM; mt++)
 #pragma unroll
     for (int c = 0; c < 4; c++) acc[mt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int rbase = r0 + wave * 64;
+  // byte offset of block 0 within each of this lane's staged rows (Q4_0 rows
+  // may start 2 bytes past a dword; chunks start at multiples of 4 blocks)
+  int o0[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) o0[c] = (int)(((uint32_t)(r0 + wave * 64 + 16 * c + n) * rowbytes) & 3u);
 
-  __syncthreads();
-  for (int kc = 0; kc < nbK; kc += KC) {
-    // stage A: 16 tokens x KCH k values as f16 hi + lo, in the lanes' k order,
-    // plus each token's per-block sums
-    {
-      const int m = tid >> 4, seg = tid & 15;  // 16 threads per token, 16 k each
-      const int kb = kc * 32 + seg * 16;
-      const int row = rowid[m];
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (row >= 0 && kb + i < K) f = *reinterpret_cast<const float4 *>(arows + (size_t)row * astride + kb + i);
-        v[i] = f.x;
-        v[i + 1] = f.y;
-        v[i + 2] = f.z;
-        v[i + 3] = f.w;
-      }
-      // k within the block: kk = seg%2*16 + i; the lane holding it has
-      // kq = (kk%16)/8 + 2*(kk/16) and slot kperm(kk%8)
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int kk = (seg & 1) * 16 + i;              // k within the Q4 block
-        const int blk = seg >> 1;                        // block within the chunk
-        const int q8 = ((kk & 15) >> 3) + 2 * (kk >> 4); // k-octet of the lane
-        const int col = blk * 32 + q8 * 8 + kperm(kk & 7);
-        const _Float16 h = (_Float16)v[i];
-        ahi[m][col] = h;
-        alo[m][col] = (_Float16)(v[i] - (float)h);
-        s += v[i];
-      }
-      s += __shfl_xor(s, 1, 64);  // the two threads of one block
-      if ((seg & 1) == 0) asum[m][seg >> 1] = s;
-    }
+  __syncthreads();  // rowid
+  const int arow = rowid[tid >> 4];
+  AStage ast;
+  b_issue(0);
+  a_load(ast, arows, astride, K, arow, 0);
+
+  for (int kc = 0; kc < nbK; kc += KB) {
+    b_store();
+    a_store(ast, ahi, alo, asum);
     __syncthreads();
-    for (int b = 0; b < KC && kc + b < nbK; b++) {
-      const int bk = kc + b;
-      const half8 xh = *reinterpret_cast<const half8 *>(&ahi[n][b * 32 + kq * 8]);
-      const half8 xl = *reinterpret_cast<const half8 *>(&alo[n][b * 32 + kq * 8]);
-      float sx[4];
+    if (kc + KB < nbK) {
+      b_issue(kc + KB);
+      a_load(ast, arows, astride, K, arow, kc + KB);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; i++) sx[i] = asum[4 * kq + i][b];
+    for (int jb = 0; jb < KB; jb++) {
+      const bool valid = kc + jb < nbK;
+      const half8 xh = *reinterpret_cast<const half8 *>(&ahi[n][jb * 32 + kq * 8]);
+      const half8 xl = *reinterpret_cast<const half8 *>(&alo[n][jb * 32 + kq * 8]);
+      const float4 sx4 = *reinterpret_cast<const float4 *>(&asum[jb][4 * kq]);
+      const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
 #pragma unroll
       for (int mt = 0; mt < NM; mt++) {
-        const rsrc_t rw = mt == 0 ? rw0 : rw1;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          const int row = rbase + 16 * c + n;
-          const uint32_t off = row < R ? (uint32_t)(row * nbK + bk) * BS : 0x7ffffff0u;
-          uint32_t dm;
-          u32x2 nb;
-          QPart<QT>::load(rw, off, half, dm, nb);
           float d, m;
-          QPart<QT>::scales(dm, off, d, m);
+          u32x2 nb;
+          QStaged<QT>::get(bst[mt][wave * 64 + 16 * c + n], o0[c], jb, half, d, m, nb);
+          if (!valid) d = m = 0.f;
           const half8 q = nibbles_f16(nb, hin);
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
           z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, q, z, 0, 0, 0);
@@ -316,7 +405,8 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
     __syncthreads();
   }
 
-  // epilogue: this lane holds D[token 4*kq + i][row rbase + 16c + n]
+  // epilogue: this lane holds D[token 4*kq + i][row r0 + wave*64 + 16c + n]
+  const int rbase = r0 + wave * 64;
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const int row = rbase + 16 * c + n;
