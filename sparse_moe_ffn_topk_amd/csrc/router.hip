@@ -11,7 +11,7 @@
 //  * logits: each wave owns one router row (T <= 8) and streams it with
 //    16-byte buffer loads, all issued before the first product; products and
 //    sums in f64 (full-rate on gfx950), one rounding to f32 at the end.  Larger
-//    T uses an LDS-tiled f64 kernel.
+//    T runs on the f64 matrix cores (v_mfma_f64_16x16x4f64).
 //  * selection: one 256-thread block per token ranks the experts (a score's
 //    rank is the number of experts that beat it), which gives the k argmax
 //    rounds' picks at once.
@@ -75,31 +75,65 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
   }
 }
 
-// Any T: 16 router rows x 16 tokens per 256-thread block, K staged through
-// LDS in chunks of 64; thread (r, t) accumulates one logit in f64.
-__global__ __launch_bounds__(256) void k_router_tiled(const float *__restrict__ W, const float *__restrict__ x,
-                                                      int H, int E, int T, float *__restrict__ logits) {
-  __shared__ float ws[16][65];
-  __shared__ float xs[16][65];
-  const int tid = threadIdx.x;
-  const int r = tid >> 4, tt = tid & 15;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-  double acc = 0.0;
-  for (int k0 = 0; k0 < H; k0 += 64) {
-    // 16 rows x 64 columns of W and of x: 1024 floats each, 4 per thread.
-    for (int i = tid; i < 1024; i += 256) {
-      int rr = i >> 6, kk = i & 63;
-      int e = e0 + rr, t = t0 + rr, k = k0 + kk;
-      ws[rr][kk] = (e < E && k < H) ? W[(size_t)e * H + k] : 0.f;
-      xs[rr][kk] = (t < T && k < H) ? x[(size_t)t * H + k] : 0.f;
+// T > 8: logits = x W^T on v_mfma_f64_16x16x4f64 (f32 inputs are exact in
+// f64, so products are exact and sums are f64, as in the row kernel).  A block
+// takes 16 router rows x 64 tokens; wave w the tokens 16w..16w+15.  Lane l
+// feeds A = x[token l%16][h + l/16] and B = W[row l%16][h + l/16] and holds
+// D[token l/16 + 4i][row l%16], i < 4.  W and x are staged through LDS in
+// chunks of RKT columns (16-byte loads, next chunk prefetched into registers);
+// columns past H, rows past E and tokens past T read as zeros.
+constexpr int RKT = 64;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W, const float *__restrict__ x, int H,
+                                                     int E, int T, float *__restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) float ws[16][RKT + 4];
+  __shared__ __attribute__((aligned(16))) float xs[64][RKT + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 64;
+  const int ne = min(16, E - e0), nt = min(64, T - t0);
+  const rsrc_t rW = make_rsrc(W + (size_t)e0 * H, (uint32_t)ne * (uint32_t)H * 4u);
+  const rsrc_t rX = make_rsrc(x + (size_t)t0 * H, (uint32_t)nt * (uint32_t)H * 4u);
+  // staging roles: W row tid/16, x rows (tid + 256 i)/16; 16-byte column c4 = tid % 16
+  const int c4 = tid & 15;
+  u32x4 wr, xr[4];
+  auto issue = [&](int h0) {
+    const int h = h0 + 4 * c4;
+    {
+      const int r = tid >> 4;
+      wr = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = (tid + 256 * i) >> 4;
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
+    }
+  };
+  auto put = [&]() {
+    *reinterpret_cast<u32x4 *>(&ws[tid >> 4][4 * c4]) = wr;
+#pragma unroll
+    for (int i = 0; i < 4; i++) *reinterpret_cast<u32x4 *>(&xs[(tid + 256 * i) >> 4][4 * c4]) = xr[i];
+  };
+  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  const int m = lane & 15, kq = lane >> 4;
+  issue(0);
+  for (int h0 = 0; h0 < H; h0 += RKT) {
+    put();
+    __syncthreads();
+    if (h0 + RKT < H) issue(h0 + RKT);
+#pragma unroll
+    for (int kk = 0; kk < RKT; kk += 8) {
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xs[16 * wave + m][kk + kq], (double)ws[m][kk + kq], acc0, 0,
+                                                  0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xs[16 * wave + m][kk + 4 + kq], (double)ws[m][kk + 4 + kq],
+                                                  acc1, 0, 0, 0);
     }
     __syncthreads();
-#pragma unroll 16
-    for (int kk = 0; kk < 64; kk++) acc = __builtin_fma((double)ws[r][kk], (double)xs[tt][kk], acc);
-    __syncthreads();
   }
-  const int e = e0 + r, t = t0 + tt;
-  if (e < E && t < T) logits[(size_t)t * E + e] = (float)acc;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int t = 16 * wave + kq + 4 * i, e = m;
+    if (t < nt && e < ne) logits[(size_t)(t0 + t) * E + e0 + e] = (float)(acc0[i] + acc1[i]);
+  }
 }
 
 // ---------------------------------------------------------------- select --
@@ -146,8 +180,8 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
       MOE_ROUTER_ROWS(8);
 #undef MOE_ROUTER_ROWS
   } else {
-    dim3 grid((E + 15) / 16, (T + 15) / 16);
-    MOE_LAUNCH(1, k_router_tiled, grid, dim3(256), 0u, st, W, x, H, E, T, logits);
+    const dim3 grid((E + 15) / 16, (T + 63) / 64);
+    MOE_LAUNCH(1, k_router_mfma, grid, dim3(256), 0u, st, W, x, H, E, T, logits);
   }
   return hipGetLastError();
 }
