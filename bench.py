@@ -40,25 +40,96 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+# Sources each dominant kernel is built from: its committed traffic counters
+# are used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "gateup_swiglu": ("moe_common.h", "select_block.h", "ffn_decode.h", "ffn_decode_q41.hip", "ffn_decode_q40.hip"),
+    "group_gateup": ("moe_common.h", "prefill.hip"),
+}
+KERNEL_SYMBOLS = {"gateup_swiglu": "k_gateup_swiglu", "group_gateup": "k_group_gemm<1, 0>"}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for fn in ("moe_common.h", "select_block.h", "ffn_decode.h", "ffn_decode_q41.hip"):
+    for fn in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sparse_moe_ffn_topk_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
+def traffic_path(kernel, workload, ext):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.{ext}")
+
+
+def load_traffic(kernel, workload):
     """HBM traffic per launch of the dominant kernel from committed rocprofv3 counter runs,
     only if they were taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", f"gateup_swiglu_{workload}_traffic.json")
+    p = traffic_path(kernel, workload, "json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha") != kernel_source_hash():
+    if d.get("kernel_source_sha") != kernel_source_hash(kernel):
         return None
     return d.get("bytes_per_launch")
+
+
+def _pmc_means(run_dir, counter):
+    """Mean per-dispatch value of one counter, per kernel name, from a rocprofv3 --pmc output folder."""
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(run_dir, "*.db")) + glob.glob(os.path.join(run_dir, "*", "*.db"))
+    if not dbs:
+        raise FileNotFoundError(f"no rocprofv3 database under {run_dir}")
+    con = sqlite3.connect(dbs[0])
+    acc = {}
+    for name, val in con.execute("select name, counter_value from pmc_events where counter_name = ?", (counter,)):
+        acc.setdefault(name, []).append(val)
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def write_traffic(args):
+    """profiles/<kernel>_<workload>_traffic.{json,md} from four rocprofv3 --pmc runs: FETCH_SIZE and
+    WRITE_SIZE of the workload, and of the copy calibration (a 1 GiB device copy)."""
+    kernel = "group_gateup" if args.workload == "prefill" else "gateup_swiglu"
+    fetch_dir, write_dir, copyf_dir, copyw_dir = args.write_traffic
+    sym = KERNEL_SYMBOLS[kernel]
+
+    def pick(d, want):
+        hits = {k: v for k, v in d.items() if want(k)}
+        if not hits:
+            raise SystemExit(f"no matching kernel in {sorted(d)[:8]}")
+        return max(hits.items(), key=lambda kv: kv[1][1])  # the most dispatched
+
+    kname, (fetch, nd) = pick(_pmc_means(fetch_dir, "FETCH_SIZE"), lambda k: sym in k)
+    _, (write, _) = pick(_pmc_means(write_dir, "WRITE_SIZE"), lambda k: sym in k)
+    copy_bytes = (1 << 28) * 4
+    _, (cf, _) = pick(_pmc_means(copyf_dir, "FETCH_SIZE"), lambda k: "copy" in k.lower() or "elementwise" in k.lower())
+    _, (cw, _) = pick(_pmc_means(copyw_dir, "WRITE_SIZE"), lambda k: "copy" in k.lower() or "elementwise" in k.lower())
+    fscale, wscale = copy_bytes / 1024.0 / cf, copy_bytes / 1024.0 / cw
+    fscale, wscale = round(fscale, 3), round(wscale, 3)
+    nbytes = int(round((fetch * fscale + write * wscale) * 1024))
+    cmds = args.traffic_commands or []
+    rec = {"kernel": kname.split("(")[0], "workload": args.workload, "kernel_source_sha": kernel_source_hash(kernel),
+           "dispatches": nd, "fetch_kib_per_dispatch": round(fetch, 1), "write_kib_per_dispatch": round(write, 1),
+           "fetch_scale": fscale, "write_scale": wscale, "bytes_per_launch": nbytes, "commands": cmds}
+    with open(traffic_path(kernel, args.workload, "json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    with open(traffic_path(kernel, args.workload, "md"), "w") as f:
+        f.write(f"# HBM traffic per dispatch: {rec['kernel']} ({args.workload})\n\n")
+        f.write("Counter passes, each in its own run (repo root on the GPU box, TMPDIR=/tmp):\n\n")
+        for c in cmds:
+            f.write(f"    {c}\n")
+        f.write(f"\nCopy calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE = {cf:.0f} KiB and "
+                f"WRITE_SIZE = {cw:.0f} KiB per dispatch, so FETCH_SIZE is scaled by {fscale} and WRITE_SIZE by "
+                f"{wscale}.\n\n")
+        f.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch |\n|---|---|---|---|---|\n")
+        f.write(f"| {rec['kernel']} | {nd} | {fetch:.1f} | {write:.1f} | {nbytes:,} |\n\n")
+        f.write(f"Kernel source hash {rec['kernel_source_sha']} (the bench reports this traffic only while the "
+                f"sources are unchanged).  Written by `python bench.py --workload {args.workload} --write-traffic "
+                f"...`.\n")
+    print(json.dumps(rec))
 
 
 def main():
@@ -74,10 +145,17 @@ def main():
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="graph: each step variant (one native moe_stack_step call) replayed as a captured HIP "
                          "graph; eager: the native call itself, launched step by step")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write profiles/<kernel>_<workload>_traffic.{json,md} from rocprofv3 --pmc output folders "
+                         "(runs nothing on the GPU)")
+    ap.add_argument("--traffic-commands", nargs="*", help="the commands that made the --write-traffic folders")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device-to-device copies of 1 GiB (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
 
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
               f"the multi-GPU sharding is a design, not a measured path.", file=sys.stderr)
@@ -218,7 +296,7 @@ def main():
         flops = 2.0 * 2 * T * (wl.top_k * wl.expert_ff + wl.shared_ff) * wl.hidden
         roofline = {"bound": "hbm", "kernel": "k_group_gemm<GATEUP>", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": load_traffic(wl.name), "algorithmic_bytes_per_launch": int(per_launch),
+                    "traffic": load_traffic("group_gateup", wl.name), "algorithmic_bytes_per_launch": int(per_launch),
                     "mean_launch_us": round(us, 3),
                     "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 2), "mfma_peak_tflops_f16": 2500.0}
     if "gateup_swiglu" in kstats:
@@ -231,7 +309,7 @@ def main():
         per_launch = d_mean * gu_expert + gu_shared + act_bytes
         ach = per_launch / (kstats["gateup_swiglu"]["mean_us"] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": "k_gateup_swiglu", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": load_traffic(wl.name),
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": load_traffic("gateup_swiglu", wl.name),
                     "algorithmic_bytes_per_launch": int(per_launch),
                     "mean_launch_us": round(kstats["gateup_swiglu"]["mean_us"], 3)}
 

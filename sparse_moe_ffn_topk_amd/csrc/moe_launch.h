@@ -58,10 +58,12 @@ struct PrefillArgs {
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
 size_t prefill_sort_lds_bytes(int T, int E);
 
-// Kernel timer (diagnostics): when armed for kernel `id`, timer_slot() hands
-// out the next (start, stop) event pair, which the launch attaches to the
-// kernel's own dispatch (hipExtLaunchKernelGGL), so the events time exactly
-// that kernel's execution on its stream; otherwise both are NULL.
+// Kernel timer (diagnostics, eager launches only): when armed for kernel `id`,
+// timer_slot() hands out the next (start, stop) event pair, which the launch
+// attaches to the kernel's own dispatch (hipExtLaunchKernelGGL), so the events
+// time that kernel's execution on its stream; otherwise both are NULL.  The
+// stream is drained before a timed launch so that its start stamp is not
+// taken while earlier work on the stream is still running.
 struct TimerSlot {
   hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -71,6 +73,7 @@ TimerSlot timer_slot(int id);
 #define MOE_LAUNCH(ID, KERNEL, GRID, BLOCK, LDS, ST, ...)                                                 \
   do {                                                                                                   \
     const ::moe::TimerSlot ts_ = ::moe::timer_slot(ID);                                                  \
+    if (ts_.start) (void)hipStreamSynchronize(ST);                                                       \
     hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, ts_.start, ts_.stop, 0, __VA_ARGS__);            \
   } while (0)
 
