@@ -33,12 +33,12 @@ def lib():
         L.mo_sigmoid.restype = C.c_double
         L.mo_sigmoid.argtypes = [C.c_double]
         L.mo_swiglu.restype = C.c_double
-        L.mo_swiglu.argtypes = [C.c_double, C.c_double]
+        L.mo_swiglu.argtypes = [C.c_double, C.c_double, C.c_double]
         L.mo_group_keep.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P]
         L.mo_topk.argtypes = [P, P, C.c_int32, C.c_int32, P]
         L.mo_route.restype = C.c_int
         L.mo_route.argtypes = [P, P, P, P, P, P]
-        L.mo_expert_ffn.argtypes = [C.c_int, P, P, P, C.c_int32, C.c_int32, P, P]
+        L.mo_expert_ffn.argtypes = [C.c_int, P, P, P, C.c_int32, C.c_int32, C.c_double, P, P]
         L.mo_layer.restype = C.c_int
         L.mo_layer.argtypes = [P] + [P] * 8 + [P, C.c_int32, P, P, P, P, P]
         L.mo_sort_by_expert.argtypes = [P, C.c_int32, C.c_int32, P, P]
@@ -50,7 +50,8 @@ class Cfg(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("n_groups", C.c_int32), ("groups_used", C.c_int32),
                 ("expert_ff", C.c_int32), ("shared_ff", C.c_int32), ("qtype", C.c_int32),
-                ("weights_scale", C.c_double), ("wsum_min", C.c_double)]
+                ("weights_scale", C.c_double), ("wsum_min", C.c_double),
+                ("swiglu_limit", C.c_double), ("swiglu_limit_shared", C.c_double)]
 
 
 Q4_0, Q4_1 = 0, 1
@@ -58,9 +59,9 @@ WSUM_MIN = 6.103515625e-5
 
 
 def make_cfg(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=Q4_1, n_groups=1, groups_used=None,
-             weights_scale=1.0, wsum_min=WSUM_MIN):
+             weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0):
     return Cfg(hidden, n_experts, top_k, n_groups, groups_used if groups_used is not None else n_groups,
-               expert_ff, shared_ff, qtype, weights_scale, wsum_min)
+               expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared)
 
 
 def _p(a):
@@ -108,8 +109,8 @@ def sigmoid(v):
     return lib().mo_sigmoid(float(v))
 
 
-def swiglu(g, u):
-    return lib().mo_swiglu(float(g), float(u))
+def swiglu(g, u, limit=0.0):
+    return lib().mo_swiglu(float(g), float(u), float(limit))
 
 
 def group_keep(s32, n_groups, groups_used):
@@ -140,11 +141,11 @@ def route(cfg, logit32, logit64=None, bias=None):
     return ids, w
 
 
-def expert_ffn(qtype, gate, up, down, H, F, x):
+def expert_ffn(qtype, gate, up, down, H, F, x, limit=0.0):
     g, u, d = (_c(a, np.uint8) for a in (gate, up, down))
     xd = _c(x, np.float64)
     y = np.empty(H, np.float64)
-    lib().mo_expert_ffn(qtype, _p(g), _p(u), _p(d), H, F, _p(xd), _p(y))
+    lib().mo_expert_ffn(qtype, _p(g), _p(u), _p(d), H, F, float(limit), _p(xd), _p(y))
     return y
 
 

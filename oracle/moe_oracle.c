@@ -41,6 +41,8 @@ typedef struct {
   int32_t qtype;
   double weights_scale;
   double wsum_min;
+  double swiglu_limit;         /* routed experts' SwiGLU clamp L; 0 = none */
+  double swiglu_limit_shared;  /* the shared expert's; 0 = none */
 } mo_cfg;
 
 /* ---------------------------------------------------------------- f16 ---- */
@@ -243,25 +245,34 @@ int mo_route(const mo_cfg *c, const float *logit32, const double *logit64, const
 
 /* ----------------------------------------------------------- experts ---- */
 
-/* SwiGLU activation silu(g)*u with silu(g) = g / (1 + e^-g) ([LING] swiglu
- * with no clamp; [LFM] siluSplitB). */
-double mo_swiglu(double g, double u) { return g / (1.0 + exp(-g)) * u; }
+/* SwiGLU activation silu(g)*u with silu(g) = g / (1 + e^-g) ([LING] swiglu;
+ * [LFM] siluSplitB).  With a clamp L > 0 ([LING] swiglu kernel and the FFN
+ * line of its file header: some layers clamp the SwiGLU), u is clamped to
+ * [-L, L] and silu(g) is capped at L from above only; L = 0 is no clamp. */
+double mo_swiglu(double g, double u, double L) {
+  double sg = g / (1.0 + exp(-g));
+  if (L > 0.0) {
+    u = u < -L ? -L : (u > L ? L : u);
+    sg = sg > L ? L : sg;
+  }
+  return sg * u;
+}
 
 /* One SwiGLU expert on one token (double throughout):
  *   g_f = sum_h Wg[f][h] x_h,  u_f = sum_h Wu[f][h] x_h,  a_f = silu(g_f) u_f,
- *   y_h = sum_f Wd[h][f] a_f.
+ *   y_h = sum_f Wd[h][f] a_f  (a_f clamped as in mo_swiglu when limit > 0).
  * gate/up hold F rows of H/32 blocks, down holds H rows of F/32 blocks (GGUF
  * ffn_{gate,up}_exps [H, F] and ffn_down_exps [F, H] per expert, rows of the
  * first dimension). */
 void mo_expert_ffn(int qtype, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
-                   int32_t H, int32_t F, const double *x, double *y) {
+                   int32_t H, int32_t F, double limit, const double *x, double *y) {
   int bs = mo_block_bytes(qtype);
   int nbH = H / 32, nbF = F / 32;
   double *a = (double *)malloc(sizeof(double) * (size_t)F);
   for (int f = 0; f < F; f++) {
     double g = mo_row_dot(qtype, gate + (size_t)f * nbH * bs, nbH, x);
     double u = mo_row_dot(qtype, up + (size_t)f * nbH * bs, nbH, x);
-    a[f] = mo_swiglu(g, u);
+    a[f] = mo_swiglu(g, u, limit);
   }
   for (int h = 0; h < H; h++) y[h] = mo_row_dot(qtype, down + (size_t)h * nbF * bs, nbF, a);
   free(a);
@@ -308,12 +319,12 @@ int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const ui
     for (int j = 0; j < k; j++) {
       int e = ids[(size_t)t * k + j];
       mo_expert_ffn(c->qtype, gate_exps + (size_t)e * exp_gu, up_exps + (size_t)e * exp_gu,
-                    down_exps + (size_t)e * exp_dn, H, F, xd, y);
+                    down_exps + (size_t)e * exp_dn, H, F, c->swiglu_limit, xd, y);
       double wj = w[(size_t)t * k + j];
       for (int h = 0; h < H; h++) o[h] += wj * y[h];
     }
     if (SF > 0 && gate_sh && up_sh && down_sh) {
-      mo_expert_ffn(c->qtype, gate_sh, up_sh, down_sh, H, SF, xd, y);
+      mo_expert_ffn(c->qtype, gate_sh, up_sh, down_sh, H, SF, c->swiglu_limit_shared, xd, y);
       for (int h = 0; h < H; h++) o[h] += y[h];
     }
   }

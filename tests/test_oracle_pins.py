@@ -297,6 +297,70 @@ def test_swiglu_closed_forms():
         assert O.swiglu(g, 2.0) == 2.0 * O.swiglu(g, 1.0)
 
 
+def _silu(g):
+    return g / (1.0 + math.exp(-g))
+
+
+def _const_q4_1_rows(n_rows, n_blocks, m):
+    """Q4_1 rows whose every weight is m: d = 0 (so d*q = 0 for any nibble) and
+    offset m, f16-encoded by numpy.  m must be exact in f16."""
+    assert float(np.float16(m)) == m
+    blk = np.zeros(20, np.uint8)
+    blk[2:4] = np.frombuffer(np.float16(m).tobytes(), np.uint8)
+    blk[4:] = 0x5A  # arbitrary nibbles: multiplied by d = 0
+    return np.tile(blk, n_rows * n_blocks).reshape(n_rows, n_blocks * 20)
+
+
+@pytest.mark.parametrize("g,u,L", [
+    (10.0, -7.0, 5.0),    # silu(g) capped at L, u clamped at -L
+    (-3.0, 2.0, 0.1),     # negative silu(g) is not raised to -L (the cap is one-sided), u clamped
+    (0.25, 1.0, 0.2),     # silu(0.25) < L stays; the clamp is on silu(g), not on g before silu
+    (10.0, -7.0, 0.0),    # L = 0: no clamp
+    (1.5, 0.75, 100.0),   # inactive clamp
+])
+def test_swiglu_clamp_closed_forms(g, u, L):
+    """ling_moe_ssd.js page, swiglu kernel and the FFN line of its file header:
+    act = min(silu(g), L) * clamp(u, -L, L) when L > 0.  Checked on a whole
+    expert whose rows are constant: with x = 1 and H = F = 32, every gate row
+    gives g = 32 m_g, every up row u = 32 m_u, and y_h = 32 m_d act."""
+    H = F = 32
+    gate = _const_q4_1_rows(F, 1, g / 32)
+    up = _const_q4_1_rows(F, 1, u / 32)
+    down = _const_q4_1_rows(H, 1, 0.0625)
+    sg = _silu(g)
+    if L > 0:
+        act = min(sg, L) * min(max(u, -L), L)
+    else:
+        act = sg * u
+    y = O.expert_ffn(O.Q4_1, gate, up, down, H, F, np.ones(H), limit=L)
+    assert np.allclose(y, 2.0 * act, rtol=1e-13, atol=0)
+    assert O.swiglu(g, u, L) == pytest.approx(act, rel=1e-15)
+
+
+def test_swiglu_clamp_routed_and_shared_limits_apply_to_their_experts():
+    """The routed experts take the routed limit and the shared expert its own
+    (ling_moe_ssd.js page: clampExp for the experts, clampShexp for the shared
+    expert).  One pick with weight p/p = 1; constant-row experts as above."""
+    H = F = SF = 32
+    E = 2
+    ge = np.stack([_const_q4_1_rows(F, 1, 10.0 / 32), _const_q4_1_rows(F, 1, 1.0 / 32)])
+    ue = np.stack([_const_q4_1_rows(F, 1, -7.0 / 32), _const_q4_1_rows(F, 1, 1.0 / 32)])
+    de = np.stack([_const_q4_1_rows(H, 1, 0.0625), _const_q4_1_rows(H, 1, 0.0625)])
+    w = {"router_w": None, "bias": None, "gate_exps": ge, "up_exps": ue, "down_exps": de,
+         "gate_sh": _const_q4_1_rows(SF, 1, -3.0 / 32), "up_sh": _const_q4_1_rows(SF, 1, 2.0 / 32),
+         "down_sh": _const_q4_1_rows(H, 1, 0.0625)}
+    cfg = O.make_cfg(H, E, 1, F, SF, O.Q4_1, swiglu_limit=5.0, swiglu_limit_shared=0.1)
+    logits = np.array([[3.0, -3.0]], np.float32)  # picks expert 0
+    out, ids, ww = O.layer(cfg, w, np.ones((1, H), np.float32), logits_in=logits)
+    assert ids[0, 0] == 0 and ww[0, 0] == 1.0
+    routed = 2.0 * (5.0 * -5.0)                       # min(silu(10), 5) * clamp(-7)
+    shared = 2.0 * (_silu(-3.0) * 0.1)                # silu(-3) < 0.1 stays; clamp(2) = 0.1
+    assert np.allclose(out[0], routed + shared, rtol=1e-13, atol=0)
+    # the limits swapped give a clearly different answer
+    swapped = 2.0 * (0.1 * -0.1) + 2.0 * (_silu(-3.0) * 2.0)
+    assert abs((routed + shared) - swapped) > 1.0
+
+
 # -------------------------------------------------------------- experts ----
 
 def _const_blocks(n_rows, cols, d, m, qtype=O.Q4_1, nib=0):
