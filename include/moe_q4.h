@@ -69,7 +69,13 @@ enum {
  *   shared_ff SF:  0 (no shared expert) or 32 <= SF <= 8192, SF % 32 == 0
  *   qtype:         MOE_Q4_0 or MOE_Q4_1 (routed and shared experts alike)
  *   weights_scale: finite, > 0 (1 for Flint and LFM2.5, 2.5 for Ling)
- *   wsum_min:      finite, > 0 (2^-14 = 6.103515625e-5 on all three pages)   */
+ *   wsum_min:      finite, > 0 (2^-14 = 6.103515625e-5 on all three pages)
+ *   swiglu_limit, swiglu_limit_shared: finite, >= 0.  SwiGLU clamp L of the
+ *                  routed experts and of the shared expert (the ling_moe_ssd.js
+ *                  page's swiglu kernel and per-layer clamp lists): with L > 0,
+ *                  act = min(silu(g), L) * clamp(u, -L, L); 0 = no clamp.
+ *                  A layer's own values; moe_stack_step applies one config
+ *                  (and so one pair of limits) to all its layers.            */
 typedef struct {
   int32_t hidden, n_experts, top_k;
   int32_t n_groups, groups_used;
@@ -77,6 +83,8 @@ typedef struct {
   int32_t qtype;
   float weights_scale;
   float wsum_min;
+  float swiglu_limit;
+  float swiglu_limit_shared;
 } moe_config;
 
 /* Weights of one MoE layer (GGUF tensor names in brackets).  Block tensors

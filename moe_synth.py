@@ -39,6 +39,8 @@ class Workload:
     groups_used: int = 1
     weights_scale: float = 1.0
     has_bias: bool = False
+    swiglu_limit: float = 0.0         # SwiGLU clamp of the routed experts (0: none)
+    swiglu_limit_shared: float = 0.0  # and of the shared expert
     tokens: int = 1
     layers: int = 1
     # distributions

@@ -28,7 +28,8 @@ class MoeConfig(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("n_groups", C.c_int32), ("groups_used", C.c_int32),
                 ("expert_ff", C.c_int32), ("shared_ff", C.c_int32), ("qtype", C.c_int32),
-                ("weights_scale", C.c_float), ("wsum_min", C.c_float)]
+                ("weights_scale", C.c_float), ("wsum_min", C.c_float),
+                ("swiglu_limit", C.c_float), ("swiglu_limit_shared", C.c_float)]
 
 
 class LayerWeights(C.Structure):
@@ -76,15 +77,16 @@ KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE = 5, 6, 7, 8
 
 
 def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,
-                weights_scale=1.0, wsum_min=WSUM_MIN):
+                weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0):
     return MoeConfig(hidden, n_experts, top_k, n_groups, n_groups if groups_used is None else groups_used,
-                     expert_ff, shared_ff, qtype, weights_scale, wsum_min)
+                     expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared)
 
 
 def config_for(wl):
     """MoeConfig of a moe_synth.Workload-like object."""
     return make_config(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
-                       wl.groups_used, wl.weights_scale)
+                       wl.groups_used, wl.weights_scale, swiglu_limit=getattr(wl, "swiglu_limit", 0.0),
+                       swiglu_limit_shared=getattr(wl, "swiglu_limit_shared", 0.0))
 
 
 def _ptr(t):

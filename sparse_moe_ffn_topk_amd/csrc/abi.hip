@@ -90,6 +90,9 @@ int check_cfg(const moe_config *c) {
   if (!(std::isfinite(c->weights_scale) && c->weights_scale > 0))
     return fail(MOE_EINVAL, "weights_scale must be finite and > 0");
   if (!(std::isfinite(c->wsum_min) && c->wsum_min > 0)) return fail(MOE_EINVAL, "wsum_min must be finite and > 0");
+  if (!(std::isfinite(c->swiglu_limit) && c->swiglu_limit >= 0) ||
+      !(std::isfinite(c->swiglu_limit_shared) && c->swiglu_limit_shared >= 0))
+    return fail(MOE_EINVAL, "swiglu limits must be finite and >= 0");
   return MOE_OK;
 }
 
@@ -163,6 +166,8 @@ int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float
   a.logits = logits;
   a.bias = w->router_bias;
   a.sel = moe::SelParams{c.n_experts, c.top_k, c.n_groups, c.groups_used, c.weights_scale, c.wsum_min};
+  a.lim = c.swiglu_limit;
+  a.lim_sh = c.swiglu_limit_shared;
   a.gate_exps = w->gate_exps;
   a.up_exps = w->up_exps;
   a.down_exps = w->down_exps;
@@ -208,6 +213,8 @@ int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const floa
     p.Y = (float *)(b + L.Y);
     p.Ysh = (float *)(b + L.Ysh);
     p.resid = resid + (size_t)t0 * c.hidden;
+    p.lim = c.swiglu_limit;
+    p.lim_sh = c.swiglu_limit_shared;
     int rc = launched(moe::launch_prefill_ffn(p, st), "grouped expert FFN");
     if (rc) return rc;
   }

@@ -69,7 +69,16 @@ __device__ __forceinline__ void stage_store(const Stage<XR> &st, int n, float *x
   }
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u, with the SwiGLU clamp when L > 0: min(silu(g), L) * clamp(u, -L, L)
+// (the ling_moe_ssd.js page's swiglu kernel).
+__device__ __forceinline__ float silu_mul(float g, float u, float L) {
+  float sg = g / (1.0f + __expf(-g));
+  if (L > 0.f) {
+    u = fminf(fmaxf(u, -L), L);
+    sg = fminf(sg, L);
+  }
+  return sg * u;
+}
 
 // grid.x: NB blocks per token; grid.y: token t.  A wave task is RW = 64/LPR
 // rows (one per lane group) of a gate/up matrix pair.  Token t's tasks are the
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
     const float *__restrict__ x, int32_t *__restrict__ ids, float *__restrict__ wts,
     const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int H, int k, int F, int SF,
     const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
-    const uint8_t *__restrict__ gate_sh, const uint8_t *__restrict__ up_sh, float *__restrict__ act) {
+    const uint8_t *__restrict__ gate_sh, const uint8_t *__restrict__ up_sh, float lim, float lim_sh,
+    float *__restrict__ act) {
   extern __shared__ float smem[];
   __shared__ SelShared sh;
   constexpr int BS = QBlock<QT>::bytes;
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
   }
   g = group_sum_last<LPR>(g);
   v = group_sum_last<LPR>(v);
-  if (li == LPR - 1 && live) out[row] = silu_mul(g, v);
+  if (li == LPR - 1 && live) out[row] = silu_mul(g, v, is_sh ? lim_sh : lim);
 }
 
 // grid.x: tiles of NT/LPR outputs h; grid.y: token t.  Each lane walks a flat
@@ -274,7 +284,8 @@ static inline int xr_for(int n, int nt) {  // float4s per thread to stage n floa
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
-             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.act);
+             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim, a.lim_sh,
+             a.act);
 }
 template <int QT, int LPR, int XR, int NT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {

@@ -34,6 +34,7 @@ struct DecodeArgs {
   const uint8_t *gate_sh, *up_sh, *down_sh;
   float *act;    // per token: [k][F] routed rows, then [SF] shared
   float *resid;  // [T][H] in/out
+  float lim, lim_sh;  // SwiGLU clamp of the routed and of the shared experts (0: none)
 };
 
 // gate||up + SwiGLU, then down + weighted per-token accumulate.
@@ -54,6 +55,7 @@ struct PrefillArgs {
   float *act, *act_sh;     // [T*k][F] sorted, [T][SF]
   float *Y, *Ysh;          // [T*k][H] sorted and weighted, [T][H]
   float *resid;            // [T][H] in/out
+  float lim, lim_sh;       // SwiGLU clamp of the routed and of the shared experts (0: none)
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
 size_t prefill_sort_lds_bytes(int T, int E);

@@ -173,6 +173,7 @@ struct GemmArgs {
   float *out;                // GATEUP: sorted act; DOWN: Y [T*k][H]
   float *out_sh;             // GATEUP: act_sh; DOWN: Ysh [T][H]
   int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
+  float lim, lim_sh;         // GATEUP: SwiGLU clamp of routed / shared experts (0: none)
 };
 
 // K is walked in chunks of KB Q4 blocks.  Per chunk a block stages, in LDS,
@@ -418,8 +419,14 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
       if (o < 0) continue;
       float v;
       if (MODE == GG_GATEUP) {
-        const float g = acc[0][c][i], u = acc[NM - 1][c][i];
-        v = g / (1.0f + __expf(-g)) * u;
+        // SwiGLU, clamped when L > 0 (the ling_moe_ssd.js page's swiglu kernel)
+        const float g = acc[0][c][i], L = shared ? a.lim_sh : a.lim;
+        float u = acc[NM - 1][c][i], sg = g / (1.0f + __expf(-g));
+        if (L > 0.f) {
+          u = fminf(fmaxf(u, -L), L);
+          sg = fminf(sg, L);
+        }
+        v = sg * u;
       } else {
         v = outw[m] * acc[0][c][i];
       }
@@ -468,6 +475,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   g.tiles = p.tiles;
   g.ntiles = p.ntiles;
   g.max_routed_tiles = (T * k + 15) / 16 + E;
+  g.lim = p.lim;
+  g.lim_sh = p.lim_sh;
   const int shtiles = p.SF > 0 ? (T + 15) / 16 : 0;
   // gate || up
   g.w0 = p.gate_exps;

@@ -19,7 +19,8 @@ TIE_TAU = 1e-6
 
 def oracle_cfg(wl):
     return O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
-                      wl.groups_used, wl.weights_scale)
+                      wl.groups_used, wl.weights_scale, swiglu_limit=wl.swiglu_limit,
+                      swiglu_limit_shared=wl.swiglu_limit_shared)
 
 
 def to_device(w, device="cuda"):
@@ -63,9 +64,10 @@ def oracle_given_routing(wl, wnp, x_t, ids, wts, resid_t=None):
     xd = x_t.astype(np.float64)
     for e, wj in zip(ids, wts):
         out += float(wj) * O.expert_ffn(wl.qtype, wnp["gate_exps"][e], wnp["up_exps"][e], wnp["down_exps"][e],
-                                        H, F, xd)
+                                        H, F, xd, limit=wl.swiglu_limit)
     if SF:
-        out += O.expert_ffn(wl.qtype, wnp["gate_sh"], wnp["up_sh"], wnp["down_sh"], H, SF, xd)
+        out += O.expert_ffn(wl.qtype, wnp["gate_sh"], wnp["up_sh"], wnp["down_sh"], H, SF, xd,
+                            limit=wl.swiglu_limit_shared)
     return out
 
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert C.sizeof(moe.MoeConfig) == 10 * 4
+    assert C.sizeof(moe.MoeConfig) == 12 * 4
     assert C.sizeof(moe.LayerWeights) == 8 * 8
 
 
@@ -51,6 +51,8 @@ def _cfg(**kw):
     (dict(top_k=5, n_groups=4, groups_used=2), "exceeds"),
     (dict(expert_ff=100), "expert_ff"), (dict(shared_ff=16), "shared_ff"),
     (dict(qtype=2), "qtype"), (dict(weights_scale=0.0), "weights_scale"), (dict(wsum_min=-1.0), "wsum_min"),
+    (dict(swiglu_limit=-1.0), "swiglu"), (dict(swiglu_limit_shared=float("inf")), "swiglu"),
+    (dict(swiglu_limit=float("nan")), "swiglu"),
 ])
 def test_invalid_config_rejected(kw, msg):
     L = moe.load_library()

@@ -105,6 +105,28 @@ def test_layer_prefill_chunk(gpu):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512)])
+def test_layer_swiglu_clamp(gpu, name, T):
+    # SwiGLU clamp (ling_moe_ssd.js page: min(silu(g), L) * clamp(u, -L, L)),
+    # distinct limits for the routed and the shared experts, at magnitudes where
+    # both clamps are active (g, u ~ N(0, 4.5^2) for these weights)
+    import dataclasses
+    wl = dataclasses.replace(S.WORKLOADS[name], swiglu_limit=3.0, swiglu_limit_shared=2.0)
+    _say(f"layer {name} T={T} with SwiGLU clamps 3.0 / 2.0")
+    w, x = _layer(wl, seed=13)
+    wnp = S.to_numpy(w)
+    sample = None if T <= 8 else list(range(0, T, 37)) + [T - 1]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=wnp, sample=sample)
+    # the clamps change the layer's output (so the test exercises them)
+    rows = [0] if sample is None else sample[:2]
+    ref_c = O.layer(oracle_cfg(wl), wnp, x.numpy()[rows])[0]
+    ref_u = O.layer(oracle_cfg(dataclasses.replace(wl, swiglu_limit=0.0, swiglu_limit_shared=0.0)), wnp,
+                    x.numpy()[rows])[0]
+    assert row_rel_err(ref_c, ref_u).max() > 0.05
+    print(f"[result] clamp {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("T", [600, 1100])
 def test_layer_prefill_multi_chunk(gpu, T):
     # more tokens than one chunk: the chunks run one after another
