@@ -288,6 +288,9 @@ void mo_expert_ffn(int qtype, const uint8_t *gate, const uint8_t *up, const uint
  *   of H rows x F/32 blocks, shared tensors likewise with SF (NULL if SF = 0).
  *   logits_in: NULL -> logits from the router weights in double; else [T][E]
  *   f32 logits used for both decisions and weights.
+ * A dense SwiGLU FFN layer is E = k = 0: no routing, out = resid +
+ * FFN_shared(x) ([FLINT] and [LING] file headers: a dense SwiGLU FFN of 6144
+ * on the first two layers; [LFM] likewise with 11776).
  * Outputs out[T][H] (double), ids[T][k], w[T][k].  Returns 0 or -1. */
 int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const uint8_t *gate_exps,
              const uint8_t *up_exps, const uint8_t *down_exps, const uint8_t *gate_sh,
@@ -305,15 +308,19 @@ int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const ui
     const float *xt = x + (size_t)t * H;
     for (int h = 0; h < H; h++) xd[h] = xt[h];
     const double *lv = NULL;
-    if (logits_in) {
+    if (E == 0) {
+      /* a dense layer: no router, only the FFN held in the shared tensors */
+    } else if (logits_in) {
       for (int e = 0; e < E; e++) l32[e] = logits_in[(size_t)t * E + e];
     } else {
       mo_router_logits(router_w, xt, E, H, l64);
       for (int e = 0; e < E; e++) l32[e] = (float)l64[e];
       lv = l64;
     }
-    rc = mo_route(c, l32, lv, bias, ids + (size_t)t * k, w + (size_t)t * k);
-    if (rc) break;
+    if (E > 0) {
+      rc = mo_route(c, l32, lv, bias, ids + (size_t)t * k, w + (size_t)t * k);
+      if (rc) break;
+    }
     double *o = out + (size_t)t * H;
     for (int h = 0; h < H; h++) o[h] = resid ? (double)resid[(size_t)t * H + h] : 0.0;
     for (int j = 0; j < k; j++) {

@@ -361,6 +361,21 @@ def test_swiglu_clamp_routed_and_shared_limits_apply_to_their_experts():
     assert abs((routed + shared) - swapped) > 1.0
 
 
+def test_dense_layer_is_the_ffn_alone():
+    """A dense SwiGLU FFN layer (the pages' leading layers: no router) is
+    E = k = 0 with the FFN in the shared tensors: out = resid + FFN(x).
+    Constant-row FFN as above: g = 10, u = -7, y_h = 32 * 0.0625 * act."""
+    H = SF = 32
+    w = {"router_w": None, "bias": None, "gate_exps": None, "up_exps": None, "down_exps": None,
+         "gate_sh": _const_q4_1_rows(SF, 1, 10.0 / 32), "up_sh": _const_q4_1_rows(SF, 1, -7.0 / 32),
+         "down_sh": _const_q4_1_rows(H, 1, 0.0625)}
+    cfg = O.make_cfg(H, 0, 0, 0, SF, O.Q4_1)
+    resid = np.linspace(-1, 1, H, dtype=np.float32)[None, :]
+    out, ids, ww = O.layer(cfg, w, np.ones((1, H), np.float32), resid=resid)
+    assert ids.shape == (1, 0) and ww.shape == (1, 0)
+    assert np.allclose(out[0], resid[0].astype(np.float64) + 2.0 * _silu(10.0) * -7.0, rtol=1e-13, atol=1e-13)
+
+
 # -------------------------------------------------------------- experts ----
 
 def _const_blocks(n_rows, cols, d, m, qtype=O.Q4_1, nib=0):
