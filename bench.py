@@ -137,7 +137,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="flint", choices=["flint", "flint8", "lfm25", "ling", "tiny", "prefill"])
+    ap.add_argument("--workload", default="flint",
+                    choices=["flint", "flint8", "lfm25", "ling", "tiny", "prefill", "flint_dense", "lfm25_dense"])
     ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

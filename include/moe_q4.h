@@ -61,12 +61,16 @@ enum {
 
 /* Layer shape.  Limits (the pages cap E at 512 and k at 32):
  *   hidden H:      32 <= H <= 8192, H % 32 == 0
- *   n_experts E:   1 <= E <= 512
- *   top_k k:       1 <= k <= min(32, E)
+ *   n_experts E:   1 <= E <= 512, or 0 for a dense SwiGLU FFN layer (the
+ *                  leading layers of the three pages' models: no router, the
+ *                  FFN sits in the shared-expert tensors, shared_ff is its
+ *                  size; then top_k = 0, n_groups = groups_used = 1, and
+ *                  expert_ff and the routed tensors are ignored)
+ *   top_k k:       1 <= k <= min(32, E)  (0 for a dense layer)
  *   n_groups G:    1 <= G <= 64, E % G == 0, E/G >= 2 when G > 1
  *   groups_used:   1 <= Gu <= G, k <= Gu * (E/G); Gu == G means no group limit
  *   expert_ff F:   32 <= F <= 8192, F % 32 == 0
- *   shared_ff SF:  0 (no shared expert) or 32 <= SF <= 8192, SF % 32 == 0
+ *   shared_ff SF:  0 (no shared expert) or 32 <= SF <= 16384, SF % 32 == 0
  *   qtype:         MOE_Q4_0 or MOE_Q4_1 (routed and shared experts alike)
  *   weights_scale: finite, > 0 (1 for Flint and LFM2.5, 2.5 for Ling)
  *   wsum_min:      finite, > 0 (2^-14 = 6.103515625e-5 on all three pages)

@@ -58,6 +58,10 @@ WORKLOADS = {
     "ling": Workload("ling", 2560, 512, 8, 768, 768, Q4_1, n_groups=8, groups_used=4, weights_scale=2.5,
                      has_bias=True, tokens=1, layers=1),
     "prefill": Workload("prefill", 2048, 256, 6, 512, 1024, Q4_1, tokens=512, layers=1),
+    # dense leading SwiGLU FFN layers (no router): Flint and Ling 6144, LFM2.5 11776 (Q4_0 here).  The
+    # models have two such layers; 16 generated copies are cycled so the weights exceed the 256 MB MALL.
+    "flint_dense": Workload("flint_dense", 2048, 0, 0, 0, 6144, Q4_1, tokens=1, layers=16),
+    "lfm25_dense": Workload("lfm25_dense", 2048, 0, 0, 0, 11776, Q4_0, tokens=1, layers=16),
 }
 
 
@@ -111,12 +115,13 @@ def make_layer(wl, layer=0, device="cpu", master=0):
     """All weights of one MoE layer of workload `wl`, on `device`."""
     H, E, F, SF = wl.hidden, wl.n_experts, wl.expert_ff, wl.shared_ff
     s = lambda name: seed_for(master, wl.name, layer, name)
+    routed = E > 0  # E == 0: a dense SwiGLU FFN layer, held in the shared tensors
     w = {
-        "router_w": normal((E, H), wl.router_std, device, s("router_w")),
-        "bias": normal((E,), wl.bias_std, device, s("bias")) if wl.has_bias else None,
-        "gate_exps": expert_tensor(E, F, H, wl.qtype, device, s("gate_exps"), wl),
-        "up_exps": expert_tensor(E, F, H, wl.qtype, device, s("up_exps"), wl),
-        "down_exps": expert_tensor(E, H, F, wl.qtype, device, s("down_exps"), wl),
+        "router_w": normal((E, H), wl.router_std, device, s("router_w")) if routed else None,
+        "bias": normal((E,), wl.bias_std, device, s("bias")) if wl.has_bias and routed else None,
+        "gate_exps": expert_tensor(E, F, H, wl.qtype, device, s("gate_exps"), wl) if routed else None,
+        "up_exps": expert_tensor(E, F, H, wl.qtype, device, s("up_exps"), wl) if routed else None,
+        "down_exps": expert_tensor(E, H, F, wl.qtype, device, s("down_exps"), wl) if routed else None,
         "gate_sh": None, "up_sh": None, "down_sh": None,
     }
     if SF:

@@ -42,7 +42,8 @@ struct Layout {
 
 Layout layout(const moe_config &c, int32_t T) {
   Layout L;
-  const size_t k = c.top_k, E = c.n_experts, F = c.expert_ff, SF = c.shared_ff, H = c.hidden;
+  const size_t k = c.top_k, E = c.n_experts, SF = c.shared_ff, H = c.hidden;
+  const size_t F = c.top_k > 0 ? c.expert_ff : 0;  // (a dense layer: no routed rows)
   const size_t Tc = T < moe::PREFILL_CHUNK ? (size_t)T : (size_t)moe::PREFILL_CHUNK;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -76,16 +77,23 @@ int check_cfg(const moe_config *c) {
   if (!c) return fail(MOE_EINVAL, "cfg is NULL");
   const int H = c->hidden, E = c->n_experts, k = c->top_k, G = c->n_groups, Gu = c->groups_used;
   if (H < 32 || H > 8192 || H % 32) return fail(MOE_EINVAL, "hidden %d: need 32 <= H <= 8192, H %% 32 == 0", H);
-  if (E < 1 || E > 512) return fail(MOE_EINVAL, "n_experts %d: need 1..512", E);
-  if (k < 1 || k > 32 || k > E) return fail(MOE_EINVAL, "top_k %d: need 1 <= k <= min(32, E=%d)", k, E);
-  if (G < 1 || G > 64 || E % G) return fail(MOE_EINVAL, "n_groups %d: need 1..64 dividing E=%d", G, E);
-  if (G > 1 && E / G < 2) return fail(MOE_EINVAL, "groups of %d experts: need >= 2 per group", E / G);
-  if (Gu < 1 || Gu > G) return fail(MOE_EINVAL, "groups_used %d: need 1..G=%d", Gu, G);
-  if ((long)k > (long)Gu * (E / G)) return fail(MOE_EINVAL, "top_k %d exceeds the experts of %d kept groups", k, Gu);
-  if (c->expert_ff < 32 || c->expert_ff > 8192 || c->expert_ff % 32)
-    return fail(MOE_EINVAL, "expert_ff %d: need 32 <= F <= 8192, F %% 32 == 0", c->expert_ff);
-  if (c->shared_ff != 0 && (c->shared_ff < 32 || c->shared_ff > 8192 || c->shared_ff % 32))
-    return fail(MOE_EINVAL, "shared_ff %d: need 0 or 32 <= SF <= 8192, SF %% 32 == 0", c->shared_ff);
+  if (E == 0) {
+    // a dense SwiGLU FFN layer: no router, the shared-expert tensors hold the FFN
+    if (k != 0) return fail(MOE_EINVAL, "top_k %d: a dense layer (n_experts 0) needs top_k 0", k);
+    if (G != 1 || Gu != 1) return fail(MOE_EINVAL, "n_groups/groups_used: a dense layer needs 1 and 1");
+    if (c->shared_ff == 0) return fail(MOE_EINVAL, "shared_ff 0: a dense layer (n_experts 0) needs its FFN size");
+  } else {
+    if (E < 1 || E > 512) return fail(MOE_EINVAL, "n_experts %d: need 0 (dense) or 1..512", E);
+    if (k < 1 || k > 32 || k > E) return fail(MOE_EINVAL, "top_k %d: need 1 <= k <= min(32, E=%d)", k, E);
+    if (G < 1 || G > 64 || E % G) return fail(MOE_EINVAL, "n_groups %d: need 1..64 dividing E=%d", G, E);
+    if (G > 1 && E / G < 2) return fail(MOE_EINVAL, "groups of %d experts: need >= 2 per group", E / G);
+    if (Gu < 1 || Gu > G) return fail(MOE_EINVAL, "groups_used %d: need 1..G=%d", Gu, G);
+    if ((long)k > (long)Gu * (E / G)) return fail(MOE_EINVAL, "top_k %d exceeds the experts of %d kept groups", k, Gu);
+    if (c->expert_ff < 32 || c->expert_ff > 8192 || c->expert_ff % 32)
+      return fail(MOE_EINVAL, "expert_ff %d: need 32 <= F <= 8192, F %% 32 == 0", c->expert_ff);
+  }
+  if (c->shared_ff != 0 && (c->shared_ff < 32 || c->shared_ff > 16384 || c->shared_ff % 32))
+    return fail(MOE_EINVAL, "shared_ff %d: need 0 or 32 <= SF <= 16384, SF %% 32 == 0", c->shared_ff);
   if (c->qtype != MOE_Q4_0 && c->qtype != MOE_Q4_1) return fail(MOE_EINVAL, "qtype %d: need 0 or 1", c->qtype);
   if (!(std::isfinite(c->weights_scale) && c->weights_scale > 0))
     return fail(MOE_EINVAL, "weights_scale must be finite and > 0");
@@ -118,9 +126,10 @@ int check_ws(const moe_config &c, int32_t T, void *ws, size_t bytes) {
 
 int check_expert_ptrs(const moe_config &c, const moe_layer_weights *w) {
   int rc;
-  if ((rc = check_ptr(w->gate_exps, "gate_exps", true))) return rc;
-  if ((rc = check_ptr(w->up_exps, "up_exps", true))) return rc;
-  if ((rc = check_ptr(w->down_exps, "down_exps", true))) return rc;
+  const bool routed = c.n_experts > 0;
+  if ((rc = check_ptr(w->gate_exps, "gate_exps", routed))) return rc;
+  if ((rc = check_ptr(w->up_exps, "up_exps", routed))) return rc;
+  if ((rc = check_ptr(w->down_exps, "down_exps", routed))) return rc;
   const bool sh = c.shared_ff > 0;
   if ((rc = check_ptr(w->gate_shexp, "gate_shexp", sh))) return rc;
   if ((rc = check_ptr(w->up_shexp, "up_shexp", sh))) return rc;
@@ -158,7 +167,7 @@ int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float
   a.T = T;
   a.H = c.hidden;
   a.k = c.top_k;
-  a.F = c.expert_ff;
+  a.F = c.top_k > 0 ? c.expert_ff : 0;  // (a dense layer: no routed rows)
   a.SF = c.shared_ff;
   a.x = x;
   a.ids = ids;
@@ -191,7 +200,7 @@ int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const floa
     p.T = Tc;
     p.H = c.hidden;
     p.k = c.top_k;
-    p.F = c.expert_ff;
+    p.F = c.top_k > 0 ? c.expert_ff : 0;
     p.SF = c.shared_ff;
     p.E = c.n_experts;
     p.x = x + (size_t)t0 * c.hidden;
@@ -307,7 +316,7 @@ int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const flo
   int rc;
   if ((rc = check_cfg(cfg))) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
-  if (T == 0) return MOE_OK;
+  if (T == 0 || cfg->n_experts == 0) return MOE_OK;  // (a dense layer routes nothing)
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_ptr(logits_in, "logits_in", false))) return rc;
   if (!logits_in) {
@@ -332,8 +341,8 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
-  if ((rc = check_ptr4(ids, "ids", true))) return rc;
-  if ((rc = check_ptr4(weights, "weights", true))) return rc;
+  if ((rc = check_ptr4(ids, "ids", cfg->top_k > 0))) return rc;
+  if ((rc = check_ptr4(weights, "weights", cfg->top_k > 0))) return rc;
   if ((rc = check_ptr(resid, "resid", true))) return rc;
   if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
@@ -352,7 +361,8 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
   if (T == 0) return MOE_OK;
   if (!w) return fail(MOE_EINVAL, "weights is NULL");
-  if ((rc = check_ptr(w->router_w, "router_w", true))) return rc;
+  const bool dense = cfg->n_experts == 0;
+  if ((rc = check_ptr(w->router_w, "router_w", !dense))) return rc;
   if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
@@ -365,6 +375,10 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
   float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
   hipStream_t st = (hipStream_t)stream;
+  if (dense) {  // no router: only the FFN held in the shared-expert tensors
+    if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
+    return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
+  }
   if (T <= kDecodeMaxT && decode_fits(*cfg)) {
     // decode: router logits, then the gate||up kernel routes in its prologue
     float *lg = (float *)((char *)workspace + L.logits);

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
   const int u = wave * NB + blockIdx.x;
   const bool is_sh = u < nsw;
   const bool wlive = u < nsw + k * nfw;
-  const int j = is_sh ? 0 : min((u - nsw) / nfw, k - 1);
+  const int j = (is_sh || k == 0) ? 0 : min((u - nsw) / nfw, k - 1);  // (no routed tasks when k == 0)
   const int row = (is_sh ? u : u - nsw - j * nfw) * RW + gi;
   const bool live = wlive && row < (is_sh ? SF : F);
   const uint32_t rowbytes = (uint32_t)nbH * BS;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   stage_load<NT, XR>(ast, act + (size_t)t * (k * F + SF), k * F + SF);
 
   // task q: the shared row (j = k) for q < bplS, then pick j = (q - bplS) / bplF
-  auto pick = [&](int q) { return q < bplS ? k : (q - bplS) / bplF; };
+  auto pick = [&](int q) { return (q < bplS || bplF == 0) ? k : (q - bplS) / bplF; };  // (k == 0: shared only)
   auto block = [&](int q, int j) { return li + LPR * (q < bplS ? q : q - bplS - j * bplF); };
   auto rsrc_for = [&](int j) {
     return j < k ? make_rsrc(down_exps + (size_t)__builtin_amdgcn_readlane(id_v, j) * mat, (uint32_t)mat)
@@ -336,11 +336,11 @@ static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
 // 16 float4 per thread.
 template <int QT>
 static hipError_t down_q(const DecodeArgs &a, hipStream_t st) {
-  const int nbF = a.F / 32, nbS = a.SF / 32;
-  int lpr = lanes_for(nbF);
+  const int nbF = a.k > 0 ? a.F / 32 : 0, nbS = a.SF / 32;
+  int lpr = nbF > 0 ? lanes_for(nbF) : 16;  // (a dense layer has only the shared row)
   if (nbS > 0 && lanes_for(nbS) < lpr) lpr = lanes_for(nbS);
   const size_t lds = (size_t)(a.k * nbF + nbS) * (XSTRIDE + 1) * sizeof(float);
-  const int n = a.k * a.F + a.SF;
+  const int n = a.k * nbF * 32 + a.SF;
   const bool wide = (size_t)((a.H + 256 / lpr - 1) / (256 / lpr)) * a.T >= 256 || n > 4 * 128 * 16;
   const int nt = wide ? 256 : 128;
   const dim3 grid((a.H + nt / lpr - 1) / (nt / lpr), a.T);

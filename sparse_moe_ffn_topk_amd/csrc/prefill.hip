@@ -454,11 +454,13 @@ size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32)
 
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
-  const size_t lds = prefill_sort_lds_bytes(T, E);
-  MOE_LAUNCH(5, k_sort_by_expert, dim3(1), dim3(1024), (uint32_t)lds, st, p.ids, T, k, E, p.offsets, p.pos, p.perm,
-             p.tiles, p.ntiles);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (k > 0) {  // (a dense layer, k == 0, has no routed pairs to sort)
+    const size_t lds = prefill_sort_lds_bytes(T, E);
+    MOE_LAUNCH(5, k_sort_by_expert, dim3(1), dim3(1024), (uint32_t)lds, st, p.ids, T, k, E, p.offsets, p.pos,
+               p.perm, p.tiles, p.ntiles);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   GemmArgs g{};
   g.T = T;
   g.k = k;

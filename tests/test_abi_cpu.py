@@ -51,6 +51,9 @@ def _cfg(**kw):
     (dict(top_k=5, n_groups=4, groups_used=2), "exceeds"),
     (dict(expert_ff=100), "expert_ff"), (dict(shared_ff=16), "shared_ff"),
     (dict(qtype=2), "qtype"), (dict(weights_scale=0.0), "weights_scale"), (dict(wsum_min=-1.0), "wsum_min"),
+    (dict(n_experts=0), "needs top_k 0"), (dict(n_experts=0, top_k=0), "needs its FFN size"),
+    (dict(n_experts=0, top_k=0, shared_ff=64, n_groups=2, groups_used=1), "dense layer needs"),
+    (dict(shared_ff=16416), "shared_ff"),
     (dict(swiglu_limit=-1.0), "swiglu"), (dict(swiglu_limit_shared=float("inf")), "swiglu"),
     (dict(swiglu_limit=float("nan")), "swiglu"),
 ])
@@ -63,6 +66,18 @@ def test_invalid_config_rejected(kw, msg):
                           C.c_void_p(0x3000), 1 << 30, None)
     assert rc == -1
     assert msg in L.moe_last_error().decode()
+
+
+def test_dense_layer_config_accepted():
+    # n_experts = top_k = 0: a dense SwiGLU FFN layer held in the shared tensors; expert_ff is ignored
+    L = moe.load_library()
+    for ff in (6144, 11776, 16384):
+        cfg = _cfg(n_experts=0, top_k=0, expert_ff=0, shared_ff=ff)
+        assert L.moe_workspace_bytes(C.byref(cfg), 1) > 0
+        assert L.moe_workspace_bytes(C.byref(cfg), 600) > 0
+    # routing a dense layer is a no-op that succeeds
+    cfg = _cfg(n_experts=0, top_k=0, expert_ff=0, shared_ff=64)
+    assert L.moe_router_topk(C.byref(cfg), None, None, 4, None, None, None, None, 0, None) == 0
 
 
 def test_workspace_bytes_grows_with_tokens():

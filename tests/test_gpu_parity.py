@@ -105,6 +105,19 @@ def test_layer_prefill_chunk(gpu):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("name,T", [("flint_dense", 1), ("flint_dense", 8), ("flint_dense", 40),
+                                    ("lfm25_dense", 1), ("lfm25_dense", 3), ("lfm25_dense", 520)])
+def test_dense_ffn_layer(gpu, name, T):
+    # dense leading SwiGLU FFN layers (no router), decode and grouped paths
+    wl = S.WORKLOADS[name]
+    _say(f"dense layer {name} SF={wl.shared_ff} Q4_{wl.qtype} T={T}")
+    w, x = _layer(wl, seed=17, tokens=T)
+    sample = None if T <= 40 else list(range(0, T, 29)) + [T - 1]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
+    print(f"[result] dense {name} T={T} max_row_rel_err={err:.3e}", flush=True)
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512)])
 def test_layer_swiglu_clamp(gpu, name, T):
     # SwiGLU clamp (ling_moe_ssd.js page: min(silu(g), L) * clamp(u, -L, L)),
