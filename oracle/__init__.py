@@ -40,7 +40,8 @@ def lib():
         L.mo_route.argtypes = [P, P, P, P, P, P]
         L.mo_expert_ffn.argtypes = [C.c_int, P, P, P, C.c_int32, C.c_int32, C.c_double, P, P]
         L.mo_layer.restype = C.c_int
-        L.mo_layer.argtypes = [P] + [P] * 8 + [P, C.c_int32, P, P, P, P, P]
+        L.mo_layer.argtypes = [P] + [P] * 9 + [P, C.c_int32, P, P, P, P, P]
+        L.mo_rmsnorm.argtypes = [P, P, C.c_int32, C.c_double, P]
         L.mo_sort_by_expert.argtypes = [P, C.c_int32, C.c_int32, P, P]
         _lib = L
     return _lib
@@ -51,7 +52,7 @@ class Cfg(C.Structure):
                 ("n_groups", C.c_int32), ("groups_used", C.c_int32),
                 ("expert_ff", C.c_int32), ("shared_ff", C.c_int32), ("qtype", C.c_int32),
                 ("weights_scale", C.c_double), ("wsum_min", C.c_double),
-                ("swiglu_limit", C.c_double), ("swiglu_limit_shared", C.c_double)]
+                ("swiglu_limit", C.c_double), ("swiglu_limit_shared", C.c_double), ("norm_eps", C.c_double)]
 
 
 Q4_0, Q4_1 = 0, 1
@@ -59,9 +60,9 @@ WSUM_MIN = 6.103515625e-5
 
 
 def make_cfg(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=Q4_1, n_groups=1, groups_used=None,
-             weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0):
+             weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0, norm_eps=1e-5):
     return Cfg(hidden, n_experts, top_k, n_groups, groups_used if groups_used is not None else n_groups,
-               expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared)
+               expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared, norm_eps)
 
 
 def _p(a):
@@ -151,7 +152,8 @@ def expert_ffn(qtype, gate, up, down, H, F, x, limit=0.0):
 
 def layer(cfg, w, x, resid=None, logits_in=None):
     """w: dict with router_w [E,H] f32, bias [E] f32 or None, gate_exps/up_exps/down_exps uint8,
-    gate_sh/up_sh/down_sh uint8 or None.  x: [T,H] f32.  Returns (out f64 [T,H], ids [T,k], w [T,k])."""
+    gate_sh/up_sh/down_sh uint8 or None, optional ffn_norm [H] f32 (then x is the residual stream and the
+    FFN input is its RMSNorm).  x: [T,H] f32.  Returns (out f64 [T,H], ids [T,k], w [T,k])."""
     x = _c(x, np.float32)
     T, H = x.shape
     k = cfg.top_k
@@ -159,16 +161,25 @@ def layer(cfg, w, x, resid=None, logits_in=None):
     bias = _c(w.get("bias"), np.float32)
     ge, ue, de = (_c(w[n], np.uint8) for n in ("gate_exps", "up_exps", "down_exps"))
     gs, us, ds = (_c(w.get(n), np.uint8) for n in ("gate_sh", "up_sh", "down_sh"))
+    gn = _c(w.get("ffn_norm"), np.float32)
     r = _c(resid, np.float32)
     li = _c(logits_in, np.float32)
     out = np.empty((T, H), np.float64)
     ids = np.empty((T, k), np.int32)
     ww = np.empty((T, k), np.float64)
-    rc = lib().mo_layer(C.byref(cfg), _p(rw), _p(bias), _p(ge), _p(ue), _p(de), _p(gs), _p(us), _p(ds),
+    rc = lib().mo_layer(C.byref(cfg), _p(rw), _p(bias), _p(ge), _p(ue), _p(de), _p(gs), _p(us), _p(ds), _p(gn),
                         _p(x), T, _p(r), _p(li), _p(out), _p(ids), _p(ww))
     if rc:
         raise ValueError("oracle: fewer selectable experts than top_k")
     return out, ids, ww
+
+
+def rmsnorm(x, g, eps):
+    """Pre-FFN RMSNorm of one token, rounded to f32 (mo_rmsnorm)."""
+    xv, gv = _c(x, np.float32), _c(g, np.float32)
+    out = np.empty(xv.size, np.float32)
+    lib().mo_rmsnorm(_p(xv), _p(gv), xv.size, float(eps), _p(out))
+    return out
 
 
 def sort_by_expert(ids, n_experts):

@@ -43,6 +43,7 @@ typedef struct {
   double wsum_min;
   double swiglu_limit;         /* routed experts' SwiGLU clamp L; 0 = none */
   double swiglu_limit_shared;  /* the shared expert's; 0 = none */
+  double norm_eps;             /* RMSNorm epsilon, used when a norm weight is given */
 } mo_cfg;
 
 /* ---------------------------------------------------------------- f16 ---- */
@@ -280,6 +281,20 @@ void mo_expert_ffn(int qtype, const uint8_t *gate, const uint8_t *up, const uint
 
 /* ------------------------------------------------------------- layer ---- */
 
+/* Pre-FFN RMSNorm of one token: xn_h = f32(x_h * s * g_h) with
+ * s = 1 / sqrt(mean_h(x_h^2) + eps) in double, h ascending ([FLINT], [LFM]
+ * file headers: the FFN input is rms_norm(x) * ffn_norm; the Ling page's
+ * normalising kernels divide by sqrt(sum(x^2) / n + eps) and then multiply by
+ * the weight; eps is the model's attention.layer_norm_rms_epsilon).  The
+ * result is rounded once to f32, as the pages keep the normalised input in an
+ * f32 buffer. */
+void mo_rmsnorm(const float *x, const float *g, int32_t H, double eps, float *xn) {
+  double ss = 0.0;
+  for (int h = 0; h < H; h++) ss += (double)x[h] * (double)x[h];
+  const double s = 1.0 / sqrt(ss / (double)H + eps);
+  for (int h = 0; h < H; h++) xn[h] = (float)((double)x[h] * s * (double)g[h]);
+}
+
 /* The whole MoE FFN step for T tokens:
  *   out[t][h] = resid[t][h] + sum_j w_tj * FFN_{id_tj}(x_t)[h] + FFN_shared(x_t)[h]
  * ([LING] moeAccum; [LFM] moeAccumB and the shared-expert addInPlace; the
@@ -288,13 +303,15 @@ void mo_expert_ffn(int qtype, const uint8_t *gate, const uint8_t *up, const uint
  *   of H rows x F/32 blocks, shared tensors likewise with SF (NULL if SF = 0).
  *   logits_in: NULL -> logits from the router weights in double; else [T][E]
  *   f32 logits used for both decisions and weights.
+ * ffn_norm: NULL -> x is the FFN input; else x is the residual stream and
+ * the FFN input is mo_rmsnorm(x) with that weight (x may alias resid).
  * A dense SwiGLU FFN layer is E = k = 0: no routing, out = resid +
  * FFN_shared(x) ([FLINT] and [LING] file headers: a dense SwiGLU FFN of 6144
  * on the first two layers; [LFM] likewise with 11776).
  * Outputs out[T][H] (double), ids[T][k], w[T][k].  Returns 0 or -1. */
 int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const uint8_t *gate_exps,
              const uint8_t *up_exps, const uint8_t *down_exps, const uint8_t *gate_sh,
-             const uint8_t *up_sh, const uint8_t *down_sh, const float *x, int32_t T,
+             const uint8_t *up_sh, const uint8_t *down_sh, const float *ffn_norm, const float *x, int32_t T,
              const float *resid, const float *logits_in, double *out, int32_t *ids, double *w) {
   int H = c->hidden, E = c->n_experts, k = c->top_k, F = c->expert_ff, SF = c->shared_ff;
   int bs = mo_block_bytes(c->qtype);
@@ -302,10 +319,15 @@ int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const ui
   double *l64 = (double *)malloc(sizeof(double) * (size_t)E);
   float *l32 = (float *)malloc(sizeof(float) * (size_t)E);
   double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+  float *xn = (float *)malloc(sizeof(float) * (size_t)H);
   double *y = (double *)malloc(sizeof(double) * (size_t)H);
   int rc = 0;
   for (int t = 0; t < T && rc == 0; t++) {
     const float *xt = x + (size_t)t * H;
+    if (ffn_norm) {
+      mo_rmsnorm(x + (size_t)t * H, ffn_norm, H, c->norm_eps, xn);
+      xt = xn;
+    }
     for (int h = 0; h < H; h++) xd[h] = xt[h];
     const double *lv = NULL;
     if (E == 0) {
@@ -338,6 +360,7 @@ int mo_layer(const mo_cfg *c, const float *router_w, const float *bias, const ui
   free(l64);
   free(l32);
   free(xd);
+  free(xn);
   free(y);
   return rc;
 }

@@ -376,6 +376,46 @@ def test_dense_layer_is_the_ffn_alone():
     assert np.allclose(out[0], resid[0].astype(np.float64) + 2.0 * _silu(10.0) * -7.0, rtol=1e-13, atol=1e-13)
 
 
+# ------------------------------------------------------------- RMSNorm ----
+
+def test_rmsnorm_closed_forms():
+    """Pre-FFN RMSNorm, x / sqrt(mean(x^2) + eps) * g (flint/lfm2 page file
+    headers: rms_norm(x) * ffn_norm; ling page: the normalising kernels divide
+    by sqrt(sum/n + eps) before the weight), rounded once to f32."""
+    # x = (3, 4): mean(x^2) = 12.5
+    got = O.rmsnorm(np.array([3.0, 4.0]), np.array([1.0, 1.0]), 0.0)
+    assert np.allclose(got, np.float32(np.array([3.0, 4.0]) / math.sqrt(12.5)), rtol=0, atol=0)
+    # constant c with eps = c^2: s = 1 / (c * sqrt(2)); a sum in place of the mean, or eps outside the
+    # square root, would give 1 / (c sqrt(H + 1)) or 1 / (c + c^2)
+    c, H = 0.5, 64
+    g = np.linspace(-2.0, 2.0, H).astype(np.float32)  # the weight is an f32 tensor
+    got = O.rmsnorm(np.full(H, c), g, c * c)
+    want = g.astype(np.float64) / math.sqrt(2.0)
+    assert np.allclose(got, want, rtol=1.2e-7, atol=0)  # one f32 rounding
+    # weight 1 and eps 0: every element of a constant vector becomes 1 (sign kept)
+    assert np.array_equal(O.rmsnorm(np.full(32, -7.25), np.ones(32), 0.0), -np.ones(32, np.float32))
+
+
+def test_rmsnorm_chained_dense_layer():
+    """With a norm weight the layer input is the residual stream h and the FFN
+    sees rms_norm(h) * w; the chained form passes h as both x and resid:
+    out = h + FFN(rms_norm(h) * w).  h = 2 * 1, w = 1, eps = 0: rms_norm(h) = 1,
+    and the constant-row FFN of test_dense_layer_is_the_ffn_alone gives
+    2 silu(10) (-7) on top."""
+    H = SF = 32
+    w = {"router_w": None, "bias": None, "gate_exps": None, "up_exps": None, "down_exps": None,
+         "gate_sh": _const_q4_1_rows(SF, 1, 10.0 / 32), "up_sh": _const_q4_1_rows(SF, 1, -7.0 / 32),
+         "down_sh": _const_q4_1_rows(H, 1, 0.0625), "ffn_norm": np.ones(H, np.float32)}
+    cfg = O.make_cfg(H, 0, 0, 0, SF, O.Q4_1, norm_eps=0.0)
+    h = np.full((1, H), 2.0, np.float32)
+    out, _, _ = O.layer(cfg, w, h, resid=h)
+    assert np.allclose(out[0], 2.0 + 2.0 * _silu(10.0) * -7.0, rtol=1e-13, atol=0)
+    # without the norm the same h feeds the FFN directly: g = 20, u = -14
+    w2 = dict(w, ffn_norm=None)
+    out2, _, _ = O.layer(cfg, w2, h, resid=h)
+    assert np.allclose(out2[0], 2.0 + 2.0 * _silu(20.0) * -14.0, rtol=1e-13, atol=0)
+
+
 # -------------------------------------------------------------- experts ----
 
 def _const_blocks(n_rows, cols, d, m, qtype=O.Q4_1, nib=0):
