@@ -79,7 +79,16 @@ enum {
  *                  page's swiglu kernel and per-layer clamp lists): with L > 0,
  *                  act = min(silu(g), L) * clamp(u, -L, L); 0 = no clamp.
  *                  A layer's own values; moe_stack_step applies one config
- *                  (and so one pair of limits) to all its layers.            */
+ *                  (and so one pair of limits) to all its layers.
+ *   norm_eps:      RMSNorm epsilon (attention.layer_norm_rms_epsilon), used
+ *                  when a layer's ffn_norm is given: finite, > 0 then.
+ *
+ * Pre-FFN RMSNorm: when moe_layer_weights.ffn_norm is not NULL, the x a call
+ * takes is the residual stream h and the FFN input is xn = f32(h * s * w),
+ * s = 1 / sqrt(mean(h^2) + eps) (the flint_moe_ssd.js and lfm2_moe_ssd.js
+ * file headers: ffn(rms_norm(x) * ffn_norm)); x may then alias resid, which
+ * is the chained form resid += FFN(rms_norm(resid) * w).  Without ffn_norm, x
+ * is the (already normalised) FFN input and must not alias resid.          */
 typedef struct {
   int32_t hidden, n_experts, top_k;
   int32_t n_groups, groups_used;
@@ -89,6 +98,7 @@ typedef struct {
   float wsum_min;
   float swiglu_limit;
   float swiglu_limit_shared;
+  float norm_eps;
 } moe_config;
 
 /* Weights of one MoE layer (GGUF tensor names in brackets).  Block tensors
@@ -104,6 +114,7 @@ typedef struct {
   const uint8_t *gate_shexp;  /* [SF][H/32] blocks, NULL iff SF == 0 (ffn_gate_shexp)   */
   const uint8_t *up_shexp;    /* [SF][H/32] blocks, NULL iff SF == 0 (ffn_up_shexp)     */
   const uint8_t *down_shexp;  /* [H][SF/32] blocks, NULL iff SF == 0 (ffn_down_shexp)   */
+  const float *ffn_norm;      /* [H] f32 pre-FFN RMSNorm weight, or NULL  (ffn_norm)    */
 } moe_layer_weights;
 
 /* Bytes of device workspace the calls below need for T tokens (16-byte
@@ -176,7 +187,8 @@ enum {
   MOE_KERNEL_SORT = 5,    /* pairs grouped by expert (grouped path)      */
   MOE_KERNEL_GROUP_GATEUP = 6, /* grouped gate||up MFMA GEMM + SwiGLU     */
   MOE_KERNEL_GROUP_DOWN = 7,   /* grouped down MFMA GEMM, weighted        */
-  MOE_KERNEL_COMBINE = 8       /* per-token sum into the residual         */
+  MOE_KERNEL_COMBINE = 8,      /* per-token sum into the residual         */
+  MOE_KERNEL_RMSNORM = 9       /* pre-FFN RMSNorm (when ffn_norm is given) */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
 int moe_kernel_timer_end(int32_t *count, double *total_ms);

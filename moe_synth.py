@@ -41,6 +41,8 @@ class Workload:
     has_bias: bool = False
     swiglu_limit: float = 0.0         # SwiGLU clamp of the routed experts (0: none)
     swiglu_limit_shared: float = 0.0  # and of the shared expert
+    norm_eps: float = 0.0             # > 0: layers carry a pre-FFN RMSNorm weight, 1 + N(0, norm_std)
+    norm_std: float = 0.1
     tokens: int = 1
     layers: int = 1
     # distributions
@@ -124,6 +126,8 @@ def make_layer(wl, layer=0, device="cpu", master=0):
         "down_exps": expert_tensor(E, H, F, wl.qtype, device, s("down_exps"), wl) if routed else None,
         "gate_sh": None, "up_sh": None, "down_sh": None,
     }
+    if wl.norm_eps > 0:
+        w["ffn_norm"] = normal((H,), wl.norm_std, device, s("ffn_norm")) + 1.0
     if SF:
         w["gate_sh"] = expert_tensor(1, SF, H, wl.qtype, device, s("gate_sh"), wl)[0]
         w["up_sh"] = expert_tensor(1, SF, H, wl.qtype, device, s("up_sh"), wl)[0]

@@ -29,12 +29,12 @@ class MoeConfig(C.Structure):
                 ("n_groups", C.c_int32), ("groups_used", C.c_int32),
                 ("expert_ff", C.c_int32), ("shared_ff", C.c_int32), ("qtype", C.c_int32),
                 ("weights_scale", C.c_float), ("wsum_min", C.c_float),
-                ("swiglu_limit", C.c_float), ("swiglu_limit_shared", C.c_float)]
+                ("swiglu_limit", C.c_float), ("swiglu_limit_shared", C.c_float), ("norm_eps", C.c_float)]
 
 
 class LayerWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("router_w", "router_bias", "gate_exps", "up_exps", "down_exps",
-                                          "gate_shexp", "up_shexp", "down_shexp")]
+                                          "gate_shexp", "up_shexp", "down_shexp", "ffn_norm")]
 
 
 def load_library(path=LIB_PATH):
@@ -73,20 +73,21 @@ def load_library(path=LIB_PATH):
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
             "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step")
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
-KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE = 5, 6, 7, 8
+KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE, KERNEL_RMSNORM = 5, 6, 7, 8, 9
 
 
 def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,
-                weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0):
+                weights_scale=1.0, wsum_min=WSUM_MIN, swiglu_limit=0.0, swiglu_limit_shared=0.0, norm_eps=1e-5):
     return MoeConfig(hidden, n_experts, top_k, n_groups, n_groups if groups_used is None else groups_used,
-                     expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared)
+                     expert_ff, shared_ff, qtype, weights_scale, wsum_min, swiglu_limit, swiglu_limit_shared, norm_eps)
 
 
 def config_for(wl):
     """MoeConfig of a moe_synth.Workload-like object."""
     return make_config(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
                        wl.groups_used, wl.weights_scale, swiglu_limit=getattr(wl, "swiglu_limit", 0.0),
-                       swiglu_limit_shared=getattr(wl, "swiglu_limit_shared", 0.0))
+                       swiglu_limit_shared=getattr(wl, "swiglu_limit_shared", 0.0),
+                       norm_eps=getattr(wl, "norm_eps", 0.0) or 1e-5)
 
 
 def _ptr(t):
@@ -115,11 +116,12 @@ def layer_weights(w):
     import torch
     _check(w.get("router_w"), "router_w", torch.float32)
     _check(w.get("bias"), "bias", torch.float32)
+    _check(w.get("ffn_norm"), "ffn_norm", torch.float32)
     for n in ("gate_exps", "up_exps", "down_exps", "gate_sh", "up_sh", "down_sh"):
         _check(w.get(n), n, torch.uint8)
     return LayerWeights(*[None if w.get(n) is None else w[n].data_ptr()
                           for n in ("router_w", "bias", "gate_exps", "up_exps", "down_exps",
-                                    "gate_sh", "up_sh", "down_sh")])
+                                    "gate_sh", "up_sh", "down_sh", "ffn_norm")])
 
 
 def _raise(rc):

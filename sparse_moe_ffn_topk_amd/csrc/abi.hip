@@ -37,7 +37,7 @@ size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 // uses logits/ids/wts/act; the grouped path works on chunks of at most
 // PREFILL_CHUNK tokens and adds the sort results and its act and Y rows.
 struct Layout {
-  size_t logits, ids, wts, act, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, total;
+  size_t logits, ids, wts, act, xn, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, total;
 };
 
 Layout layout(const moe_config &c, int32_t T) {
@@ -55,6 +55,7 @@ Layout layout(const moe_config &c, int32_t T) {
   L.ids = take((size_t)T * k * 4);
   L.wts = take((size_t)T * k * 4);
   L.act = take(((size_t)T * k * F + (size_t)T * SF) * 4);
+  L.xn = take((size_t)T * H * 4);  // normalised FFN input (layers with ffn_norm)
   const bool grouped = T > kDecodeMaxT || moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) > 65536;
   if (grouped) {
     L.offsets = take((E + 1) * 4);
@@ -136,6 +137,11 @@ int check_expert_ptrs(const moe_config &c, const moe_layer_weights *w) {
   if ((rc = check_ptr(w->down_shexp, "down_shexp", sh))) return rc;
   return MOE_OK;
 }
+
+// With a norm weight: check it and eps, and normalise x into the workspace.
+// *xin is then the normalised input (else x itself).
+int prologue_norm(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, void *ws,
+                  hipStream_t st, const float **xin);
 
 int launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(MOE_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -230,6 +236,23 @@ int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const floa
   return MOE_OK;
 }
 
+int prologue_norm(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, void *ws,
+                  hipStream_t st, const float **xin) {
+  *xin = x;
+  if (!w->ffn_norm) return MOE_OK;
+  float *xn = (float *)((char *)ws + layout(c, T).xn);
+  *xin = xn;
+  return launched(moe::launch_rmsnorm(x, w->ffn_norm, c.hidden, T, c.norm_eps, xn, st), "rmsnorm");
+}
+
+int check_norm(const moe_config &c, const moe_layer_weights *w) {
+  int rc;
+  if ((rc = check_ptr(w->ffn_norm, "ffn_norm", false))) return rc;
+  if (w->ffn_norm && !(std::isfinite(c.norm_eps) && c.norm_eps > 0))
+    return fail(MOE_EINVAL, "norm_eps must be finite and > 0 when ffn_norm is given");
+  return MOE_OK;
+}
+
 // Decode kernels stage a token's whole act row in LDS; configurations whose
 // row does not fit take the grouped path at any T.
 bool decode_fits(const moe_config &c) { return moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) <= 65536; }
@@ -260,7 +283,7 @@ int moe_kernel_timer_end(int32_t *count, double *total_ms);
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
   g_err.clear();
   if (g_timer.kernel) moe_kernel_timer_end(nullptr, nullptr);
-  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_COMBINE || capacity < 1 || capacity > (1 << 20))
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_RMSNORM || capacity < 1 || capacity > (1 << 20))
     return fail(MOE_EINVAL, "kernel timer: bad kernel %d or capacity %d", kernel, capacity);
   g_timer.start = new hipEvent_t[capacity];
   g_timer.stop = new hipEvent_t[capacity];
@@ -326,8 +349,11 @@ int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const flo
   if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
   if ((rc = check_ptr4(ids, "ids", true))) return rc;
   if ((rc = check_ptr4(weights, "weights", true))) return rc;
+  if ((rc = check_norm(*cfg, w))) return rc;
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
-  return router_topk_impl(*cfg, w, x, T, logits_in, ids, weights, workspace, (hipStream_t)stream);
+  const float *xin = x;
+  if (!logits_in && (rc = prologue_norm(*cfg, w, x, T, workspace, (hipStream_t)stream, &xin))) return rc;
+  return router_topk_impl(*cfg, w, xin, T, logits_in, ids, weights, workspace, (hipStream_t)stream);
 }
 
 int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
@@ -344,11 +370,14 @@ int moe_expert_ffn_q4(const moe_config *cfg, const moe_layer_weights *w, const f
   if ((rc = check_ptr4(ids, "ids", cfg->top_k > 0))) return rc;
   if ((rc = check_ptr4(weights, "weights", cfg->top_k > 0))) return rc;
   if ((rc = check_ptr(resid, "resid", true))) return rc;
-  if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
+  if ((rc = check_norm(*cfg, w))) return rc;
+  if (resid == x && !w->ffn_norm) return fail(MOE_EINVAL, "resid must not alias x (unless ffn_norm is given)");
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
+  const float *xin;
+  if ((rc = prologue_norm(*cfg, w, x, T, workspace, (hipStream_t)stream, &xin))) return rc;
   if (T > kDecodeMaxT || !decode_fits(*cfg))
-    return prefill_ffn_impl(*cfg, w, x, T, ids, weights, resid, workspace, (hipStream_t)stream);
-  return expert_ffn_impl(*cfg, w, x, T, const_cast<int32_t *>(ids), const_cast<float *>(weights), nullptr, resid,
+    return prefill_ffn_impl(*cfg, w, xin, T, ids, weights, resid, workspace, (hipStream_t)stream);
+  return expert_ffn_impl(*cfg, w, xin, T, const_cast<int32_t *>(ids), const_cast<float *>(weights), nullptr, resid,
                          workspace, (hipStream_t)stream);
 }
 
@@ -367,7 +396,8 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if ((rc = check_expert_ptrs(*cfg, w))) return rc;
   if ((rc = check_ptr(x, "x", true))) return rc;
   if ((rc = check_ptr(resid, "resid", true))) return rc;
-  if (resid == x) return fail(MOE_EINVAL, "resid must not alias x");
+  if ((rc = check_norm(*cfg, w))) return rc;
+  if (resid == x && !w->ffn_norm) return fail(MOE_EINVAL, "resid must not alias x (unless ffn_norm is given)");
   if ((rc = check_ptr4(ids_out, "ids_out", false))) return rc;
   if ((rc = check_ptr4(weights_out, "weights_out", false))) return rc;
   if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
@@ -375,6 +405,7 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
   float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
   hipStream_t st = (hipStream_t)stream;
+  if ((rc = prologue_norm(*cfg, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
   if (dense) {  // no router: only the FFN held in the shared-expert tensors
     if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
     return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);

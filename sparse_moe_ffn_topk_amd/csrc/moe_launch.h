@@ -11,7 +11,11 @@ namespace moe {
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
                                 hipStream_t st);
 
-// Scores, optional group limit, top-k, weights; one wave per token.
+// Pre-FFN RMSNorm of T tokens: xn = f32(x * s * g), s = 1/sqrt(mean(x^2) + eps)
+// with the sum of squares in f64; one block per token.
+hipError_t launch_rmsnorm(const float *x, const float *g, int H, int T, float eps, float *xn, hipStream_t st);
+
+// Scores, optional group limit, top-k, weights; one block per token.
 hipError_t launch_select(const float *logits, const float *bias, int T, int E, int k, int G, int Gu,
                          float scale, float wsum_min, int32_t *ids, float *wts, hipStream_t st);
 

@@ -136,6 +136,43 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
   }
 }
 
+// --------------------------------------------------------------- rmsnorm --
+
+// One 256-thread block per token: the sum of squares in f64 (fixed order:
+// per-thread strided partials, wave sums, then the four waves in order),
+// s = 1/sqrt(ss/H + eps), xn = f32(x * s * g).  H % 32 == 0.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, const float *__restrict__ g, int H,
+                                                 float eps, float *__restrict__ xn) {
+  __shared__ double part[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float4 *x4 = reinterpret_cast<const float4 *>(x + (size_t)t * H);
+  const float4 *g4 = reinterpret_cast<const float4 *>(g);
+  float4 *o4 = reinterpret_cast<float4 *>(xn + (size_t)t * H);
+  const int n4 = H >> 2;
+  double ss = 0.0;
+  for (int i = tid; i < n4; i += 256) {
+    const float4 v = x4[i];
+    ss = __builtin_fma((double)v.x, (double)v.x, ss);
+    ss = __builtin_fma((double)v.y, (double)v.y, ss);
+    ss = __builtin_fma((double)v.z, (double)v.z, ss);
+    ss = __builtin_fma((double)v.w, (double)v.w, ss);
+  }
+  ss = wave_sum_d(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const double s = 1.0 / sqrt(((part[0] + part[1]) + (part[2] + part[3])) / (double)H + (double)eps);
+  for (int i = tid; i < n4; i += 256) {
+    const float4 v = x4[i], w = g4[i];
+    o4[i] = make_float4((float)((double)v.x * s * (double)w.x), (float)((double)v.y * s * (double)w.y),
+                        (float)((double)v.z * s * (double)w.z), (float)((double)v.w * s * (double)w.w));
+  }
+}
+
+hipError_t launch_rmsnorm(const float *x, const float *g, int H, int T, float eps, float *xn, hipStream_t st) {
+  MOE_LAUNCH(9, k_rmsnorm, dim3(T), dim3(256), 0u, st, x, g, H, eps, xn);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- select --
 
 // One block of 256 threads per token.

@@ -20,7 +20,8 @@ TIE_TAU = 1e-6
 def oracle_cfg(wl):
     return O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
                       wl.groups_used, wl.weights_scale, swiglu_limit=wl.swiglu_limit,
-                      swiglu_limit_shared=wl.swiglu_limit_shared)
+                      swiglu_limit_shared=wl.swiglu_limit_shared,
+                      norm_eps=float(np.float32(wl.norm_eps or 1e-5)))  # the GPU config holds eps in f32
 
 
 def to_device(w, device="cuda"):
@@ -42,13 +43,20 @@ def scores64(wnp, x_t, bias):
     return p + (0.0 if bias is None else bias.astype(np.float64))
 
 
+def ffn_input(wl, wnp, x_t):
+    """The FFN input of one token: x itself, or its RMSNorm when the layer has a norm weight."""
+    if wnp.get("ffn_norm") is None:
+        return x_t
+    return O.rmsnorm(x_t, wnp["ffn_norm"], float(np.float32(wl.norm_eps or 1e-5)))
+
+
 def check_ids(wl, wnp, x, ids_gpu, ids_ref):
     """Return the list of tokens whose ids differ; assert each is a certified near-tie."""
     bad = []
     for t in range(ids_ref.shape[0]):
         if np.array_equal(ids_gpu[t], ids_ref[t]):
             continue
-        s = scores64(wnp, x[t], wnp.get("bias"))
+        s = scores64(wnp, ffn_input(wl, wnp, x[t]), wnp.get("bias"))
         a, b = set(ids_gpu[t].tolist()), set(ids_ref[t].tolist())
         disputed = sorted(a ^ b) if a != b else [int(i) for i, j in zip(ids_gpu[t], ids_ref[t]) if i != j]
         gap = max(s[disputed]) - min(s[disputed])
@@ -61,7 +69,7 @@ def oracle_given_routing(wl, wnp, x_t, ids, wts, resid_t=None):
     """Oracle FFN output of one token for forced ids / weights (used for certified near-ties)."""
     H, F, SF = wl.hidden, wl.expert_ff, wl.shared_ff
     out = np.zeros(H) if resid_t is None else resid_t.astype(np.float64).copy()
-    xd = x_t.astype(np.float64)
+    xd = ffn_input(wl, wnp, x_t).astype(np.float64)
     for e, wj in zip(ids, wts):
         out += float(wj) * O.expert_ffn(wl.qtype, wnp["gate_exps"][e], wnp["up_exps"][e], wnp["down_exps"][e],
                                         H, F, xd, limit=wl.swiglu_limit)

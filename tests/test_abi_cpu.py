@@ -32,8 +32,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    assert C.sizeof(moe.MoeConfig) == 12 * 4
-    assert C.sizeof(moe.LayerWeights) == 8 * 8
+    assert C.sizeof(moe.MoeConfig) == 13 * 4
+    assert C.sizeof(moe.LayerWeights) == 9 * 8
 
 
 def _cfg(**kw):
@@ -61,7 +61,7 @@ def test_invalid_config_rejected(kw, msg):
     L = moe.load_library()
     cfg = _cfg(**kw)
     assert L.moe_workspace_bytes(C.byref(cfg), 1) == 0
-    lw = moe.LayerWeights(*([0x1000] * 8))
+    lw = moe.LayerWeights(*([0x1000] * 8 + [0]))
     rc = L.moe_layer_step(C.byref(cfg), C.byref(lw), C.c_void_p(0x1000), 1, C.c_void_p(0x2000), None, None,
                           C.c_void_p(0x3000), 1 << 30, None)
     assert rc == -1
@@ -78,6 +78,25 @@ def test_dense_layer_config_accepted():
     # routing a dense layer is a no-op that succeeds
     cfg = _cfg(n_experts=0, top_k=0, expert_ff=0, shared_ff=64)
     assert L.moe_router_topk(C.byref(cfg), None, None, 4, None, None, None, None, 0, None) == 0
+
+
+def test_norm_rules():
+    # with ffn_norm the eps must be > 0, and x may alias resid (the chained form); without it, it may not
+    L = moe.load_library()
+    lw = moe.LayerWeights(*([0x1000] * 8 + [0x4000]))
+    bad = _cfg(norm_eps=0.0)
+    rc = L.moe_layer_step(C.byref(bad), C.byref(lw), C.c_void_p(0x2000), 1, C.c_void_p(0x3000), None, None,
+                          C.c_void_p(0x5000), 1 << 30, None)
+    assert rc == -1 and "norm_eps" in L.moe_last_error().decode()
+    ok = _cfg(norm_eps=1e-5)
+    # x == resid with a norm passes the argument checks (then stops at the missing workspace)
+    rc = L.moe_layer_step(C.byref(ok), C.byref(lw), C.c_void_p(0x2000), 1, C.c_void_p(0x2000), None, None,
+                          None, 0, None)
+    assert rc == -3, L.moe_last_error().decode()
+    lw.ffn_norm = None
+    rc = L.moe_layer_step(C.byref(ok), C.byref(lw), C.c_void_p(0x2000), 1, C.c_void_p(0x2000), None, None,
+                          None, 0, None)
+    assert rc == -1 and "alias" in L.moe_last_error().decode()
 
 
 def test_workspace_bytes_grows_with_tokens():

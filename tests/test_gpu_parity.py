@@ -118,6 +118,50 @@ def test_dense_ffn_layer(gpu, name, T):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512), ("flint_dense", 2),
+                                    ("lfm25", 1), ("ling", 1)])
+def test_layer_rmsnorm(gpu, name, T):
+    # pre-FFN RMSNorm given as ffn_norm (x is the residual stream; the FFN sees rms_norm(x) * w)
+    import dataclasses
+    wl = dataclasses.replace(S.WORKLOADS[name], norm_eps=1e-5)
+    _say(f"layer {name} T={T} with ffn_norm")
+    w, x = _layer(wl, seed=19, tokens=T)
+    x = x * 3.0 + 0.5  # a residual stream that is not already normalised
+    sample = None if T <= 8 else list(range(0, T, 41)) + [T - 1]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=S.to_numpy(w), sample=sample)
+    print(f"[result] rmsnorm {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("name", ["flint", "flint8"])
+def test_chained_stack_with_rmsnorm(gpu, name):
+    # the chained form: each layer's input is the running residual, resid += FFN(rms_norm(resid) * w);
+    # per layer against the oracle given that layer's input, and one stack call against per-layer calls
+    import dataclasses
+    moe = gpu
+    wl = dataclasses.replace(S.WORKLOADS[name], norm_eps=1e-5)
+    L = 3
+    _say(f"chained stack {name} L={L}")
+    layers = [S.make_layer(wl, layer=100 + l, device="cpu") for l in range(L)]
+    dev = [to_device(w) for w in layers]
+    h0 = S.make_x(wl, layer=99, device="cpu") * 2.0
+    cfg = moe.config_for(wl)
+    resid = h0.cuda().clone()
+    for l in range(L):
+        before = resid.cpu().numpy().copy()
+        moe.layer_step(cfg, dev[l], resid, resid)  # x aliases resid
+        torch.cuda.synchronize()
+        ref, _, _ = O.layer(oracle_cfg(wl), S.to_numpy(layers[l]), before, resid=before)
+        err = row_rel_err(resid.cpu().numpy() - before, ref - before).max()
+        print(f"[result] chained {name} layer {l} max_row_rel_err={err:.3e}", flush=True)
+        assert err <= REL_TOL
+    stacked = h0.cuda().clone()
+    st = moe.Stack(cfg, dev, [stacked] * L, stacked)
+    st.step()
+    torch.cuda.synchronize()
+    assert torch.equal(stacked, resid)
+
+
 @pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512)])
 def test_layer_swiglu_clamp(gpu, name, T):
     # SwiGLU clamp (ling_moe_ssd.js page: min(silu(g), L) * clamp(u, -L, L)),
