@@ -8,13 +8,19 @@ one decode token through all 47 layers: router logits, top-k, gate||up +
 SwiGLU, down + weighted residual accumulate, per layer, in layer order on one
 stream (each layer's expert reads start after the previous layer finished).
 
-Inputs are synthetic and seeded (moe_synth): x ~ N(0,1) fresh per layer, 16
-pre-generated steps cycled; router N(0, 0.05); Q4 scales U(0.001, 0.02) in f16;
+The stack is chained by default (--stack chained): every layer carries a
+pre-FFN RMSNorm weight (1 + N(0, 0.1)) and takes the running residual as its
+input, resid += FFN(rms_norm(resid) * w), so each layer's routing depends on
+the previous layer's output -- a real data-dependent chain, as in a decoder
+(the attention between the FFNs is outside this path).  --stack independent
+instead gives every layer its own synthetic, already normalised input
+(x ~ N(0,1), 16 pre-generated steps cycled).  Other inputs are synthetic and
+seeded (moe_synth): router N(0, 0.05); Q4 scales U(0.001, 0.02) in f16;
 uniform nibbles.  Weights are generated directly on the GPU.
 
-Timing: each of the 16 step variants (one native moe_stack_step call) is
-captured once as a HIP graph; W warm-up replays, then K timed replays between
-two synchronisations give the headline.  A second timed region of eager native
+Timing: each step variant (one native moe_stack_step call) is captured once as
+a HIP graph; W warm-up replays, then K timed replays between two
+synchronisations give the headline.  A second timed region of eager native
 steps measures kernel durations: the library attaches HIP start/stop events to
 every dispatch of the kernel under test, on its stream; the dominant kernel
 (gate||up + SwiGLU) gives the roofline line.  The CPU baseline times the f64
@@ -142,6 +148,10 @@ def main():
     ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stack", default="chained", choices=["chained", "independent"],
+                    help="chained (default): every layer has a pre-FFN RMSNorm weight and takes the running "
+                         "residual as its input, resid += FFN(rms_norm(resid) * w), a real data-dependent chain; "
+                         "independent: every layer takes its own synthetic (already normalised) input")
     ap.add_argument("--no-kernel-timer", action="store_true")
     ap.add_argument("--mode", default="graph", choices=["eager", "graph"],
                     help="graph: each step variant (one native moe_stack_step call) replayed as a captured HIP "
@@ -182,6 +192,11 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_copy": src.numel() * 4, "copies": 8}), flush=True)
         return
     wl = S.WORKLOADS[args.workload]
+    args.chained = args.stack == "chained" and args.workload != "prefill"
+    if args.chained:
+        import dataclasses
+        wl = dataclasses.replace(wl, norm_eps=1e-5)  # every layer carries its pre-FFN RMSNorm weight
+        args.slots = 1
     L, T, nS = wl.layers, wl.tokens, args.slots
     if wl.name == "ling":
         L = 28  # 28 generated copies of the one layer shape exceed the 256 MB MALL 4x over
@@ -207,8 +222,14 @@ def main():
     resident = sum(sum(t.numel() * t.element_size() for t in w.values() if t is not None) for w in layers)
     log(f"weights resident: {resident / 1e9:.2f} GB in {time.time() - t0:.1f}s")
 
-    xs = [[S.make_x(wl, T, layer=l, step=s, device=dev) for l in range(L)] for s in range(nS)]
-    resid = torch.zeros((T, wl.hidden), dtype=torch.float32, device=dev)
+    if args.chained:
+        # the chained stack: each layer's input is the running residual (x aliases resid),
+        # resid += FFN(rms_norm(resid) * ffn_norm) layer after layer
+        resid = S.make_x(wl, T, layer=0, step=0, device=dev)
+        xs = [[resid] * L]
+    else:
+        xs = [[S.make_x(wl, T, layer=l, step=s, device=dev) for l in range(L)] for s in range(nS)]
+        resid = torch.zeros((T, wl.hidden), dtype=torch.float32, device=dev)
     ws = moe.alloc_workspace(cfg, T, dev)
     ids = [torch.empty((L, T, wl.top_k), dtype=torch.int32, device=dev) for _ in range(nS)]
     wts = [torch.empty((L, T, wl.top_k), dtype=torch.float32, device=dev) for _ in range(nS)]
@@ -337,7 +358,8 @@ def main():
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl.name}_T{T}_{L}layers", "hidden": wl.hidden, "n_experts": wl.n_experts,
+        "config": {"workload": f"{wl.name}_T{T}_{L}layers" + ("_chained" if args.chained else ""),
+                   "hidden": wl.hidden, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "expert_ff": wl.expert_ff, "shared_ff": wl.shared_ff,
                    "qtype": f"Q4_{wl.qtype}", "tokens": T, "layers": L, "global_batch": T,
                    "parallelism": "single-gpu"},

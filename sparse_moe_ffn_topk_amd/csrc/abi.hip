@@ -405,6 +405,18 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
   float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
   hipStream_t st = (hipStream_t)stream;
+  const bool decode = T <= kDecodeMaxT && decode_fits(*cfg);
+  if (decode && !dense && w->ffn_norm && moe::router_fuses_norm(cfg->hidden, T)) {
+    // decode with a norm: the router kernel normalises x and writes xn; the
+    // gate||up kernel routes in its prologue
+    float *lg = (float *)((char *)workspace + L.logits);
+    float *xn = (float *)((char *)workspace + L.xn);
+    if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st,
+                                                 w->ffn_norm, cfg->norm_eps, xn),
+                       "router logits + rmsnorm")))
+      return rc;
+    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
+  }
   if ((rc = prologue_norm(*cfg, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
   if (dense) {  // no router: only the FFN held in the shared-expert tensors
     if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);

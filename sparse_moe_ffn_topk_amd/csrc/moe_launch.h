@@ -8,8 +8,13 @@
 namespace moe {
 
 // Router logits [T][E] f32 from W [E][H] and x [T][H] (f64 accumulation).
+// With gnorm (only where router_fuses_norm(H, T)): x is the residual stream,
+// normalised in the kernel (RMSNorm weight gnorm, eps), and the normalised
+// input is written to xn [T][H].
+int router_fuses_norm(int H, int T);
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
-                                hipStream_t st);
+                                hipStream_t st, const float *gnorm = nullptr, float eps = 0.f,
+                                float *xn = nullptr);
 
 // Pre-FFN RMSNorm of T tokens: xn = f32(x * s * g), s = 1/sqrt(mean(x^2) + eps)
 // with the sum of squares in f64; one block per token.

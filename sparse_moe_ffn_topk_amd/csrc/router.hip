@@ -29,13 +29,22 @@ namespace moe {
 // loads with an out-of-range offset past the row end read zeros, so there are
 // no branches between them).  Products and sums in f64, one f32 rounding.
 constexpr uint32_t ROUTER_OOB = 0x7ffffff0u;
+//
+// With gnorm != NULL (one pass: H <= 256 * NC) x is the residual stream and
+// each token is first normalised in registers: the wave's lanes hold the whole
+// row, so the sum of squares (f64) reduces across the wave, and the lanes form
+// xn = f32(x * s * g), s = 1/sqrt(ss/H + eps), before the dot; block 0 writes
+// xn for the FFN kernels.  Every block computes the same xn the same way.
 template <int TT, int NC>
 __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
-                                                    int H, int E, int T, float *__restrict__ logits) {
+                                                    int H, int E, int T, float *__restrict__ logits,
+                                                    const float *__restrict__ gnorm, float eps,
+                                                    float *__restrict__ xn_out) {
   const int e = blockIdx.x, lane = threadIdx.x;
   const uint32_t rowbytes = (uint32_t)H * 4u;
   const rsrc_t rw = make_rsrc(W + (size_t)e * H, rowbytes);
   const rsrc_t rx = make_rsrc(x, (uint32_t)T * rowbytes);
+  const rsrc_t rg = make_rsrc(gnorm, rowbytes);
   double acc[TT][2];
 #pragma unroll
   for (int t = 0; t < TT; t++) acc[t][0] = acc[t][1] = 0.0;
@@ -48,6 +57,11 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
       off[i] = o < rowbytes ? o : ROUTER_OOB;
       w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off[i], 0, 0);
     }
+    u32x4 gv[NC];
+    if (gnorm) {
+#pragma unroll
+      for (int i = 0; i < NC; i++) gv[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, (int)off[i], 0, 0);
+    }
 #pragma unroll
     for (int t = 0; t < TT; t++) {
       if (t < T) {
@@ -56,6 +70,26 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
         for (int i = 0; i < NC; i++)
           v[i] = __builtin_amdgcn_raw_buffer_load_b128(
               rx, (int)(off[i] == ROUTER_OOB ? ROUTER_OOB : (uint32_t)t * rowbytes + off[i]), 0, 0);
+        if (gnorm) {
+          double ss = 0.0;
+#pragma unroll
+          for (int i = 0; i < NC; i++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              const double f = (double)__uint_as_float(v[i][c]);
+              ss = __builtin_fma(f, f, ss);
+            }
+          const double sc = 1.0 / sqrt(wave_sum_d(ss) / (double)H + (double)eps);
+#pragma unroll
+          for (int i = 0; i < NC; i++) {
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+              v[i][c] = __float_as_uint(
+                  (float)((double)__uint_as_float(v[i][c]) * sc * (double)__uint_as_float(gv[i][c])));
+            if (e == 0 && off[i] != ROUTER_OOB)
+              *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xn_out) + (size_t)t * rowbytes + off[i]) = v[i];
+          }
+        }
 #pragma unroll
         for (int i = 0; i < NC; i++) {
           acc[t][0] = __builtin_fma((double)__uint_as_float(w[i][0]), (double)__uint_as_float(v[i][0]), acc[t][0]);
@@ -187,8 +221,11 @@ __global__ __launch_bounds__(256) void k_select(const float *__restrict__ logits
 
 // ---------------------------------------------------------------- launch --
 
+int router_fuses_norm(int H, int T) { return T <= 8 && H <= 4096; }
+
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
-                                hipStream_t st) {
+                                hipStream_t st, const float *gnorm, float eps, float *xn) {
+  if (gnorm && !router_fuses_norm(H, T)) return hipErrorInvalidValue;
   if (T <= 8) {
     // Chunks per lane and pass: the whole row in one pass up to H = 4096.
     const int n16 = (H + 3) / 4;
@@ -197,15 +234,15 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
 #define MOE_ROUTER_ROWS(TT)                                                                              \
   do {                                                                                                   \
     if (nc <= 2)                                                                                         \
-      MOE_LAUNCH(1, (k_router_rows<TT, 2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+      MOE_LAUNCH(1, (k_router_rows<TT, 2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
     else if (nc <= 4)                                                                                    \
-      MOE_LAUNCH(1, (k_router_rows<TT, 4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+      MOE_LAUNCH(1, (k_router_rows<TT, 4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
     else if (nc <= 8)                                                                                    \
-      MOE_LAUNCH(1, (k_router_rows<TT, 8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);              \
+      MOE_LAUNCH(1, (k_router_rows<TT, 8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
     else if (nc <= 12)                                                                                   \
-      MOE_LAUNCH(1, (k_router_rows<TT, 12>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);             \
+      MOE_LAUNCH(1, (k_router_rows<TT, 12>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
     else                                                                                                 \
-      MOE_LAUNCH(1, (k_router_rows<TT, 16>), grid, dim3(64), 0u, st, W, x, H, E, T, logits);             \
+      MOE_LAUNCH(1, (k_router_rows<TT, 16>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
   } while (0)
     if (T == 1)
       MOE_ROUTER_ROWS(1);
