@@ -55,7 +55,7 @@ class Cfg(C.Structure):
                 ("swiglu_limit", C.c_double), ("swiglu_limit_shared", C.c_double), ("norm_eps", C.c_double)]
 
 
-Q4_0, Q4_1 = 0, 1
+Q4_0, Q4_1, Q8_0 = 0, 1, 2
 WSUM_MIN = 6.103515625e-5
 
 
@@ -78,7 +78,7 @@ def f16(bits):
 
 
 def block_bytes(qtype):
-    return 20 if qtype == Q4_1 else 18
+    return {Q4_0: 18, Q4_1: 20, Q8_0: 34}[qtype]
 
 
 def dequant_row(qtype, row_bytes):

@@ -29,6 +29,7 @@
 
 #define MO_Q4_0 0
 #define MO_Q4_1 1
+#define MO_Q8_0 2
 
 /* Clamp on the sum of the picked sigmoids: 2^-14 in both router kernels
  * ([LFM] TOPK_SIG_BODY; [LING] routeLing). */
@@ -66,7 +67,7 @@ double mo_f16(uint16_t h) {
 
 /* --------------------------------------------------------- Q4 blocks ---- */
 
-int mo_block_bytes(int qtype) { return qtype == MO_Q4_1 ? 20 : 18; }
+int mo_block_bytes(int qtype) { return qtype == MO_Q4_1 ? 20 : (qtype == MO_Q8_0 ? 34 : 18); }
 
 /* One block of 32 weights -> 32 doubles.
  * Q4_1 ([FLINT] file header comment and the Q41DOT comment): 20 bytes, f16 d,
@@ -76,10 +77,17 @@ int mo_block_bytes(int qtype) { return qtype == MO_Q4_1 ? 20 : 18; }
  * formula and the 18-byte block are the GGUF definition named for the
  * decoder; the pages only show Q4_0's split into a nibble plane and an f16
  * scale plane ([LFM] planLayoutLfm2Moe), with the nibble bytes copied
- * unchanged, so the same nibble order is read. */
+ * unchanged, so the same nibble order is read.
+ * Q8_0 ([LFM] planLayoutLfm2Moe: an int8 plane of 32 bytes per 32 values and
+ * the same f16 scale plane; Q8_BLOCK): 34 bytes, f16 d then 32 signed bytes,
+ * element i = byte i; value = d*q. */
 void mo_dequant_block(int qtype, const uint8_t *blk, double *out) {
   uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
   double d = mo_f16(dbits);
+  if (qtype == MO_Q8_0) {
+    for (int i = 0; i < 32; i++) out[i] = d * (double)(int8_t)blk[2 + i];
+    return;
+  }
   const uint8_t *qs;
   double m = 0.0;
   if (qtype == MO_Q4_1) {

@@ -67,6 +67,26 @@ def test_q4_0_handbuilt_block():
     assert np.array_equal(O.dequant_row(O.Q4_0, b), v)
 
 
+def test_q8_0_handbuilt_block():
+    b, v = _read_block_fixture("q8_0_block.txt")
+    assert b.size == 34 and v.size == 32
+    assert np.array_equal(O.dequant_row(O.Q8_0, b), v)
+
+
+def test_q8_0_matches_numpy_views():
+    # Q8_0 through numpy's own f16 and int8 views of random blocks (incl. subnormal and negative scales)
+    rng = np.random.default_rng(5)
+    nb = 64
+    row = rng.integers(0, 256, size=(nb, 34), dtype=np.uint8)
+    row[:, 0:2] = rng.uniform(-2.0, 2.0, size=nb).astype(np.float16)[:, None].view(np.uint8)
+    row[0, 0:2] = np.array([np.float16(6e-7)]).view(np.uint8)  # a subnormal scale
+    d = row[:, 0:2].copy().view(np.float16).astype(np.float64)
+    q = row[:, 2:].copy().view(np.int8).astype(np.float64)
+    assert np.array_equal(O.dequant_row(O.Q8_0, row.reshape(-1)), (d * q).reshape(-1))
+    x = rng.integers(-4, 5, size=32 * nb).astype(np.float64)
+    assert O.row_dot(O.Q8_0, row.reshape(-1), x) == pytest.approx(float(((d * q).reshape(-1) * x).sum()), rel=1e-15)
+
+
 @pytest.mark.parametrize("nib,expect", [(8, 0.0), (0, -8.0), (15, 7.0)])
 def test_q4_0_constant_nibbles(nib, expect):
     d = np.float16(0.375)
