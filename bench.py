@@ -144,7 +144,8 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="flint",
-                    choices=["flint", "flint8", "lfm25", "ling", "tiny", "prefill", "flint_dense", "lfm25_dense"])
+                    choices=["flint", "flint8", "lfm25", "lfm25_q8", "ling", "tiny", "prefill", "flint_dense",
+                             "lfm25_dense"])
     ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -361,7 +362,7 @@ def main():
         "config": {"workload": f"{wl.name}_T{T}_{L}layers" + ("_chained" if args.chained else ""),
                    "hidden": wl.hidden, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "expert_ff": wl.expert_ff, "shared_ff": wl.shared_ff,
-                   "qtype": f"Q4_{wl.qtype}", "tokens": T, "layers": L, "global_batch": T,
+                   "qtype": {0: "Q4_0", 1: "Q4_1", 2: "Q8_0"}[wl.qtype], "tokens": T, "layers": L, "global_batch": T,
                    "parallelism": "single-gpu"},
         "weight_stream_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "us_per_layer": round(ms_step * 1e3 / L, 3), "tok_s_per_layer": round(tok_s * L, 1),

@@ -49,7 +49,7 @@ extern "C" {
 
 typedef struct ihipStream_t *moe_stream_t; /* a hipStream_t; NULL = default stream */
 
-enum { MOE_Q4_0 = 0, MOE_Q4_1 = 1 };
+enum { MOE_Q4_0 = 0, MOE_Q4_1 = 1, MOE_Q8_0 = 2 };
 
 enum {
   MOE_OK = 0,
@@ -71,7 +71,9 @@ enum {
  *   groups_used:   1 <= Gu <= G, k <= Gu * (E/G); Gu == G means no group limit
  *   expert_ff F:   32 <= F <= 8192, F % 32 == 0
  *   shared_ff SF:  0 (no shared expert) or 32 <= SF <= 16384, SF % 32 == 0
- *   qtype:         MOE_Q4_0 or MOE_Q4_1 (routed and shared experts alike)
+ *   qtype:         MOE_Q4_0, MOE_Q4_1 or MOE_Q8_0 (routed and shared experts
+ *                  alike; Q8_0 = f16 d and 32 signed bytes, 34 B, value d*q,
+ *                  as the lfm2_moe_ssd.js page's int8 expert plane)
  *   weights_scale: finite, > 0 (1 for Flint and LFM2.5, 2.5 for Ling)
  *   wsum_min:      finite, > 0 (2^-14 = 6.103515625e-5 on all three pages)
  *   swiglu_limit, swiglu_limit_shared: finite, >= 0.  SwiGLU clamp L of the

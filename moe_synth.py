@@ -22,8 +22,8 @@ import hashlib
 
 import torch
 
-Q4_0, Q4_1 = 0, 1
-BLOCK_BYTES = {Q4_0: 18, Q4_1: 20}
+Q4_0, Q4_1, Q8_0 = 0, 1, 2
+BLOCK_BYTES = {Q4_0: 18, Q4_1: 20, Q8_0: 34}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +60,10 @@ WORKLOADS = {
     "ling": Workload("ling", 2560, 512, 8, 768, 768, Q4_1, n_groups=8, groups_used=4, weights_scale=2.5,
                      has_bias=True, tokens=1, layers=1),
     "prefill": Workload("prefill", 2048, 256, 6, 512, 1024, Q4_1, tokens=512, layers=1),
+    # LFM2.5 shape with Q8_0 experts (the lfm2_moe_ssd.js page's int8 expert plane); Q8_0 scales are a
+    # row block's max |w| / 127, so they are drawn smaller
+    "lfm25_q8": Workload("lfm25_q8", 2048, 64, 4, 1536, 0, Q8_0, has_bias=True, tokens=1, layers=38,
+                         scale_lo=0.0001, scale_hi=0.0004),
     # dense leading SwiGLU FFN layers (no router): Flint and Ling 6144, LFM2.5 11776 (Q4_0 here).  The
     # models have two such layers; 16 generated copies are cycled so the weights exceed the 256 MB MALL.
     "flint_dense": Workload("flint_dense", 2048, 0, 0, 0, 6144, Q4_1, tokens=1, layers=16),
@@ -84,10 +88,11 @@ def normal(shape, std, device, seed):
 
 
 def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24):
-    """n_blocks random GGUF blocks as a uint8 tensor [n_blocks, 18|20].
+    """n_blocks random GGUF blocks as a uint8 tensor [n_blocks, 18|20|34].
 
     Byte layout: f16 d (little endian), for Q4_1 also f16 m, then 16 bytes of
-    nibbles.  d, m ~ U(lo, hi) rounded to f16; nibble bytes uniform 0..255."""
+    nibbles (Q4) or 32 signed bytes (Q8_0).  d, m ~ U(lo, hi) rounded to f16;
+    nibble and int8 bytes uniform 0..255."""
     bs = BLOCK_BYTES[qtype]
     out = torch.empty((n_blocks, bs), dtype=torch.uint8, device=device)
     g = _gen(device, seed)
@@ -101,7 +106,7 @@ def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24):
             m = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo).to(torch.float16)
             o[:, 2:4] = m.view(torch.uint8).view(n, 2)
             q0 = 4
-        o[:, q0:] = torch.randint(0, 256, (n, 16), generator=g, device=device, dtype=torch.uint8)
+        o[:, q0:] = torch.randint(0, 256, (n, bs - q0), generator=g, device=device, dtype=torch.uint8)
     return out
 
 

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_q4.so")
 
-MOE_Q4_0, MOE_Q4_1 = 0, 1
+MOE_Q4_0, MOE_Q4_1, MOE_Q8_0 = 0, 1, 2
 WSUM_MIN = 6.103515625e-5  # 2^-14
 
 _lib = None

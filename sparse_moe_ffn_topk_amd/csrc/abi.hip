@@ -95,7 +95,8 @@ int check_cfg(const moe_config *c) {
   }
   if (c->shared_ff != 0 && (c->shared_ff < 32 || c->shared_ff > 16384 || c->shared_ff % 32))
     return fail(MOE_EINVAL, "shared_ff %d: need 0 or 32 <= SF <= 16384, SF %% 32 == 0", c->shared_ff);
-  if (c->qtype != MOE_Q4_0 && c->qtype != MOE_Q4_1) return fail(MOE_EINVAL, "qtype %d: need 0 or 1", c->qtype);
+  if (c->qtype != MOE_Q4_0 && c->qtype != MOE_Q4_1 && c->qtype != MOE_Q8_0)
+    return fail(MOE_EINVAL, "qtype %d: need 0 (Q4_0), 1 (Q4_1) or 2 (Q8_0)", c->qtype);
   if (!(std::isfinite(c->weights_scale) && c->weights_scale > 0))
     return fail(MOE_EINVAL, "weights_scale must be finite and > 0");
   if (!(std::isfinite(c->wsum_min) && c->wsum_min > 0)) return fail(MOE_EINVAL, "wsum_min must be finite and > 0");

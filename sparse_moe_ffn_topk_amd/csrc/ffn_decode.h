@@ -1,5 +1,5 @@
 // ffn_decode.h -- expert FFNs for small T (decode): fused dequant-GEMVs
-// read straight from GGUF Q4_0 / Q4_1 blocks (gfx950, wave64).
+// read straight from GGUF Q4_0 / Q4_1 / Q8_0 blocks (gfx950, wave64).
 //
 // Computes, per token t and pick j (plus the always-on shared expert):
 //   act[f] = silu(g_f) * u_f,  g = Wg x_t, u = Wu x_t        (gate || up)
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
     e = ids[(size_t)t * k + j];
 
   const int nch = (nbH / LPR + NCH - 1) / NCH;  // LPR divides nbH
-  Raw5 ga[NCH], ua[NCH], gb[NCH], ub[NCH];
+  typedef typename QBlock<QT>::Raw Raw;
+  Raw ga[NCH], ua[NCH], gb[NCH], ub[NCH];
   rsrc_t rg = make_rsrc(gate_sh, (uint32_t)SF * rowbytes), ru = make_rsrc(up_sh, (uint32_t)SF * rowbytes);
   auto offset = [&](int c, int i) {
     const int b = li + LPR * (c * NCH + i);
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
   // early: every wave issues the same loads (routed waves at the out-of-range
   // offset, which moves no data), so each wave has the same count in flight and
   // routing waits for exactly its own inputs
-  auto load = [&](Raw5 *G, Raw5 *U, int c, bool early) {
+  auto load = [&](Raw *G, Raw *U, int c, bool early) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
       const uint32_t off = (early && !is_sh) ? OOB : offset(c, i);
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void k_gateup_swiglu(
   __syncthreads();
 
   float g = 0.f, v = 0.f;
-  auto compute = [&](const Raw5 *G, const Raw5 *U, int c) {
+  auto compute = [&](const Raw *G, const Raw *U, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
       const uint32_t off = offset(c, i);
@@ -233,8 +234,9 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   auto offset = [&](int q, int j) {
     return (live && q < nq) ? (j < k ? rowF : rowS) + (uint32_t)block(q, j) * BS : OOB;
   };
-  Raw5 A[NCH], B[NCH];
-  auto load = [&](Raw5 *W, int c) {
+  typedef typename QBlock<QT>::Raw Raw;
+  Raw A[NCH], B[NCH];
+  auto load = [&](Raw *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
       const int q = c * NCH + i, j = min(pick(q), k);
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
     }
   };
   float acc = 0.f;
-  auto compute = [&](const Raw5 *W, int c) {
+  auto compute = [&](const Raw *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCH; i++) {
       const int q = c * NCH + i, j = min(pick(q), k);

@@ -1,0 +1,13 @@
+// ffn_decode_q80.hip -- decode expert-FFN kernels instantiated for Q8_0 blocks.
+#include "ffn_decode.h"
+
+namespace moe {
+
+hipError_t decode_ffn_q80(const DecodeArgs &a, hipStream_t st) {
+  hipError_t e = gateup_q<MOE_Q8_0>(a, st);
+  if (e != hipSuccess) return e;
+  e = down_q<MOE_Q8_0>(a, st);
+  return e;
+}
+
+}  // namespace moe

@@ -5,15 +5,21 @@
 // element i in its low half and element i+16 in its high half (block layout of
 // the diskformer flint_moe_ssd.js page, file header and Q41DOT comment).
 //
+// Q8_0 = f16 d, 32 signed bytes (34 B, value d*q, element i = byte i; the
+// lfm2_moe_ssd.js page's int8 expert plane).
+//
 // A block's dot with 32 inputs is d*sum(q x) + m*sum(x) (the same page's
-// q41dot identity); Q4_0 is the case m = -8d.  The per-block input sum is
-// computed once per input vector and kept in LDS beside the inputs.
+// q41dot identity); Q4_0 is the case m = -8d.  Q8_0 takes the same form with
+// q' = q + 128 (each byte XOR 0x80, then converted as unsigned) and
+// m = -128d.  The per-block input sum is computed once per input vector and
+// kept in LDS beside the inputs.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #define MOE_Q4_0 0
 #define MOE_Q4_1 1
+#define MOE_Q8_0 2
 
 // Dword 3 of a raw buffer resource on gfx9-family parts (gfx950 included):
 // 32-bit data format, no swizzle, no stride; out-of-range loads return 0.
@@ -40,6 +46,7 @@ struct Raw5 {
 };
 
 template <> struct QBlock<MOE_Q4_1> {
+  typedef Raw5 Raw;
   static constexpr int bytes = 20;
   // Block at byte offset `off` (4-byte aligned: rows of 20-byte blocks).
   static __device__ __forceinline__ Raw5 load(rsrc_t r, uint32_t off) {
@@ -57,6 +64,7 @@ template <> struct QBlock<MOE_Q4_1> {
 };
 
 template <> struct QBlock<MOE_Q4_0> {
+  typedef Raw5 Raw;
   static constexpr int bytes = 18;
   // Block at byte offset `off` (2-byte aligned): five dwords from the dword
   // boundary at or below it, realigned in registers.
@@ -76,6 +84,36 @@ template <> struct QBlock<MOE_Q4_0> {
   // Nibble word k = block bytes 2+4k .. 5+4k.
   static __device__ __forceinline__ uint32_t nib(const Raw5 &b, uint32_t off, int k) {
     return (off & 2u) ? b.w[1 + k] : __builtin_amdgcn_alignbyte(b.w[1 + k], b.w[k], 2);
+  }
+};
+
+// Nine dwords from the dword boundary at or below a Q8_0 block (34 bytes,
+// 2-byte aligned).
+struct Raw9 {
+  uint32_t w[9];
+};
+template <> struct QBlock<MOE_Q8_0> {
+  typedef Raw9 Raw;
+  static constexpr int bytes = 34;
+  static __device__ __forceinline__ Raw9 load(rsrc_t r, uint32_t off) {
+    const uint32_t a = off & ~3u;
+    Raw9 b;
+    const u32x4 v0 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)a, 0, 0);
+    const u32x4 v1 = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(a + 16), 0, 0);
+    b.w[0] = v0.x; b.w[1] = v0.y; b.w[2] = v0.z; b.w[3] = v0.w;
+    b.w[4] = v1.x; b.w[5] = v1.y; b.w[6] = v1.z; b.w[7] = v1.w;
+    b.w[8] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(a + 32), 0, 0);
+    return b;
+  }
+  static __device__ __forceinline__ void scales(const Raw9 &b, uint32_t off, float &d, float &m) {
+    const uint16_t db = (off & 2u) ? (uint16_t)(b.w[0] >> 16) : (uint16_t)(b.w[0] & 0xffffu);
+    d = (float)__builtin_bit_cast(_Float16, db);
+    m = -128.0f * d;
+  }
+  // Byte word k = block bytes 2+4k .. 5+4k (elements 4k .. 4k+3), as q + 128.
+  static __device__ __forceinline__ uint32_t word(const Raw9 &b, uint32_t off, int k) {
+    const uint32_t w = (off & 2u) ? b.w[1 + k] : __builtin_amdgcn_alignbyte(b.w[1 + k], b.w[k], 2);
+    return w ^ 0x80808080u;
   }
 };
 
@@ -99,9 +137,9 @@ __device__ __forceinline__ void nib_word_dot(uint32_t w, const float4 &xl, const
   hi = __builtin_fmaf((float)(h >> 24), xh.w, hi);
 }
 
-// Dot of one loaded block with its 32 inputs xb (LDS) and their sum sx.
+// Q4 block dot with its 32 inputs xb (LDS) and their sum sx.
 template <int QT>
-__device__ __forceinline__ float block_dot(const Raw5 &b, uint32_t off, const float *xb, float sx) {
+__device__ __forceinline__ float block_dot_q4(const Raw5 &b, uint32_t off, const float *xb, float sx) {
   float d, m;
   QBlock<QT>::scales(b, off, d, m);
   float lo = 0.f, hi = 0.f;
@@ -115,17 +153,31 @@ __device__ __forceinline__ float block_dot(const Raw5 &b, uint32_t off, const fl
   return __builtin_fmaf(d, q, m * sx);
 }
 
-// Same dot with the 32 inputs given as 8 float4 already in registers.
+// Dot of one loaded block with its 32 inputs xb (LDS) and their sum sx.
 template <int QT>
-__device__ __forceinline__ float block_dot_regs(const Raw5 &b, uint32_t off, const float4 *x8, float sx) {
-  float d, m;
-  QBlock<QT>::scales(b, off, d, m);
-  float lo = 0.f, hi = 0.f;
+__device__ __forceinline__ float block_dot(const typename QBlock<QT>::Raw &b, uint32_t off, const float *xb,
+                                           float sx) {
+  if constexpr (QT == MOE_Q8_0) {
+    float d, m;
+    QBlock<QT>::scales(b, off, d, m);
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-  for (int k = 0; k < 4; k++) nib_word_dot(QBlock<QT>::nib(b, off, k), x8[k], x8[4 + k], lo, hi);
-  float q = __builtin_fmaf(hi, 0.0625f, lo);
-  return __builtin_fmaf(d, q, m * sx);
+    for (int k = 0; k < 8; k++) {
+      uint32_t w = QBlock<QT>::word(b, off, k);
+      asm("" : "+v"(w));  // one v_cvt_f32_ubyteN per byte (see nib_word_dot)
+      const float4 xv = *reinterpret_cast<const float4 *>(xb + 4 * k);
+      float &acc = (k & 1) ? a1 : a0;
+      acc = __builtin_fmaf((float)(w & 0xff), xv.x, acc);
+      acc = __builtin_fmaf((float)((w >> 8) & 0xff), xv.y, acc);
+      acc = __builtin_fmaf((float)((w >> 16) & 0xff), xv.z, acc);
+      acc = __builtin_fmaf((float)(w >> 24), xv.w, acc);
+    }
+    return __builtin_fmaf(d, a0 + a1, m * sx);
+  } else {
+    return block_dot_q4<QT>(b, off, xb, sx);
+  }
 }
+
 
 // LDS layout of an input vector: block b's 32 floats at b*XSTRIDE (36 floats:
 // a 16-byte pad per block spreads a lane group's 128-bit reads over the banks).

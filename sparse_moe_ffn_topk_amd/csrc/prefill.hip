@@ -22,7 +22,8 @@
 //  4. k_combine: resid[t] += sum_j Y[pos(t, j)] + Ysh[t], fixed order: no
 //     atomics, bitwise reproducible.
 //
-// Numerics of the GEMM: a Q4 block's nibbles q are exact in f16, so each
+// Numerics of the GEMM: a Q4 block's nibbles q (and a Q8_0 block's bytes as
+// q + 128) are exact in f16, so each
 // block's MFMA partial sum_k q_k x_k is exact up to f32 accumulation once x
 // is split as x = hi + lo (two f16, about 22 significant bits); the block's
 // f32 scale d and offset term m * sum_k x_k are applied per block in f32
@@ -102,44 +103,6 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
 
 // ------------------------------------------------------------- grouped GEMM --
 
-// Q4 block pieces a lane needs for one MFMA B operand: the f16 scale and
-// offset (as f32) and 8 nibble bytes -- bytes 0..7 or 8..15 of the block's 16.
-template <int QT> struct QPart;
-template <> struct QPart<MOE_Q4_1> {
-  static constexpr int bytes = 20;
-  static __device__ __forceinline__ void load(rsrc_t r, uint32_t off, int half, uint32_t &dm, u32x2 &nb) {
-    dm = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-    nb = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 4 + 8 * half), 0, 0);
-  }
-  static __device__ __forceinline__ void scales(uint32_t dm, uint32_t, float &d, float &m) {
-    d = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm & 0xffffu));
-    m = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm >> 16));
-  }
-};
-template <> struct QPart<MOE_Q4_0> {
-  static constexpr int bytes = 18;
-  // The block starts 2-byte aligned: load 3 aligned dwords covering the 8
-  // nibble bytes and realign them; the scale comes from the dword holding it.
-  static __device__ __forceinline__ void load(rsrc_t r, uint32_t off, int half, uint32_t &dm, u32x2 &nb) {
-    dm = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off & ~3u), 0, 0);
-    const uint32_t s = off + 2 + 8 * half, a = s & ~3u;
-    const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(r, (int)a, 0, 0);
-    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(a + 8), 0, 0);
-    const uint32_t l0 = lo.x, l1 = lo.y;
-    if (s & 2u) {
-      nb.x = __builtin_amdgcn_alignbyte(l1, l0, 2);
-      nb.y = __builtin_amdgcn_alignbyte(hi, l1, 2);
-    } else {
-      nb.x = l0;
-      nb.y = l1;
-    }
-  }
-  static __device__ __forceinline__ void scales(uint32_t dm, uint32_t off, float &d, float &m) {
-    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((off & 2u) ? (dm >> 16) : (dm & 0xffffu)));
-    m = -8.0f * d;
-  }
-};
-
 // 8 nibbles of 8 bytes (low halves, or high halves if hi) as exact f16 q,
 // in the order k = 0,2,1,3,4,6,5,7 of the bytes (two mask-ors per dword).
 __device__ __forceinline__ half8 nibbles_f16(u32x2 nb, bool hi) {
@@ -159,6 +122,17 @@ __device__ __forceinline__ half8 nibbles_f16(u32x2 nb, bool hi) {
 // (matches nibbles_f16's order 0,2,1,3,4,6,5,7).
 __device__ __forceinline__ int kperm(int j) { return (j & 4) | ((j & 1) << 1) | ((j >> 1) & 1); }
 
+// 8 bytes (Q8_0 values, already as q + 128) as exact f16 q + 128 in the same
+// order 0,2,1,3,4,6,5,7 (two mask-ors per dword: f16 1024 + b, minus 1024).
+__device__ __forceinline__ half8 bytes_f16(u32x2 nb) {
+  const uint32_t w0 = nb.x, w1 = nb.y;
+  const uint32_t a = (w0 & 0x00FF00FFu) | 0x64006400u, b = ((w0 >> 8) & 0x00FF00FFu) | 0x64006400u;
+  const uint32_t c = (w1 & 0x00FF00FFu) | 0x64006400u, d = ((w1 >> 8) & 0x00FF00FFu) | 0x64006400u;
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v) - (half8)(_Float16)1024.0f;
+}
+
 enum { GG_GATEUP = 0, GG_DOWN = 1 };
 
 struct GemmArgs {
@@ -176,13 +150,14 @@ struct GemmArgs {
   float lim, lim_sh;         // GATEUP: SwiGLU clamp of routed / shared experts (0: none)
 };
 
-// K is walked in chunks of KB Q4 blocks.  Per chunk a block stages, in LDS,
-// the raw bytes of its 256 weight rows (BROW bytes each: 4 x 20, or 4 x 18
-// plus 2 bytes of alignment slack) read with contiguous 16-byte loads, and
-// its 16 tokens' inputs as f16 hi + lo in the MFMA lanes' k order.
+// K is walked in chunks of KB blocks.  Per chunk a block stages, in LDS, the
+// raw bytes of its 256 weight rows (brow<QT>() bytes each: 4 x 20; 4 x 18 or
+// 4 x 34 plus 2 bytes of alignment slack, rounded up to 16) read with
+// contiguous 16-byte loads, and its 16 tokens' inputs as f16 hi + lo in the
+// MFMA lanes' k order.
 constexpr int KB = 4;
-constexpr int BROW = 80;
-constexpr int BRW = BROW / 4;          // dwords per staged row
+template <int QT>
+constexpr int brow() { return QT == MOE_Q8_0 ? 144 : 80; }
 constexpr int APAD = KB * 32 + 8;      // f16 per staged input row (16-byte pad)
 
 // A chunk: 16 threads per token, 8 consecutive k each.
@@ -228,28 +203,33 @@ __device__ __forceinline__ void a_store(const AStage &st, _Float16 (*ahi)[APAD],
   if ((seg & 3) == 0) asum[blk][m] = s;
 }
 
-// Scale, offset and the lane's 8 nibble bytes of block jb of a staged row
-// (w: the row's BRW dwords; o0: byte offset of block 0 in them).
+// Scale, offset and the lane's MFMA B fragment (8 k values of block jb of a
+// staged row as exact f16, in the order kperm() gives) for k-octet kq
+// (w: the row's dwords; o0: byte offset of block 0 in them).  Q4: bytes 0..7
+// or 8..15 of the nibbles (kq odd), low nibbles for kq < 2, high otherwise.
+// Q8_0: bytes 8kq .. 8kq+7 as q + 128, with m = -128 d.
 template <int QT> struct QStaged;
 template <> struct QStaged<MOE_Q4_1> {
-  static __device__ __forceinline__ void get(const uint32_t *w, int, int jb, int half, float &d, float &m,
-                                             u32x2 &nb) {
+  static __device__ __forceinline__ half8 frag(const uint32_t *w, int, int jb, int kq, float &d, float &m) {
     const uint32_t dm = w[5 * jb];
     d = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm & 0xffffu));
     m = (float)__builtin_bit_cast(_Float16, (uint16_t)(dm >> 16));
+    const int half = kq & 1;
+    u32x2 nb;
     nb.x = w[5 * jb + 1 + 2 * half];
     nb.y = w[5 * jb + 2 + 2 * half];
+    return nibbles_f16(nb, kq >= 2);
   }
 };
 template <> struct QStaged<MOE_Q4_0> {
-  static __device__ __forceinline__ void get(const uint32_t *w, int o0, int jb, int half, float &d, float &m,
-                                             u32x2 &nb) {
+  static __device__ __forceinline__ half8 frag(const uint32_t *w, int o0, int jb, int kq, float &d, float &m) {
     const int o = o0 + 18 * jb;  // even
     const uint32_t dw = w[o >> 2];
     d = (float)__builtin_bit_cast(_Float16, (uint16_t)((o & 2) ? (dw >> 16) : (dw & 0xffffu)));
     m = -8.0f * d;
-    const int s = o + 2 + 8 * half, a = s >> 2;
+    const int s = o + 2 + 8 * (kq & 1), a = s >> 2;
     const uint32_t w0 = w[a], w1 = w[a + 1], w2 = w[a + 2];
+    u32x2 nb;
     if (s & 2) {
       nb.x = __builtin_amdgcn_alignbyte(w1, w0, 2);
       nb.y = __builtin_amdgcn_alignbyte(w2, w1, 2);
@@ -257,6 +237,28 @@ template <> struct QStaged<MOE_Q4_0> {
       nb.x = w0;
       nb.y = w1;
     }
+    return nibbles_f16(nb, kq >= 2);
+  }
+};
+template <> struct QStaged<MOE_Q8_0> {
+  static __device__ __forceinline__ half8 frag(const uint32_t *w, int o0, int jb, int kq, float &d, float &m) {
+    const int o = o0 + 34 * jb;  // even
+    const uint32_t dw = w[o >> 2];
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((o & 2) ? (dw >> 16) : (dw & 0xffffu)));
+    m = -128.0f * d;
+    const int s = o + 2 + 8 * kq, a = s >> 2;
+    const uint32_t w0 = w[a], w1 = w[a + 1], w2 = w[a + 2];
+    u32x2 nb;
+    if (s & 2) {
+      nb.x = __builtin_amdgcn_alignbyte(w1, w0, 2);
+      nb.y = __builtin_amdgcn_alignbyte(w2, w1, 2);
+    } else {
+      nb.x = w0;
+      nb.y = w1;
+    }
+    nb.x ^= 0x80808080u;
+    nb.y ^= 0x80808080u;
+    return bytes_f16(nb);
   }
 };
 
@@ -266,8 +268,10 @@ template <> struct QStaged<MOE_Q4_0> {
 // from LDS, barrier.  Blocks past K get d = m = 0 (their inputs are 0 too).
 template <int QT, int MODE>
 __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
-  constexpr int BS = QPart<QT>::bytes;
+  constexpr int BS = QBlock<QT>::bytes;
   constexpr int NM = MODE == GG_GATEUP ? 2 : 1;  // weight matrices
+  constexpr int BRW = brow<QT>() / 4;            // staged dwords per row
+  constexpr int PR = brow<QT>() / 16;            // 16-byte pieces per row
   __shared__ __attribute__((aligned(16))) uint32_t bst[NM][256][BRW];
   __shared__ __attribute__((aligned(16))) _Float16 ahi[16][APAD], alo[16][APAD];
   __shared__ __attribute__((aligned(16))) float asum[KB][16];
@@ -321,14 +325,14 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   const float *arows = MODE == GG_GATEUP ? a.x : (shared ? a.act_sh : a.act);
   const int astride = K;
 
-  // weight pieces of this thread: p = tid + 256 i (i < 5) -> row p / 5, 16 bytes p % 5
-  u32x4 breg[NM][5];
+  // weight pieces of this thread: p = tid + 256 i (i < PR) -> row p / PR, 16 bytes p % PR
+  u32x4 breg[NM][PR];
   auto b_issue = [&](int kc) {
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) {
 #pragma unroll
-      for (int i = 0; i < 5; i++) {
-        const int p = tid + 256 * i, row = p / 5, j = p - 5 * row;
+      for (int i = 0; i < PR; i++) {
+        const int p = tid + 256 * i, row = p / PR, j = p - PR * row;
         const int grow = r0 + row;
         const uint32_t seg = (uint32_t)grow * rowbytes + (uint32_t)kc * BS;
         const uint32_t off = (grow < R && kc < nbK) ? (seg & ~3u) + 16u * j : 0x7ffffff0u;
@@ -340,8 +344,8 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 #pragma unroll
     for (int mt = 0; mt < NM; mt++) {
 #pragma unroll
-      for (int i = 0; i < 5; i++) {
-        const int p = tid + 256 * i, row = p / 5, j = p - 5 * row;
+      for (int i = 0; i < PR; i++) {
+        const int p = tid + 256 * i, row = p / PR, j = p - PR * row;
         *reinterpret_cast<u32x4 *>(&bst[mt][row][4 * j]) = breg[mt][i];
       }
     }
@@ -350,8 +354,6 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   // lane roles in the MFMA: token m = lane%16 (A) / column n = lane%16 (B),
   // k-octet kq = lane/16; D rows (tokens) 4*kq + i, column n
   const int n = lane & 15, kq = lane >> 4;
-  const int half = kq & 1;       // nibble bytes 0..7 or 8..15
-  const bool hin = kq >= 2;      // high nibbles (k + 16)
   f32x4 acc[NM][4];
 #pragma unroll
   for (int mt = 0; mt < NM; mt++)
@@ -389,10 +391,8 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           float d, m;
-          u32x2 nb;
-          QStaged<QT>::get(bst[mt][wave * 64 + 16 * c + n], o0[c], jb, half, d, m, nb);
+          const half8 q = QStaged<QT>::frag(bst[mt][wave * 64 + 16 * c + n], o0[c], jb, kq, d, m);
           if (!valid) d = m = 0.f;
-          const half8 q = nibbles_f16(nb, hin);
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
           z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, q, z, 0, 0, 0);
           z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, q, z, 0, 0, 0);
@@ -492,6 +492,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     dim3 grid(g.max_routed_tiles + shtiles, (rows + 255) / 256);
     if (p.qtype == MOE_Q4_1)
       MOE_LAUNCH(6, (k_group_gemm<MOE_Q4_1, GG_GATEUP>), grid, dim3(256), 0u, st, g);
+    else if (p.qtype == MOE_Q8_0)
+      MOE_LAUNCH(6, (k_group_gemm<MOE_Q8_0, GG_GATEUP>), grid, dim3(256), 0u, st, g);
     else
       MOE_LAUNCH(6, (k_group_gemm<MOE_Q4_0, GG_GATEUP>), grid, dim3(256), 0u, st, g);
   }
@@ -507,6 +509,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
     if (p.qtype == MOE_Q4_1)
       MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_1, GG_DOWN>), grid, dim3(256), 0u, st, g);
+    else if (p.qtype == MOE_Q8_0)
+      MOE_LAUNCH(7, (k_group_gemm<MOE_Q8_0, GG_DOWN>), grid, dim3(256), 0u, st, g);
     else
       MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_0, GG_DOWN>), grid, dim3(256), 0u, st, g);
   }

@@ -50,7 +50,7 @@ def _cfg(**kw):
     (dict(n_groups=4, groups_used=5), "groups_used"), (dict(n_groups=4, groups_used=0), "groups_used"),
     (dict(top_k=5, n_groups=4, groups_used=2), "exceeds"),
     (dict(expert_ff=100), "expert_ff"), (dict(shared_ff=16), "shared_ff"),
-    (dict(qtype=2), "qtype"), (dict(weights_scale=0.0), "weights_scale"), (dict(wsum_min=-1.0), "wsum_min"),
+    (dict(qtype=3), "qtype"), (dict(weights_scale=0.0), "weights_scale"), (dict(wsum_min=-1.0), "wsum_min"),
     (dict(n_experts=0), "needs top_k 0"), (dict(n_experts=0, top_k=0), "needs its FFN size"),
     (dict(n_experts=0, top_k=0, shared_ff=64, n_groups=2, groups_used=1), "dense layer needs"),
     (dict(shared_ff=16416), "shared_ff"),

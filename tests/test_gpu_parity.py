@@ -215,6 +215,28 @@ def test_layer_q4_0_unaligned_rows(gpu, H, F, SF, T):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("name,T", [("lfm25_q8", 1), ("lfm25_q8", 3), ("lfm25_q8", 520)])
+def test_layer_q8_0(gpu, name, T):
+    # Q8_0 experts (f16 d, 32 signed bytes; the lfm2_moe_ssd.js page's int8 expert plane), decode and grouped
+    wl = S.WORKLOADS[name]
+    _say(f"layer {name} Q8_0 T={T}")
+    w, x = _layer(wl, seed=23, tokens=T)
+    sample = None if T <= 8 else list(range(0, T, 31)) + [T - 1]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
+    print(f"[result] q8_0 {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
+@pytest.mark.parametrize("H,F,SF,T", [(96, 96, 64, 3), (96, 96, 64, 20), (2080, 160, 224, 1), (2080, 160, 224, 9)])
+def test_layer_q8_0_odd_rows_and_shared(gpu, H, F, SF, T):
+    # odd block counts give Q8_0 rows at 2-byte alignment; a shared expert too (T <= 8 decode, else grouped)
+    wl = S.Workload("q80odd", H, 16, 3, F, SF, S.Q8_0, has_bias=True, scale_lo=0.0001, scale_hi=0.0004)
+    _say("q8_0 odd rows", H, F, SF, "T", T)
+    w, x = _layer(wl, seed=H + F + T, tokens=T)
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    assert err <= REL_TOL
+
+
 def test_layer_single_expert_and_k_equals_E(gpu):
     for E, k in ((1, 1), (6, 6)):
         wl = S.Workload("kE", 128, E, k, 64, 32, S.Q4_1)
