@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--slots", type=int, default=16, help="distinct input steps cycled")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swiglu-limit", type=float, default=0.0,
+                    help="SwiGLU clamp L for the routed and the shared experts (0: none)")
     ap.add_argument("--stack", default="chained", choices=["chained", "independent"],
                     help="chained (default): every layer has a pre-FFN RMSNorm weight and takes the running "
                          "residual as its input, resid += FFN(rms_norm(resid) * w), a real data-dependent chain; "
@@ -194,6 +196,9 @@ def main():
         return
     wl = S.WORKLOADS[args.workload]
     args.chained = args.stack == "chained" and args.workload != "prefill"
+    if args.swiglu_limit > 0:
+        import dataclasses
+        wl = dataclasses.replace(wl, swiglu_limit=args.swiglu_limit, swiglu_limit_shared=args.swiglu_limit)
     if args.chained:
         import dataclasses
         wl = dataclasses.replace(wl, norm_eps=1e-5)  # every layer carries its pre-FFN RMSNorm weight
@@ -359,7 +364,8 @@ def main():
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{wl.name}_T{T}_{L}layers" + ("_chained" if args.chained else ""),
+        "config": {"workload": f"{wl.name}_T{T}_{L}layers" + ("_chained" if args.chained else "")
+                               + (f"_clamp{args.swiglu_limit:g}" if args.swiglu_limit > 0 else ""),
                    "hidden": wl.hidden, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "expert_ff": wl.expert_ff, "shared_ff": wl.shared_ff,
                    "qtype": {0: "Q4_0", 1: "Q4_1", 2: "Q8_0"}[wl.qtype], "tokens": T, "layers": L, "global_batch": T,

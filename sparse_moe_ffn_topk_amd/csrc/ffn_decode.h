@@ -28,8 +28,10 @@
 
 namespace moe {
 
-// Blocks per lane held in registers per chunk (two chunks in flight).
-constexpr int NCH = 4;
+// Blocks per lane held in registers per chunk, two chunks in flight: 2 in the
+// gate||up kernel (whose blocks then fit two to a CU), 4 in the down kernel.
+constexpr int NCH = 2;
+constexpr int NCHD = 4;
 // Offset past every buffer resource's range: loads there return zeros without
 // touching memory, and an all-zero block contributes exactly 0 to a dot.
 constexpr uint32_t OOB = 0x7ffffff0u;
@@ -90,7 +92,7 @@ __device__ __forceinline__ float silu_mul(float g, float u, float L) {
 // With logits != NULL every block routes its token (select_load/select_rank)
 // and block (0, t) writes the token's ids and weights; otherwise ids are read.
 template <int QT, int LPR, int XR>
-__global__ __launch_bounds__(256) void k_gateup_swiglu(
+__global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
     const float *__restrict__ x, int32_t *__restrict__ ids, float *__restrict__ wts,
     const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int H, int k, int F, int SF,
     const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   const bool live = h < H;
   const int bplF = nbF / LPR, bplS = nbS / LPR;  // LPR divides both
   const int nq = bplS + k * bplF;
-  const int nch = (nq + NCH - 1) / NCH;
+  const int nch = (nq + NCHD - 1) / NCHD;
   const size_t mat = (size_t)H * nbF * BS;
   const uint32_t rowF = (uint32_t)h * nbF * BS;
   const uint32_t rowS = (uint32_t)h * nbS * BS;
@@ -235,19 +237,19 @@ __global__ __launch_bounds__(NT) void k_down_accum(
     return (live && q < nq) ? (j < k ? rowF : rowS) + (uint32_t)block(q, j) * BS : OOB;
   };
   typedef typename QBlock<QT>::Raw Raw;
-  Raw A[NCH], B[NCH];
+  Raw A[NCHD], B[NCHD];
   auto load = [&](Raw *W, int c) {
 #pragma unroll
-    for (int i = 0; i < NCH; i++) {
-      const int q = c * NCH + i, j = min(pick(q), k);
+    for (int i = 0; i < NCHD; i++) {
+      const int q = c * NCHD + i, j = min(pick(q), k);
       W[i] = QBlock<QT>::load(rsrc_for(j), offset(q, j));
     }
   };
   float acc = 0.f;
   auto compute = [&](const Raw *W, int c) {
 #pragma unroll
-    for (int i = 0; i < NCH; i++) {
-      const int q = c * NCH + i, j = min(pick(q), k);
+    for (int i = 0; i < NCHD; i++) {
+      const int q = c * NCHD + i, j = min(pick(q), k);
       const int ab = min(j * nbF + block(q, j), nbAll - 1);  // staged act block (shared row after routed)
       const float d = block_dot<QT>(W[i], offset(q, j), xs + ab * XSTRIDE, sx[ab]);
       const int wbits = j < k ? __builtin_amdgcn_readlane(__float_as_int(wt_v), j) : __float_as_int(1.0f);
