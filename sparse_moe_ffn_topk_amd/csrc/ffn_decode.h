@@ -191,29 +191,40 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   if (li == LPR - 1 && live) out[row] = silu_mul(g, v, is_sh ? lim_sh : lim);
 }
 
-// grid.x: tiles of NT/LPR outputs h; grid.y: token t.  Each lane walks a flat
-// list of (row, block) tasks -- the shared row h first (its loads need no
-// routing and go out at once), then the token's k routed rows h -- two
-// register chunks at a time.  The token's ids and weights are fetched into
-// lanes 0..k-1 ahead of everything else.
-template <int QT, int LPR, int XR, int NT>
+// grid.x: tiles of outputs h; grid.y: token t.  Each lane of a row's lane
+// group walks a flat list of (row, block) tasks -- the shared row h first (its
+// loads need no routing and go out at once), then the token's k routed rows h
+// -- two register chunks at a time.  With S > 1 the list of a row is split
+// over S waves of the block (wave s takes tasks s, s + S, ...), so long lists
+// keep all their loads in flight; the S partial sums of a row are added in
+// LDS in split order (fixed: bitwise reproducible).  A block is (NT/64)/S row
+// groups of 64/LPR rows (SPLIT == false: S is 1).  The token's ids and
+// weights are fetched into lanes 0..k-1 ahead of everything else.
+template <int QT, int LPR, int XR, int NT, bool SPLIT>
 __global__ __launch_bounds__(NT) void k_down_accum(
     const float *__restrict__ act, const int32_t *__restrict__ ids, const float *__restrict__ wts, int H, int k,
     int F, int SF, const uint8_t *__restrict__ down_exps, const uint8_t *__restrict__ down_sh,
-    float *__restrict__ resid) {
+    float *__restrict__ resid, int S_arg) {
   extern __shared__ float smem[];
+  __shared__ float part[SPLIT ? NT / LPR : 1];  // [split][row of the block]
+  const int S = SPLIT ? S_arg : 1;
   constexpr int BS = QBlock<QT>::bytes;
-  constexpr int ROWS = NT / LPR;
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int rows = (NT / 64 / S) * RPW;
   const int t = blockIdx.y;
   const int nbF = F >> 5, nbS = SF >> 5;
   const int nbAll = k * nbF + nbS;
   float *xs = smem, *sx = smem + nbAll * XSTRIDE;
-  const int gi = threadIdx.x / LPR, li = threadIdx.x % LPR;
-  const int h = blockIdx.x * ROWS + gi;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ws = wave % S, rg = wave / S;  // task split, row group
+  const int gi = (threadIdx.x & 63) / LPR, li = threadIdx.x % LPR;
+  const int rb = rg * RPW + gi;  // row within the block
+  const int h = blockIdx.x * rows + rb;
   const bool live = h < H;
   const int bplF = nbF / LPR, bplS = nbS / LPR;  // LPR divides both
   const int nq = bplS + k * bplF;
-  const int nch = (nq + NCHD - 1) / NCHD;
+  const int nqw = (nq - ws + S - 1) / S;  // this wave's tasks: q = ws + S * i
+  const int nch = (nqw + NCHD - 1) / NCHD;
   const size_t mat = (size_t)H * nbF * BS;
   const uint32_t rowF = (uint32_t)h * nbF * BS;
   const uint32_t rowS = (uint32_t)h * nbS * BS;
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   auto load = [&](Raw *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCHD; i++) {
-      const int q = c * NCHD + i, j = min(pick(q), k);
+      const int q = ws + S * (c * NCHD + i), j = min(pick(q), k);
       W[i] = QBlock<QT>::load(rsrc_for(j), offset(q, j));
     }
   };
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   auto compute = [&](const Raw *W, int c) {
 #pragma unroll
     for (int i = 0; i < NCHD; i++) {
-      const int q = c * NCHD + i, j = min(pick(q), k);
+      const int q = ws + S * (c * NCHD + i), j = min(pick(q), k);
       const int ab = min(j * nbF + block(q, j), nbAll - 1);  // staged act block (shared row after routed)
       const float d = block_dot<QT>(W[i], offset(q, j), xs + ab * XSTRIDE, sx[ab]);
       const int wbits = j < k ? __builtin_amdgcn_readlane(__float_as_int(wt_v), j) : __float_as_int(1.0f);
@@ -270,7 +281,18 @@ __global__ __launch_bounds__(NT) void k_down_accum(
     }
   }
   acc = group_sum_last<LPR>(acc);
-  if (li == LPR - 1 && live) resid[(size_t)t * H + h] += acc;
+  if constexpr (!SPLIT) {
+    if (li == LPR - 1 && live) resid[(size_t)t * H + h] += acc;
+  } else {
+    if (li == LPR - 1) part[ws * rows + rb] = acc;
+    __syncthreads();
+    const int hb = blockIdx.x * rows + (int)threadIdx.x;
+    if ((int)threadIdx.x < rows && hb < H) {
+      float y = part[threadIdx.x];
+      for (int s2 = 1; s2 < S; s2++) y += part[s2 * rows + threadIdx.x];
+      resid[(size_t)t * H + hb] += y;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- launch --
@@ -291,18 +313,23 @@ static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_
              a.bias, a.sel, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim, a.lim_sh,
              a.act);
 }
-template <int QT, int LPR, int XR, int NT>
+template <int QT, int LPR, int XR, int NT, bool SPLIT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT>), grid, dim3(NT), (uint32_t)lds, st, (const float *)a.act,
-             (const int32_t *)a.ids, (const float *)a.wts, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid);
+  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT, SPLIT>), grid, dim3(NT), (uint32_t)lds, st, (const float *)a.act,
+             (const int32_t *)a.ids, (const float *)a.wts, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid,
+             a.down_split);
 }
 template <int QT, int LPR, int XR>
 static void down_launch_128(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  down_launch_nt<QT, LPR, XR, 128>(a, grid, lds, st);
+  down_launch_nt<QT, LPR, XR, 128, false>(a, grid, lds, st);
 }
 template <int QT, int LPR, int XR>
 static void down_launch_256(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  down_launch_nt<QT, LPR, XR, 256>(a, grid, lds, st);
+  down_launch_nt<QT, LPR, XR, 256, false>(a, grid, lds, st);
+}
+template <int QT, int LPR, int XR>
+static void down_launch_split(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  down_launch_nt<QT, LPR, XR, 256, true>(a, grid, lds, st);
 }
 
 #define MOE_XR_SWITCH(FN, QT, LPR)                  \
@@ -335,21 +362,34 @@ static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Down blocks of 256 threads, or of 128 where that leaves fewer than 256
+// Down launch shape.  The split S (waves per row group) is the smallest power
+// of two <= 4 that leaves each lane at most two register chunks of blocks, so
+// all of a lane's loads are in flight at once; S > 1 runs 256-thread blocks.
+// Unsplit blocks are 256 threads, or 128 where 256 would leave fewer than 256
 // blocks (so the launch covers the 256 CUs) and the act row still stages in
 // 16 float4 per thread.
+static inline int down_split(int nq) {
+  int S = 1;
+  while (S < 4 && (nq + S - 1) / S > 2 * NCHD) S <<= 1;
+  return S;
+}
 template <int QT>
-static hipError_t down_q(const DecodeArgs &a, hipStream_t st) {
+static hipError_t down_q(DecodeArgs a, hipStream_t st) {
   const int nbF = a.k > 0 ? a.F / 32 : 0, nbS = a.SF / 32;
   int lpr = nbF > 0 ? lanes_for(nbF) : 16;  // (a dense layer has only the shared row)
   if (nbS > 0 && lanes_for(nbS) < lpr) lpr = lanes_for(nbS);
   const size_t lds = (size_t)(a.k * nbF + nbS) * (XSTRIDE + 1) * sizeof(float);
   const int n = a.k * nbF * 32 + a.SF;
-  const bool wide = (size_t)((a.H + 256 / lpr - 1) / (256 / lpr)) * a.T >= 256 || n > 4 * 128 * 16;
+  const int S = down_split(a.k * (nbF / lpr) + nbS / lpr);
+  auto rows_for = [&](int nt) { return (nt / 64 / S) * (64 / lpr); };
+  const bool wide = S > 1 || (size_t)((a.H + rows_for(256) - 1) / rows_for(256)) * a.T >= 256 || n > 4 * 128 * 16;
   const int nt = wide ? 256 : 128;
-  const dim3 grid((a.H + nt / lpr - 1) / (nt / lpr), a.T);
+  const dim3 grid((a.H + rows_for(nt) - 1) / rows_for(nt), a.T);
   const int xr = xr_for(n, nt);
-  if (wide) {
+  a.down_split = S;
+  if (S > 1) {
+    MOE_LPR_SWITCH(down_launch_split, QT)
+  } else if (wide) {
     MOE_LPR_SWITCH(down_launch_256, QT)
   } else {
     MOE_LPR_SWITCH(down_launch_128, QT)

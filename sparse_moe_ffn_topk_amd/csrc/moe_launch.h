@@ -44,6 +44,7 @@ struct DecodeArgs {
   float *act;    // per token: [k][F] routed rows, then [SF] shared
   float *resid;  // [T][H] in/out
   float lim, lim_sh;  // SwiGLU clamp of the routed and of the shared experts (0: none)
+  int down_split = 1;  // waves sharing one row group's task list in the down kernel (set by its launcher)
 };
 
 // gate||up + SwiGLU, then down + weighted per-token accumulate.
