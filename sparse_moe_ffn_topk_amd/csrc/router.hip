@@ -8,10 +8,11 @@
 // page: router comment and TOPK_SIG_BODY; ling_moe_ssd.js page: routeLing).
 //
 // MI355X design:
-//  * logits: each wave owns one router row (T <= 8) and streams it with
-//    16-byte buffer loads, all issued before the first product; products and
-//    sums in f64 (full-rate on gfx950), one rounding to f32 at the end.  Larger
-//    T runs on the f64 matrix cores (v_mfma_f64_16x16x4f64).
+//  * logits: one block owns one router row (T <= 8), its waves splitting the
+//    tokens, and streams it with 16-byte buffer loads, all issued before the
+//    first product; products and sums in f64 (full-rate on gfx950), one
+//    rounding to f32 at the end.  Larger T runs on the f64 matrix cores
+//    (v_mfma_f64_16x16x4f64).
 //  * selection: one 256-thread block per token ranks the experts (a score's
 //    rank is the number of experts that beat it), which gives the k argmax
 //    rounds' picks at once.
@@ -23,11 +24,13 @@ namespace moe {
 
 // ---------------------------------------------------------------- logits --
 
-// T <= 8 tokens: one 64-thread block per router row e; logits[t][e].  A lane
-// takes NC 16-byte chunks of the row per pass and, per token, the matching NC
-// chunks of x; every load of a pass is issued before the first product (buffer
-// loads with an out-of-range offset past the row end read zeros, so there are
-// no branches between them).  Products and sums in f64, one f32 rounding.
+// T <= 8 tokens: one block of NW = min(T, 4) waves per router row e;
+// logits[t][e].  Wave w takes tokens w, w + NW (TPW of them), so a wave's
+// serial path is at most two tokens long.  A lane takes NC 16-byte chunks of
+// the row per pass and, per token, the matching NC chunks of x; every load of
+// a pass is issued before the first product (buffer loads with an
+// out-of-range offset past the row end read zeros, so there are no branches
+// between them).  Products and sums in f64, one f32 rounding.
 constexpr uint32_t ROUTER_OOB = 0x7ffffff0u;
 //
 // With gnorm != NULL (one pass: H <= 256 * NC) x is the residual stream and
@@ -35,27 +38,28 @@ constexpr uint32_t ROUTER_OOB = 0x7ffffff0u;
 // row, so the sum of squares (f64) reduces across the wave, and the lanes form
 // xn = f32(x * s * g), s = 1/sqrt(ss/H + eps), before the dot; block 0 writes
 // xn for the FFN kernels.  Every block computes the same xn the same way.
-template <int TT, int NC>
-__global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
-                                                    int H, int E, int T, float *__restrict__ logits,
-                                                    const float *__restrict__ gnorm, float eps,
-                                                    float *__restrict__ xn_out) {
-  const int e = blockIdx.x, lane = threadIdx.x;
+template <int TPW, int NC>
+__global__ __launch_bounds__(256) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
+                                                     int H, int E, int T, float *__restrict__ logits,
+                                                     const float *__restrict__ gnorm, float eps,
+                                                     float *__restrict__ xn_out) {
+  const int e = blockIdx.x, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), NW = blockDim.x >> 6;
   const uint32_t rowbytes = (uint32_t)H * 4u;
   const rsrc_t rw = make_rsrc(W + (size_t)e * H, rowbytes);
   const rsrc_t rx = make_rsrc(x, (uint32_t)T * rowbytes);
   const rsrc_t rg = make_rsrc(gnorm, rowbytes);
-  double acc[TT][2];
+  double acc[TPW][2];
 #pragma unroll
-  for (int t = 0; t < TT; t++) acc[t][0] = acc[t][1] = 0.0;
+  for (int i = 0; i < TPW; i++) acc[i][0] = acc[i][1] = 0.0;
   for (uint32_t c0 = 0; c0 < rowbytes; c0 += 1024u * NC) {
     uint32_t off[NC];
-    u32x4 w[NC];
+    u32x4 wr[NC];
 #pragma unroll
     for (int i = 0; i < NC; i++) {
       const uint32_t o = c0 + 16u * (uint32_t)(lane + 64 * i);
       off[i] = o < rowbytes ? o : ROUTER_OOB;
-      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off[i], 0, 0);
+      wr[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off[i], 0, 0);
     }
     u32x4 gv[NC];
     if (gnorm) {
@@ -63,7 +67,8 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
       for (int i = 0; i < NC; i++) gv[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, (int)off[i], 0, 0);
     }
 #pragma unroll
-    for (int t = 0; t < TT; t++) {
+    for (int ti = 0; ti < TPW; ti++) {
+      const int t = w + NW * ti;
       if (t < T) {
         u32x4 v[NC];
 #pragma unroll
@@ -92,18 +97,19 @@ __global__ __launch_bounds__(64) void k_router_rows(const float *__restrict__ W,
         }
 #pragma unroll
         for (int i = 0; i < NC; i++) {
-          acc[t][0] = __builtin_fma((double)__uint_as_float(w[i][0]), (double)__uint_as_float(v[i][0]), acc[t][0]);
-          acc[t][1] = __builtin_fma((double)__uint_as_float(w[i][1]), (double)__uint_as_float(v[i][1]), acc[t][1]);
-          acc[t][0] = __builtin_fma((double)__uint_as_float(w[i][2]), (double)__uint_as_float(v[i][2]), acc[t][0]);
-          acc[t][1] = __builtin_fma((double)__uint_as_float(w[i][3]), (double)__uint_as_float(v[i][3]), acc[t][1]);
+          acc[ti][0] = __builtin_fma((double)__uint_as_float(wr[i][0]), (double)__uint_as_float(v[i][0]), acc[ti][0]);
+          acc[ti][1] = __builtin_fma((double)__uint_as_float(wr[i][1]), (double)__uint_as_float(v[i][1]), acc[ti][1]);
+          acc[ti][0] = __builtin_fma((double)__uint_as_float(wr[i][2]), (double)__uint_as_float(v[i][2]), acc[ti][0]);
+          acc[ti][1] = __builtin_fma((double)__uint_as_float(wr[i][3]), (double)__uint_as_float(v[i][3]), acc[ti][1]);
         }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < TT; t++) {
+  for (int ti = 0; ti < TPW; ti++) {
+    const int t = w + NW * ti;
     if (t < T) {
-      const double s = wave_sum_d(acc[t][0] + acc[t][1]);
+      const double s = wave_sum_d(acc[ti][0] + acc[ti][1]);
       if (lane == 0) logits[(size_t)t * E + e] = (float)s;
     }
   }
@@ -230,28 +236,24 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
     // Chunks per lane and pass: the whole row in one pass up to H = 4096.
     const int n16 = (H + 3) / 4;
     const int nc = (n16 + 63) / 64;
-    const dim3 grid(E);
-#define MOE_ROUTER_ROWS(TT)                                                                              \
+    const dim3 grid(E), block(64 * (T < 4 ? T : 4));
+#define MOE_ROUTER_ROWS(TPW)                                                                             \
   do {                                                                                                   \
     if (nc <= 2)                                                                                         \
-      MOE_LAUNCH(1, (k_router_rows<TT, 2>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
+      MOE_LAUNCH(1, (k_router_rows<TPW, 2>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn); \
     else if (nc <= 4)                                                                                    \
-      MOE_LAUNCH(1, (k_router_rows<TT, 4>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
+      MOE_LAUNCH(1, (k_router_rows<TPW, 4>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn); \
     else if (nc <= 8)                                                                                    \
-      MOE_LAUNCH(1, (k_router_rows<TT, 8>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
+      MOE_LAUNCH(1, (k_router_rows<TPW, 8>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn); \
     else if (nc <= 12)                                                                                   \
-      MOE_LAUNCH(1, (k_router_rows<TT, 12>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
+      MOE_LAUNCH(1, (k_router_rows<TPW, 12>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
     else                                                                                                 \
-      MOE_LAUNCH(1, (k_router_rows<TT, 16>), grid, dim3(64), 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
+      MOE_LAUNCH(1, (k_router_rows<TPW, 16>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
   } while (0)
-    if (T == 1)
+    if (T <= 4)
       MOE_ROUTER_ROWS(1);
-    else if (T <= 2)
-      MOE_ROUTER_ROWS(2);
-    else if (T <= 4)
-      MOE_ROUTER_ROWS(4);
     else
-      MOE_ROUTER_ROWS(8);
+      MOE_ROUTER_ROWS(2);
 #undef MOE_ROUTER_ROWS
   } else {
     const dim3 grid((E + 15) / 16, (T + 63) / 64);
