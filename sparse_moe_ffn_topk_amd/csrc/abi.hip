@@ -28,6 +28,10 @@ int fail(int code, const char *fmt, ...) {
 }
 
 constexpr int kDecodeMaxT = 8;
+// Up to this many tokens every gate||up block routes its token in its prologue
+// (hidden behind the shared expert's loads); beyond it that work would repeat
+// in every block of every token, so a select kernel routes each token once.
+constexpr int kRouteInGateupMaxT = 1;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -409,22 +413,25 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   const bool decode = T <= kDecodeMaxT && decode_fits(*cfg);
   if (decode && !dense && w->ffn_norm && moe::router_fuses_norm(cfg->hidden, T)) {
     // decode with a norm: the router kernel normalises x and writes xn; the
-    // gate||up kernel routes in its prologue
+    // gate||up kernel routes a single token in its prologue, more tokens are
+    // routed once each by the select kernel
     float *lg = (float *)((char *)workspace + L.logits);
     float *xn = (float *)((char *)workspace + L.xn);
     if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st,
                                                  w->ffn_norm, cfg->norm_eps, xn),
                        "router logits + rmsnorm")))
       return rc;
-    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
+    if (T <= kRouteInGateupMaxT) return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
+    if ((rc = router_topk_impl(*cfg, w, xn, T, lg, ids, wts, workspace, st))) return rc;
+    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, nullptr, resid, workspace, st);
   }
   if ((rc = prologue_norm(*cfg, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
   if (dense) {  // no router: only the FFN held in the shared-expert tensors
     if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
     return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
   }
-  if (T <= kDecodeMaxT && decode_fits(*cfg)) {
-    // decode: router logits, then the gate||up kernel routes in its prologue
+  if (T <= kDecodeMaxT && decode_fits(*cfg) && T <= kRouteInGateupMaxT) {
+    // decode of one token: router logits, then the gate||up kernel routes in its prologue
     float *lg = (float *)((char *)workspace + L.logits);
     if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st),
                        "router logits")))
