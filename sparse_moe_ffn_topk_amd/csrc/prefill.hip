@@ -103,16 +103,23 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
 
 // ------------------------------------------------------------- grouped GEMM --
 
-// 8 nibbles of 8 bytes (low halves, or high halves if hi) as exact f16 q,
-// in the order k = 0,2,1,3,4,6,5,7 of the bytes (two mask-ors per dword).
-__device__ __forceinline__ half8 nibbles_f16(u32x2 nb, bool hi) {
-  uint32_t w0 = nb.x, w1 = nb.y;
-  if (hi) {
-    w0 >>= 4;
-    w1 >>= 4;
-  }
-  const uint32_t a = (w0 & 0x000F000Fu) | 0x64006400u, b = ((w0 >> 8) & 0x000F000Fu) | 0x64006400u;
-  const uint32_t c = (w1 & 0x000F000Fu) | 0x64006400u, d = ((w1 >> 8) & 0x000F000Fu) | 0x64006400u;
+// (w & mask) | bits in one v_and_or_b32.  A VOP3 form takes no literal and
+// at most one scalar operand here, so the mask sits in a scalar register and
+// the bits in a vector register (set once); the compiler's own selection
+// emits a separate and + or instead.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(bits));
+  return r;
+}
+
+// 8 nibbles of 8 bytes (the low halves, or the high halves with sh = 4) as
+// exact f16 q, in the order k = 0,2,1,3,4,6,5,7 of the bytes (one mask-or per
+// f16 pair: 0x6400 | q is the f16 1024 + q).
+__device__ __forceinline__ half8 nibbles_f16(u32x2 nb, uint32_t sh) {
+  const uint32_t w0 = nb.x >> sh, w1 = nb.y >> sh;
+  const uint32_t a = and_or(w0, 0x000F000Fu, 0x64006400u), b = and_or(w0 >> 8, 0x000F000Fu, 0x64006400u);
+  const uint32_t c = and_or(w1, 0x000F000Fu, 0x64006400u), d = and_or(w1 >> 8, 0x000F000Fu, 0x64006400u);
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
   const u32x4v v = {a, b, c, d};
   // (1024 + q) - 1024 = q, exact in f16
@@ -126,8 +133,8 @@ __device__ __forceinline__ int kperm(int j) { return (j & 4) | ((j & 1) << 1) | 
 // order 0,2,1,3,4,6,5,7 (two mask-ors per dword: f16 1024 + b, minus 1024).
 __device__ __forceinline__ half8 bytes_f16(u32x2 nb) {
   const uint32_t w0 = nb.x, w1 = nb.y;
-  const uint32_t a = (w0 & 0x00FF00FFu) | 0x64006400u, b = ((w0 >> 8) & 0x00FF00FFu) | 0x64006400u;
-  const uint32_t c = (w1 & 0x00FF00FFu) | 0x64006400u, d = ((w1 >> 8) & 0x00FF00FFu) | 0x64006400u;
+  const uint32_t a = and_or(w0, 0x00FF00FFu, 0x64006400u), b = and_or(w0 >> 8, 0x00FF00FFu, 0x64006400u);
+  const uint32_t c = and_or(w1, 0x00FF00FFu, 0x64006400u), d = and_or(w1 >> 8, 0x00FF00FFu, 0x64006400u);
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
   const u32x4v v = {a, b, c, d};
   return __builtin_bit_cast(half8, v) - (half8)(_Float16)1024.0f;
@@ -165,14 +172,15 @@ struct AStage {
   float v[8];
 };
 // (buffer loads: past the row, or for no row, they read zeros -- no branches,
-// so the loads stay in order behind the weight loads)
-__device__ __forceinline__ void a_load(AStage &st, const float *arows, int astride, int K, int row, int kc) {
+// so the loads stay in order behind the weight loads).  r covers all the
+// input rows (one resource for the wave: the rows differ per lane).
+__device__ __forceinline__ void a_load(AStage &st, rsrc_t r, int K, int row, int kc) {
   const int seg = threadIdx.x & 15;
   const uint32_t kb = (uint32_t)(kc * 32 + seg * 8);
-  const rsrc_t r = make_rsrc(arows + (size_t)(row >= 0 ? row : 0) * astride, (uint32_t)K * 4u);
+  const uint32_t rowoff = (uint32_t)(row >= 0 ? row : 0) * (uint32_t)K * 4u;
 #pragma unroll
   for (int i = 0; i < 8; i += 4) {
-    const uint32_t off = (row >= 0 && kb + i < (uint32_t)K) ? (kb + i) * 4u : 0x7ffffff0u;
+    const uint32_t off = (row >= 0 && kb + i < (uint32_t)K) ? rowoff + (kb + i) * 4u : 0x7ffffff0u;
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     const uint32_t a0 = v.x, a1 = v.y, a2 = v.z, a3 = v.w;
     st.v[i] = __uint_as_float(a0);
@@ -218,7 +226,7 @@ template <> struct QStaged<MOE_Q4_1> {
     u32x2 nb;
     nb.x = w[5 * jb + 1 + 2 * half];
     nb.y = w[5 * jb + 2 + 2 * half];
-    return nibbles_f16(nb, kq >= 2);
+    return nibbles_f16(nb, (uint32_t)(kq & 2) << 1);
   }
 };
 template <> struct QStaged<MOE_Q4_0> {
@@ -237,7 +245,7 @@ template <> struct QStaged<MOE_Q4_0> {
       nb.x = w0;
       nb.y = w1;
     }
-    return nibbles_f16(nb, kq >= 2);
+    return nibbles_f16(nb, (uint32_t)(kq & 2) << 1);
   }
 };
 template <> struct QStaged<MOE_Q8_0> {
@@ -282,36 +290,38 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bx = blockIdx.x;
   const bool shared = bx >= a.max_routed_tiles;
-  int e = 0, ntok, K, R;
+  // tile parameters first, all wave-uniform and with no divergent code in
+  // between, so the weight buffer resources stay in scalar registers
+  int e = 0, first = 0, ntok, K, R;
   const uint8_t *m0p, *m1p;
   if (!shared) {
-    if (bx >= *a.ntiles) return;
-    e = a.tiles[2 * bx];
-    const int first = a.offsets[e] + a.tiles[2 * bx + 1];
-    ntok = min(16, a.offsets[e + 1] - first);
+    if (bx >= __builtin_amdgcn_readfirstlane(*a.ntiles)) return;
+    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * bx]);
+    first = __builtin_amdgcn_readfirstlane(a.offsets[e] + a.tiles[2 * bx + 1]);
+    ntok = min(16, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - first);
     K = MODE == GG_GATEUP ? a.H : a.F;
     R = MODE == GG_GATEUP ? a.F : a.H;
     const size_t mat = (size_t)R * (K / 32) * BS;
     m0p = a.w0 + (size_t)e * mat;
     m1p = MODE == GG_GATEUP ? a.w1 + (size_t)e * mat : nullptr;
-    if (tid < 16) {
-      const int q = first + tid;
-      const bool ok = tid < ntok;
-      rowid[tid] = ok ? (MODE == GG_GATEUP ? a.perm[q] / a.k : q) : -1;
-      outid[tid] = ok ? q : -1;
-      outw[tid] = ok && MODE == GG_DOWN ? a.wts[a.perm[q]] : 1.f;
-    }
   } else {
-    const int t0 = 16 * (bx - a.max_routed_tiles);
-    ntok = min(16, a.T - t0);
+    first = 16 * (bx - a.max_routed_tiles);  // the tile's first token
+    ntok = min(16, a.T - first);
     K = MODE == GG_GATEUP ? a.H : a.SF;
     R = MODE == GG_GATEUP ? a.SF : a.H;
     m0p = a.s0;
     m1p = a.s1;
-    if (tid < 16) {
-      const bool ok = tid < ntok;
-      rowid[tid] = ok ? t0 + tid : -1;
-      outid[tid] = ok ? t0 + tid : -1;
+  }
+  if (tid < 16) {
+    const bool ok = tid < ntok;
+    if (!shared) {
+      const int q = first + tid;
+      rowid[tid] = ok ? (MODE == GG_GATEUP ? a.perm[q] / a.k : q) : -1;
+      outid[tid] = ok ? q : -1;
+      outw[tid] = ok && MODE == GG_DOWN ? a.wts[a.perm[q]] : 1.f;
+    } else {
+      rowid[tid] = ok ? first + tid : -1;
+      outid[tid] = ok ? first + tid : -1;
       outw[tid] = 1.f;
     }
   }
@@ -323,7 +333,8 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   const rsrc_t rw0 = make_rsrc(m0p, mbytes);
   const rsrc_t rw1 = NM == 2 ? make_rsrc(m1p, mbytes) : rw0;
   const float *arows = MODE == GG_GATEUP ? a.x : (shared ? a.act_sh : a.act);
-  const int astride = K;
+  const int nrows = (MODE == GG_GATEUP || shared) ? a.T : a.T * a.k;  // rows of arows, K floats each
+  const rsrc_t ra = make_rsrc(arows, (uint32_t)nrows * (uint32_t)K * 4u);
 
   // weight pieces of this thread: p = tid + 256 i (i < PR) -> row p / PR, 16 bytes p % PR
   u32x4 breg[NM][PR];
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   const int arow = rowid[tid >> 4];
   AStage ast;
   b_issue(0);
-  a_load(ast, arows, astride, K, arow, 0);
+  a_load(ast, ra, K, arow, 0);
 
   for (int kc = 0; kc < nbK; kc += KB) {
     b_store();
@@ -377,7 +388,7 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
     __syncthreads();
     if (kc + KB < nbK) {
       b_issue(kc + KB);
-      a_load(ast, arows, astride, K, arow, kc + KB);
+      a_load(ast, ra, K, arow, kc + KB);
     }
 #pragma unroll
     for (int jb = 0; jb < KB; jb++) {
