@@ -301,7 +301,8 @@ def main():
         nk = min(args.steps, 60)
         others = ((("router", moe.KERNEL_ROUTER), ("select", moe.KERNEL_SELECT), ("sort", moe.KERNEL_SORT),
                    ("group_down", moe.KERNEL_GROUP_DOWN), ("combine", moe.KERNEL_COMBINE)) if grouped else
-                  (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN)))
+                  (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN))
+                  + ((("prelude", moe.KERNEL_PRELUDE),) if T > 1 else ()))
         for name, kid in ((dominant[1], dominant[0]),) + others:
             with moe.KernelTimer(kid, nk * L) as kt:
                 for i in range(nk):

@@ -28,10 +28,6 @@ int fail(int code, const char *fmt, ...) {
 }
 
 constexpr int kDecodeMaxT = 8;
-// Up to this many tokens every gate||up block routes its token in its prologue
-// (hidden behind the shared expert's loads); beyond it that work would repeat
-// in every block of every token, so a select kernel routes each token once.
-constexpr int kRouteInGateupMaxT = 1;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -169,7 +165,8 @@ int router_topk_impl(const moe_config &c, const moe_layer_weights *w, const floa
 }
 
 // Expert FFNs.  With logits != NULL (decode path of moe_layer_step) the
-// gate||up kernel routes each token itself and writes ids / wts.
+// tokens are routed on the way (one token: in the gate||up kernel's prologue;
+// more: in the decode prelude), which writes ids / wts.
 int expert_ffn_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, int32_t *ids,
                     float *wts, const float *logits, float *resid, void *ws, hipStream_t st) {
   const Layout L = layout(c, T);
@@ -288,7 +285,7 @@ int moe_kernel_timer_end(int32_t *count, double *total_ms);
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
   g_err.clear();
   if (g_timer.kernel) moe_kernel_timer_end(nullptr, nullptr);
-  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_RMSNORM || capacity < 1 || capacity > (1 << 20))
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_PRELUDE || capacity < 1 || capacity > (1 << 20))
     return fail(MOE_EINVAL, "kernel timer: bad kernel %d or capacity %d", kernel, capacity);
   g_timer.start = new hipEvent_t[capacity];
   g_timer.stop = new hipEvent_t[capacity];
@@ -414,24 +411,23 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if (decode && !dense && w->ffn_norm && moe::router_fuses_norm(cfg->hidden, T)) {
     // decode with a norm: the router kernel normalises x and writes xn; the
     // gate||up kernel routes a single token in its prologue, more tokens are
-    // routed once each by the select kernel
+    // routed once each in the decode prelude
     float *lg = (float *)((char *)workspace + L.logits);
     float *xn = (float *)((char *)workspace + L.xn);
     if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st,
                                                  w->ffn_norm, cfg->norm_eps, xn),
                        "router logits + rmsnorm")))
       return rc;
-    if (T <= kRouteInGateupMaxT) return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
-    if ((rc = router_topk_impl(*cfg, w, xn, T, lg, ids, wts, workspace, st))) return rc;
-    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, nullptr, resid, workspace, st);
+    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
   }
   if ((rc = prologue_norm(*cfg, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
   if (dense) {  // no router: only the FFN held in the shared-expert tensors
     if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
     return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
   }
-  if (T <= kDecodeMaxT && decode_fits(*cfg) && T <= kRouteInGateupMaxT) {
-    // decode of one token: router logits, then the gate||up kernel routes in its prologue
+  if (T <= kDecodeMaxT && decode_fits(*cfg)) {
+    // decode: router logits, then the gate||up kernel routes one token in its
+    // prologue (more tokens: the decode prelude routes each once)
     float *lg = (float *)((char *)workspace + L.logits);
     if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st),
                        "router logits")))

@@ -95,7 +95,7 @@ template <int QT, int LPR, int XR>
 __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
     const float *__restrict__ x, int32_t *__restrict__ ids, float *__restrict__ wts,
     const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int H, int k, int F, int SF,
-    const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
+    int sf_tasks, const uint8_t *__restrict__ gate_exps, const uint8_t *__restrict__ up_exps,
     const uint8_t *__restrict__ gate_sh, const uint8_t *__restrict__ up_sh, float lim, float lim_sh,
     float *__restrict__ act) {
   extern __shared__ float smem[];
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   const int t = blockIdx.y, NB = gridDim.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, gi = lane / LPR, li = lane % LPR;
-  const int nsw = (SF + RW - 1) / RW, nfw = (F + RW - 1) / RW;
+  const int nsw = (sf_tasks + RW - 1) / RW, nfw = (F + RW - 1) / RW;  // (sf_tasks: SF, or 0 when done elsewhere)
   const int u = wave * NB + blockIdx.x;
   const bool is_sh = u < nsw;
   const bool wlive = u < nsw + k * nfw;
@@ -189,6 +189,124 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   g = group_sum_last<LPR>(g);
   v = group_sum_last<LPR>(v);
   if (li == LPR - 1 && live) out[row] = silu_mul(g, v, is_sh ? lim_sh : lim);
+}
+
+// Sum of a float over the whole wave (row sums, then the four rows in a fixed
+// order); the result is uniform.
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v = group_sum_last<16>(v);
+  auto rl = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+  return (rl(15) + rl(31)) + (rl(47) + rl(63));
+}
+
+// Prelude of a decode step of several tokens, in one launch.  Blocks
+// [0, nsel) route token blockIdx.x (select_block: ids and weights).  The other
+// blocks compute the shared expert's gate||up rows for groups of up to TG
+// tokens, so its weights stream once per group rather than once per token:
+// shared block s takes rows 4 (s % nrg) + wave (nrg = SF/4 rounded up) for the
+// tokens of group s / nrg.  A wave's 64 lanes split the row's blocks (lane i:
+// blocks i and i + 64, so H <= 4096); each block is unpacked once and dotted
+// with every token's input staged in LDS.  Writes act[t][k*F + f].
+template <int QT, int XR, int TG>
+__global__ __launch_bounds__(256) void k_decode_prelude(
+    const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int nsel,
+    int32_t *__restrict__ ids, float *__restrict__ wts, const float *__restrict__ x, int T, int H, int k, int F,
+    int SF, const uint8_t *__restrict__ gate_sh, const uint8_t *__restrict__ up_sh, float lim_sh,
+    float *__restrict__ act) {
+  __shared__ SelShared sh;
+  extern __shared__ float smem[];
+  if ((int)blockIdx.x < nsel) {
+    const int t = blockIdx.x;
+    select_block(logits + (size_t)t * P.E, bias, P, sh, wts + (size_t)t * P.k);
+    if ((int)threadIdx.x < P.k) ids[(size_t)t * P.k + threadIdx.x] = sh.pick[threadIdx.x];
+    return;
+  }
+  constexpr int BS = QBlock<QT>::bytes;
+  constexpr int NBL = 2;  // blocks per lane
+  const int nbH = H >> 5;
+  const int nrg = (SF + 3) >> 2;
+  const int s = (int)blockIdx.x - nsel;
+  const int t0 = (s / nrg) * TG, nt = min(TG, T - t0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = (s % nrg) * 4 + wave;
+  const bool live = row < SF;
+  const uint32_t rowbytes = (uint32_t)nbH * BS;
+
+  // the group's inputs (tokens past T read as zeros), then the weights, then
+  // the LDS stores: the weight loads are in flight while the inputs land
+  Stage<XR> xst[TG];
+#pragma unroll
+  for (int tt = 0; tt < TG; tt++)
+    stage_load<256, XR>(xst[tt], x + (size_t)min(t0 + tt, T - 1) * H, tt < nt ? H : 0);
+  typedef typename QBlock<QT>::Raw Raw;
+  Raw gw[NBL], uw[NBL];
+  const rsrc_t rg = make_rsrc(gate_sh, (uint32_t)SF * rowbytes), ru = make_rsrc(up_sh, (uint32_t)SF * rowbytes);
+  auto offset = [&](int i) {
+    const int b = lane + 64 * i;
+    return (live && b < nbH) ? (uint32_t)row * rowbytes + (uint32_t)b * BS : OOB;
+  };
+#pragma unroll
+  for (int i = 0; i < NBL; i++) {
+    gw[i] = QBlock<QT>::load(rg, offset(i));
+    uw[i] = QBlock<QT>::load(ru, offset(i));
+  }
+  float *xs = smem, *sx = smem + TG * nbH * XSTRIDE;  // token tt: blocks at tt*nbH*XSTRIDE, sums at tt*nbH
+#pragma unroll
+  for (int tt = 0; tt < TG; tt++) stage_store<256, XR>(xst[tt], H, xs + tt * nbH * XSTRIDE, sx + tt * nbH);
+  __syncthreads();
+
+  float ga[TG], ua[TG];
+#pragma unroll
+  for (int tt = 0; tt < TG; tt++) ga[tt] = ua[tt] = 0.f;
+  // 2-byte-aligned blocks (Q4_0, Q8_0) are shifted once so that every block
+  // starts at byte 0 of its first dword (offset 0 below): the accessors then
+  // select nothing per lane
+  auto realign = [&](Raw &r, uint32_t off) {
+    if constexpr (QT != MOE_Q4_1) {
+      constexpr int NW = sizeof(Raw) / 4;
+      const bool odd = (off & 2u) != 0u;
+#pragma unroll
+      for (int j = 0; j < NW; j++) {
+        const uint32_t nx = j + 1 < NW ? r.w[j + 1] : 0u;
+        r.w[j] = odd ? __builtin_amdgcn_alignbyte(nx, r.w[j], 2) : r.w[j];
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NBL; i++) {
+    realign(gw[i], offset(i));
+    realign(uw[i], offset(i));
+  }
+#pragma unroll
+  for (int i = 0; i < NBL; i++) {
+    if (64 * i >= nbH) break;  // (uniform: no lane has a block i)
+    const int b = min(lane + 64 * i, nbH - 1);  // (blocks past the row are zeros: they add 0)
+    float q[32], d, m;
+    // (a scheduling barrier per token pair keeps the pair's 64 input reads next
+    // to its FMAs instead of all tokens' inputs live at once)
+    block_unpack<QT>(gw[i], 0u, q, d, m);
+#pragma unroll
+    for (int tt = 0; tt < TG; tt++) {
+      ga[tt] += unpacked_dot(q, d, m, xs + (tt * nbH + b) * XSTRIDE, sx[tt * nbH + b]);
+      if (tt & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    block_unpack<QT>(uw[i], 0u, q, d, m);
+#pragma unroll
+    for (int tt = 0; tt < TG; tt++) {
+      ua[tt] += unpacked_dot(q, d, m, xs + (tt * nbH + b) * XSTRIDE, sx[tt * nbH + b]);
+      if (tt & 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float gv = 0.f, uv = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < TG; tt++) {
+    const float g = wave_sum_f(ga[tt]), u = wave_sum_f(ua[tt]);
+    if (lane == tt) {
+      gv = g;
+      uv = u;
+    }
+  }
+  if (live && lane < nt) act[(size_t)(t0 + lane) * ((size_t)k * F + SF) + (size_t)k * F + row] = silu_mul(gv, uv, lim_sh);
 }
 
 // grid.x: tiles of outputs h; grid.y: token t.  Each lane of a row's lane
@@ -310,7 +428,8 @@ static inline int xr_for(int n, int nt) {  // float4s per thread to stage n floa
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
-             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim, a.lim_sh,
+             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.sf_tasks, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim,
+             a.lim_sh,
              a.act);
 }
 template <int QT, int LPR, int XR, int NT, bool SPLIT>
@@ -349,12 +468,53 @@ static void down_launch_split(const DecodeArgs &a, dim3 grid, size_t lds, hipStr
     default: MOE_XR_SWITCH(FN, QT, 16) break;          \
   }
 
+// Multi-token prelude.  Tokens per shared-expert group: 4, or 2 when T <= 2
+// or when 4 tokens' inputs do not fit the LDS left beside the select state
+// (0: the shared rows stay in the gate||up kernel, per token).
+int prelude_token_group(int T, int H);
+template <int QT, int XR, int TG>
+static void prelude_launch(const DecodeArgs &a, int nsel, int nsh, size_t lds, hipStream_t st) {
+  MOE_LAUNCH(10, (k_decode_prelude<QT, XR, TG>), dim3(nsel + nsh), dim3(256), (uint32_t)lds, st, a.logits, a.bias,
+             a.sel, nsel, a.ids, a.wts, a.x, a.T, a.H, a.k, a.F, a.SF, a.gate_sh, a.up_sh, a.lim_sh, a.act);
+}
+// With several tokens: route each token once (when logits are given) and run
+// the shared expert's gate||up for all tokens, in one launch; a is updated so
+// the gate||up kernel then reads the ids and skips the shared rows.
+template <int QT>
+static hipError_t prelude_q(DecodeArgs &a, hipStream_t st) {
+  a.sf_tasks = a.SF;
+  if (a.T < 2) return hipSuccess;
+  const int nsel = a.logits ? a.T : 0;
+  const int tg = a.SF > 0 ? prelude_token_group(a.T, a.H) : 0;
+  if (nsel == 0 && tg == 0) return hipSuccess;
+  const int nsh = tg ? ((a.SF + 3) / 4) * ((a.T + tg - 1) / tg) : 0;
+  const size_t lds = tg ? (size_t)tg * (a.H / 32) * (XSTRIDE + 1) * sizeof(float) : 0;
+  const int xr = xr_for(a.H, 256);
+#define MOE_PRELUDE_XR(TG)                                             \
+  switch (xr) {                                                        \
+    case 1: prelude_launch<QT, 1, TG>(a, nsel, nsh, lds, st); break;   \
+    case 2: prelude_launch<QT, 2, TG>(a, nsel, nsh, lds, st); break;   \
+    default: prelude_launch<QT, 4, TG>(a, nsel, nsh, lds, st); break;  \
+  }
+  if (tg >= 4) {
+    MOE_PRELUDE_XR(4)
+  } else {
+    MOE_PRELUDE_XR(2)
+  }
+#undef MOE_PRELUDE_XR
+  const hipError_t e = hipGetLastError();
+  if (nsel) a.logits = nullptr;
+  if (tg) a.sf_tasks = 0;
+  return e;
+}
+
 template <int QT>
 static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
   const int nbH = a.H / 32;
   const int lpr = lanes_for(nbH);
   const int rw = 64 / lpr;  // rows per wave task
-  const int tasks = (a.SF + rw - 1) / rw + a.k * ((a.F + rw - 1) / rw);
+  const int tasks = (a.sf_tasks + rw - 1) / rw + a.k * ((a.F + rw - 1) / rw);
+  if (tasks == 0) return hipSuccess;  // (a dense layer whose rows the prelude computed)
   const dim3 grid((tasks + 3) / 4, a.T);
   const size_t lds = (size_t)nbH * (XSTRIDE + 1) * sizeof(float);
   const int xr = xr_for(a.H, 256);

@@ -3,8 +3,11 @@
 
 namespace moe {
 
-hipError_t decode_ffn_q80(const DecodeArgs &a, hipStream_t st) {
-  hipError_t e = gateup_q<MOE_Q8_0>(a, st);
+hipError_t decode_ffn_q80(const DecodeArgs &a0, hipStream_t st) {
+  DecodeArgs a = a0;
+  hipError_t e = prelude_q<MOE_Q8_0>(a, st);
+  if (e != hipSuccess) return e;
+  e = gateup_q<MOE_Q8_0>(a, st);
   if (e != hipSuccess) return e;
   e = down_q<MOE_Q8_0>(a, st);
   return e;

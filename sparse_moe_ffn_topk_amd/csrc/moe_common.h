@@ -178,6 +178,56 @@ __device__ __forceinline__ float block_dot(const typename QBlock<QT>::Raw &b, ui
   }
 }
 
+// A block's 32 quants as floats (Q4: q, in element order; Q8_0: q + 128) and
+// its scale and offset, so that value_i = d * q[i] + m.  For dots of one block
+// with several inputs: the conversion is done once.
+template <int QT>
+__device__ __forceinline__ void block_unpack(const typename QBlock<QT>::Raw &b, uint32_t off, float (&q)[32],
+                                             float &d, float &m) {
+  QBlock<QT>::scales(b, off, d, m);
+  if constexpr (QT == MOE_Q8_0) {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t w = QBlock<QT>::word(b, off, k);
+      asm("" : "+v"(w));  // one v_cvt_f32_ubyteN per byte (see nib_word_dot)
+      q[4 * k] = (float)(w & 0xff);
+      q[4 * k + 1] = (float)((w >> 8) & 0xff);
+      q[4 * k + 2] = (float)((w >> 16) & 0xff);
+      q[4 * k + 3] = (float)(w >> 24);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t w = QBlock<QT>::nib(b, off, k);
+      uint32_t l = w & 0x0F0F0F0Fu, h = (w >> 4) & 0x0F0F0F0Fu;
+      asm("" : "+v"(l));
+      asm("" : "+v"(h));
+      q[4 * k] = (float)(l & 0xff);
+      q[4 * k + 1] = (float)((l >> 8) & 0xff);
+      q[4 * k + 2] = (float)((l >> 16) & 0xff);
+      q[4 * k + 3] = (float)(l >> 24);
+      q[16 + 4 * k] = (float)(h & 0xff);
+      q[16 + 4 * k + 1] = (float)((h >> 8) & 0xff);
+      q[16 + 4 * k + 2] = (float)((h >> 16) & 0xff);
+      q[16 + 4 * k + 3] = (float)(h >> 24);
+    }
+  }
+}
+
+// d * sum_i q[i] x[i] + m * sx for an unpacked block and its 32 inputs xb (LDS).
+__device__ __forceinline__ float unpacked_dot(const float (&q)[32], float d, float m, const float *xb, float sx) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const float4 xv = *reinterpret_cast<const float4 *>(xb + 4 * k);
+    float &acc = (k & 1) ? a1 : a0;
+    acc = __builtin_fmaf(q[4 * k], xv.x, acc);
+    acc = __builtin_fmaf(q[4 * k + 1], xv.y, acc);
+    acc = __builtin_fmaf(q[4 * k + 2], xv.z, acc);
+    acc = __builtin_fmaf(q[4 * k + 3], xv.w, acc);
+  }
+  return __builtin_fmaf(d, a0 + a1, m * sx);
+}
 
 // LDS layout of an input vector: block b's 32 floats at b*XSTRIDE (36 floats:
 // a 16-byte pad per block spreads a lane group's 128-bit reads over the banks).

@@ -45,6 +45,7 @@ struct DecodeArgs {
   float *resid;  // [T][H] in/out
   float lim, lim_sh;  // SwiGLU clamp of the routed and of the shared experts (0: none)
   int down_split = 1;  // waves sharing one row group's task list in the down kernel (set by its launcher)
+  int sf_tasks = 0;    // shared rows the gate||up kernel computes: SF, or 0 after the multi-token prelude
 };
 
 // gate||up + SwiGLU, then down + weighted per-token accumulate.
