@@ -155,15 +155,15 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
     if (writer && threadIdx.x < k) ids[(size_t)t * k + threadIdx.x] = sh.pick[threadIdx.x];
     e = __builtin_amdgcn_readfirstlane(sh.pick[j]);
   }
-  float *xs = smem, *sx = smem + nbH * XSTRIDE;
-  stage_store<256, XR>(xst, H, xs, sx);
-  if (!is_sh) {
+  if (!is_sh) {  // the routed loads go out first: the input's LDS stores are off their path
     const size_t mat = (size_t)F * rowbytes;
     rg = make_rsrc(gate_exps + (size_t)e * mat, (uint32_t)mat);
     ru = make_rsrc(up_exps + (size_t)e * mat, (uint32_t)mat);
     load(ga, ua, 0, false);
     if (nch > 1) load(gb, ub, 1, false);
   }
+  float *xs = smem, *sx = smem + nbH * XSTRIDE;
+  stage_store<256, XR>(xst, H, xs, sx);
   __syncthreads();
 
   float g = 0.f, v = 0.f;

@@ -305,15 +305,20 @@ def test_determinism_and_token_independence(gpu):
         assert err.max() <= 1e-6
 
 
-def test_split_calls_equal_layer_step(gpu):
+@pytest.mark.parametrize("name,T", [("ling", 1), ("flint8", 8), ("flint8", 5)])
+def test_split_calls_equal_layer_step(gpu, name, T):
+    # one token: routing inside the gate||up kernel vs the select kernel; several
+    # tokens: the decode prelude routing and running the shared expert, vs
+    # the select kernel then the prelude's shared half alone
     moe = gpu
-    wl = S.WORKLOADS["ling"]
-    _say("router_topk + expert_ffn_q4 == layer_step")
-    w, x = _layer(wl, seed=5)
+    wl = S.WORKLOADS[name]
+    _say("router_topk + expert_ffn_q4 == layer_step", name, f"T={T}")
+    w, x = _layer(wl, seed=5, tokens=T)
     wd, xd = to_device(w), x.cuda()
     cfg = moe.config_for(wl)
     a = torch.zeros_like(xd)
-    ids, wts = torch.empty((1, 8), dtype=torch.int32, device="cuda"), torch.empty((1, 8), device="cuda")
+    ids = torch.empty((T, wl.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, wl.top_k), device="cuda")
     moe.layer_step(cfg, wd, xd, a, ids, wts)
     ids2, wts2 = moe.router_topk(cfg, wd, xd)
     b = torch.zeros_like(xd)
