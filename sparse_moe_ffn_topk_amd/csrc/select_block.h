@@ -96,6 +96,25 @@ __device__ __forceinline__ void select_load(const float *__restrict__ l, const f
   }
 }
 
+// Merge of two top-2 multisets (an equal value counts as the second).
+__device__ __forceinline__ void top2_merge(float &a, float &b, float a2, float b2) {
+  const float lo = fminf(a, a2);
+  a = fmaxf(a, a2);
+  b = fmaxf(lo, fmaxf(b, b2));
+}
+template <int N>
+__device__ __forceinline__ float row_ror_f(float v) {  // DPP row_ror:N (register moves within a 16-lane row)
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+// Top-2 of each 16-lane row, in every lane of the row: rotations by 8, 4, 2,
+// 1 merge disjoint halves (max / min only, so exact in any order).
+__device__ __forceinline__ void row_top2(float &a, float &b) {
+  top2_merge(a, b, row_ror_f<8>(a), row_ror_f<8>(b));
+  top2_merge(a, b, row_ror_f<4>(a), row_ror_f<4>(b));
+  top2_merge(a, b, row_ror_f<2>(a), row_ror_f<2>(b));
+  top2_merge(a, b, row_ror_f<1>(a), row_ror_f<1>(b));
+}
+
 // Top-2 of the PG scores held by each aligned run of PG lanes (PG a power of
 // two <= 64), as a multiset (an equal value counts as the second); every lane
 // of the run gets the pair.
@@ -133,9 +152,28 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
   }
   if (tid < 4 * SEL_MAX_K) sh.ck[tid] = 0ull;
 
+  const int PG = P.G > 1 ? P.E / P.G : P.E;  // experts per group
+  const int pg_shift = (PG & (PG - 1)) == 0 ? __builtin_ctz(PG) : -1;  // (uniform)
   if (P.Gu < P.G) {
-    const int PG = P.E / P.G;
-    if (PG <= 64 && (PG & (PG - 1)) == 0) {
+    if (PG == 64) {
+      // a group is one wave's slice: each row's top-2 by DPP rotations, then
+      // the four rows' pairs read out and merged (uniform)
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        if (r < R) {
+          float a = sv[r], b = NEG;
+          row_top2(a, b);
+          auto rl = [&](float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); };
+          float A = rl(a, 15), B = rl(b, 15);
+          top2_merge(A, B, rl(a, 31), rl(b, 31));
+          top2_merge(A, B, rl(a, 47), rl(b, 47));
+          top2_merge(A, B, rl(a, 63), rl(b, 63));
+          const int e = tid + 256 * r;
+          if ((tid & 63) == 0 && e < P.E) sh.gs[e >> 6] = A + B;
+        }
+      }
+      __syncthreads();
+    } else if (pg_shift >= 0 && PG <= 64) {
       // a group is an aligned run of PG lanes of one wave: butterfly top-2
 #pragma unroll
       for (int r = 0; r < 2; r++) {
@@ -143,7 +181,7 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
           float a = sv[r], b = NEG;
           run_top2(a, b, PG);
           const int e = tid + 256 * r;
-          if (e < P.E && (e & (PG - 1)) == 0) sh.gs[e / PG] = a + b;
+          if (e < P.E && (e & (PG - 1)) == 0) sh.gs[e >> pg_shift] = a + b;
         }
       }
       __syncthreads();
@@ -175,7 +213,7 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
 #pragma unroll
   for (int r = 0; r < 2; r++) {
     const int e = tid + 256 * r;
-    const bool real = r < R && e < P.E && (P.Gu >= P.G || sh.kept[e / (P.E / P.G)]);
+    const bool real = r < R && e < P.E && (P.Gu >= P.G || sh.kept[pg_shift >= 0 ? e >> pg_shift : e / PG]);
     kr[r] = real ? sel_key(sv[r], e) : 0ull;
   }
 
