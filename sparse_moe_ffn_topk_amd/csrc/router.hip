@@ -9,8 +9,8 @@
 //
 // MI355X design:
 //  * logits: one block owns one router row (T <= 8), its waves splitting the
-//    tokens, and streams it with 16-byte buffer loads, all issued before the
-//    first product; products and sums in f64 (full-rate on gfx950), one
+//    tokens (or, for one token, the row), and streams it with 16-byte buffer
+//    loads, all issued before the first product; products and sums in f64 (full-rate on gfx950), one
 //    rounding to f32 at the end.  Larger T runs on the f64 matrix cores
 //    (v_mfma_f64_16x16x4f64).
 //  * selection: one 256-thread block per token ranks the experts (a score's
@@ -113,6 +113,70 @@ __global__ __launch_bounds__(256) void k_router_rows(const float *__restrict__ W
       if (lane == 0) logits[(size_t)t * E + e] = (float)s;
     }
   }
+}
+
+// T = 1: one block of 256 threads per router row e; thread i takes the row's
+// 16-byte chunks i, i + 256, ... (NCB of them, every load issued up front), so
+// a wave's serial f64 work is a quarter of a row.  Partial sums reduce per
+// wave, then over the four waves in LDS in wave order (fixed: reproducible).
+// With gnorm the same two-level reduction first gives the sum of squares;
+// every block normalises its chunks the same way and block 0 writes xn.
+template <int NCB>
+__global__ __launch_bounds__(256) void k_router_row1(const float *__restrict__ W, const float *__restrict__ x, int H,
+                                                     float *__restrict__ logits, const float *__restrict__ gnorm,
+                                                     float eps, float *__restrict__ xn_out) {
+  __shared__ double red[2][4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t rowbytes = (uint32_t)H * 4u;
+  const rsrc_t rw = make_rsrc(W + (size_t)e * H, rowbytes);
+  const rsrc_t rx = make_rsrc(x, rowbytes);
+  const rsrc_t rg = make_rsrc(gnorm, rowbytes);
+  uint32_t off[NCB];
+  u32x4 wr[NCB], xv[NCB], gv[NCB];
+#pragma unroll
+  for (int i = 0; i < NCB; i++) {
+    const uint32_t o = 16u * (uint32_t)(tid + 256 * i);
+    off[i] = o < rowbytes ? o : ROUTER_OOB;
+    wr[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off[i], 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NCB; i++) xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off[i], 0, 0);
+  if (gnorm) {
+#pragma unroll
+    for (int i = 0; i < NCB; i++) gv[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, (int)off[i], 0, 0);
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < NCB; i++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const double f = (double)__uint_as_float(xv[i][c]);
+        ss = __builtin_fma(f, f, ss);
+      }
+    ss = wave_sum_d(ss);
+    if (lane == 0) red[0][w] = ss;
+    __syncthreads();
+    const double sc = 1.0 / sqrt(((red[0][0] + red[0][1]) + (red[0][2] + red[0][3])) / (double)H + (double)eps);
+#pragma unroll
+    for (int i = 0; i < NCB; i++) {
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        xv[i][c] = __float_as_uint(
+            (float)((double)__uint_as_float(xv[i][c]) * sc * (double)__uint_as_float(gv[i][c])));
+      if (e == 0 && off[i] != ROUTER_OOB) *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(xn_out) + off[i]) = xv[i];
+    }
+  }
+  double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < NCB; i++) {
+    a0 = __builtin_fma((double)__uint_as_float(wr[i][0]), (double)__uint_as_float(xv[i][0]), a0);
+    a1 = __builtin_fma((double)__uint_as_float(wr[i][1]), (double)__uint_as_float(xv[i][1]), a1);
+    a0 = __builtin_fma((double)__uint_as_float(wr[i][2]), (double)__uint_as_float(xv[i][2]), a0);
+    a1 = __builtin_fma((double)__uint_as_float(wr[i][3]), (double)__uint_as_float(xv[i][3]), a1);
+  }
+  const double s = wave_sum_d(a0 + a1);
+  if (lane == 0) red[1][w] = s;
+  __syncthreads();
+  if (tid == 0) logits[e] = (float)((red[1][0] + red[1][1]) + (red[1][2] + red[1][3]));
 }
 
 // T > 8: logits = x W^T on v_mfma_f64_16x16x4f64 (f32 inputs are exact in
@@ -232,7 +296,18 @@ int router_fuses_norm(int H, int T) { return T <= 8 && H <= 4096; }
 hipError_t launch_router_logits(const float *W, const float *x, int H, int E, int T, float *logits,
                                 hipStream_t st, const float *gnorm, float eps, float *xn) {
   if (gnorm && !router_fuses_norm(H, T)) return hipErrorInvalidValue;
-  if (T <= 8) {
+  if (T == 1 && H <= 4096) {
+    const int ncb = (H / 4 + 255) / 256;  // 16-byte chunks per thread
+    const dim3 grid(E), block(256);
+    if (ncb <= 1)
+      MOE_LAUNCH(1, (k_router_row1<1>), grid, block, 0u, st, W, x, H, logits, gnorm, eps, xn);
+    else if (ncb == 2)
+      MOE_LAUNCH(1, (k_router_row1<2>), grid, block, 0u, st, W, x, H, logits, gnorm, eps, xn);
+    else if (ncb == 3)
+      MOE_LAUNCH(1, (k_router_row1<3>), grid, block, 0u, st, W, x, H, logits, gnorm, eps, xn);
+    else
+      MOE_LAUNCH(1, (k_router_row1<4>), grid, block, 0u, st, W, x, H, logits, gnorm, eps, xn);
+  } else if (T <= 8) {
     // Chunks per lane and pass: the whole row in one pass up to H = 4096.
     const int n16 = (H + 3) / 4;
     const int nc = (n16 + 63) / 64;
