@@ -523,14 +523,16 @@ static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
 }
 
 // Down launch shape.  The split S (waves per row group) is the smallest power
-// of two <= 4 that leaves each lane at most two register chunks of blocks, so
-// all of a lane's loads are in flight at once; S > 1 runs 256-thread blocks.
-// Unsplit blocks are 256 threads, or 128 where 256 would leave fewer than 256
-// blocks (so the launch covers the 256 CUs) and the act row still stages in
-// 16 float4 per thread.
-static inline int down_split(int nq) {
+// of two <= 4 that leaves each lane at most one register chunk of blocks, as
+// long as the launch stays within 512 blocks (two per CU: more waves and
+// shorter serial chains); beyond that, at most two chunks (more blocks would
+// each stage the act row again).  S > 1 runs 256-thread blocks.  Unsplit
+// blocks are 256 threads, or 128 where 256 would leave fewer than 256 blocks
+// (so the launch covers the 256 CUs) and the act row still stages in 16
+// float4 per thread.
+static inline int down_split(int nq, int per_lane) {
   int S = 1;
-  while (S < 4 && (nq + S - 1) / S > 2 * NCHD) S <<= 1;
+  while (S < 4 && (nq + S - 1) / S > per_lane) S <<= 1;
   return S;
 }
 template <int QT>
@@ -540,7 +542,10 @@ static hipError_t down_q(DecodeArgs a, hipStream_t st) {
   if (nbS > 0 && lanes_for(nbS) < lpr) lpr = lanes_for(nbS);
   const size_t lds = (size_t)(a.k * nbF + nbS) * (XSTRIDE + 1) * sizeof(float);
   const int n = a.k * nbF * 32 + a.SF;
-  const int S = down_split(a.k * (nbF / lpr) + nbS / lpr);
+  const int nq = a.k * (nbF / lpr) + nbS / lpr;  // blocks per lane of a whole row
+  int S = down_split(nq, NCHD);
+  if (S > 1 && (size_t)((a.H + (4 / S) * (64 / lpr) - 1) / ((4 / S) * (64 / lpr))) * a.T > 512)
+    S = down_split(nq, 2 * NCHD);
   auto rows_for = [&](int nt) { return (nt / 64 / S) * (64 / lpr); };
   const bool wide = S > 1 || (size_t)((a.H + rows_for(256) - 1) / rows_for(256)) * a.T >= 256 || n > 4 * 128 * 16;
   const int nt = wide ? 256 : 128;
