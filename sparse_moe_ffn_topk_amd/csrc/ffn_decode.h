@@ -508,17 +508,27 @@ static hipError_t prelude_q(DecodeArgs &a, hipStream_t st) {
   return e;
 }
 
+#define MOE_LPR32_SWITCH(FN, QT)             \
+  if (lpr == 32) {                            \
+    MOE_XR_SWITCH(FN, QT, 32)                 \
+  } else {                                    \
+    MOE_LPR_SWITCH(FN, QT)                    \
+  }
 template <int QT>
 static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
   const int nbH = a.H / 32;
-  const int lpr = lanes_for(nbH);
+  int lpr = lanes_for(nbH);
+  // one token, Q4 blocks: 32 lanes per row where they divide the row (each
+  // lane's blocks then fit one register chunk, and the launch has twice the
+  // blocks; measured slower for Q8_0's 34-byte blocks, which stay at 16)
+  if (QT != MOE_Q8_0 && a.T == 1 && lpr == 16 && nbH % 32 == 0 && nbH / 32 <= NCH) lpr = 32;
   const int rw = 64 / lpr;  // rows per wave task
   const int tasks = (a.sf_tasks + rw - 1) / rw + a.k * ((a.F + rw - 1) / rw);
   if (tasks == 0) return hipSuccess;  // (a dense layer whose rows the prelude computed)
   const dim3 grid((tasks + 3) / 4, a.T);
   const size_t lds = (size_t)nbH * (XSTRIDE + 1) * sizeof(float);
   const int xr = xr_for(a.H, 256);
-  MOE_LPR_SWITCH(gateup_launch, QT)
+  MOE_LPR32_SWITCH(gateup_launch, QT)
   return hipGetLastError();
 }
 

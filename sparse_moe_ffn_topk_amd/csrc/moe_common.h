@@ -255,14 +255,18 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
   return __builtin_bit_cast(double, ((long long)hi << 32) | (long long)(unsigned)lo);
 }
 
-// Sum over aligned groups of W consecutive lanes (W a power of two <= 16):
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 32):
 // the LAST lane of each group (lane % W == W-1) receives the group total.
+// For W = 32 the odd rows then add lane 15 of the row below (DPP row_bcast:15,
+// rows 1 and 3 written).
 template <int W>
 __device__ __forceinline__ float group_sum_last(float v) {
   if constexpr (W >= 2) v += dpp_f<DPP_ROW_SHR1>(v);
   if constexpr (W >= 4) v += dpp_f<DPP_ROW_SHR2>(v);
   if constexpr (W >= 8) v += dpp_f<DPP_ROW_SHR4>(v);
   if constexpr (W >= 16) v += dpp_f<DPP_ROW_SHR8>(v);
+  if constexpr (W >= 32)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
   return v;
 }
 
