@@ -354,6 +354,11 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   const float wt_v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rwt, (int)(lane * 4u), 0, 0));
   Stage<XR> ast;  // the token's act row: its k routed rows, then the shared row
   stage_load<NT, XR>(ast, act + (size_t)t * (k * F + SF), k * F + SF);
+  // the residual values this block updates, loaded now: the end of the kernel
+  // then adds to them without another memory round trip
+  const int hb = blockIdx.x * rows + (int)threadIdx.x;  // (SPLIT: thread i finishes row i of the block)
+  const bool writer = SPLIT ? ((int)threadIdx.x < rows && hb < H) : (li == LPR - 1 && live);
+  const float r_in = writer ? resid[(size_t)t * H + (SPLIT ? hb : h)] : 0.f;
 
   // task q: the shared row (j = k) for q < bplS, then pick j = (q - bplS) / bplF
   auto pick = [&](int q) { return (q < bplS || bplF == 0) ? k : (q - bplS) / bplF; };  // (k == 0: shared only)
@@ -400,15 +405,14 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   }
   acc = group_sum_last<LPR>(acc);
   if constexpr (!SPLIT) {
-    if (li == LPR - 1 && live) resid[(size_t)t * H + h] += acc;
+    if (writer) resid[(size_t)t * H + h] = r_in + acc;
   } else {
     if (li == LPR - 1) part[ws * rows + rb] = acc;
     __syncthreads();
-    const int hb = blockIdx.x * rows + (int)threadIdx.x;
-    if ((int)threadIdx.x < rows && hb < H) {
+    if (writer) {
       float y = part[threadIdx.x];
       for (int s2 = 1; s2 < S; s2++) y += part[s2 * rows + threadIdx.x];
-      resid[(size_t)t * H + hb] += y;
+      resid[(size_t)t * H + hb] = r_in + y;
     }
   }
 }
