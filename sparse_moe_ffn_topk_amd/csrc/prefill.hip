@@ -13,8 +13,8 @@
 // Steps:
 //  1. k_sort_by_expert (one block): a stable counting sort of the pairs by
 //     expert, tokens ascending within an expert: per-expert token bit sets,
-//     popcount prefixes, an exclusive scan -> offsets, pos[p], perm[pos], and
-//     the list of 16-token tiles of every expert.
+//     popcount prefixes, an exclusive scan (wave shuffles) -> offsets, pos[p],
+//     perm[pos], and the list of 16-token tiles of every expert.
 //  2. k_group_gemm<GATEUP>: per (tile, 256-row slice): g and u for 16 tokens
 //     x 256 rows, SwiGLU in registers, act rows written in sorted order; the
 //     shared expert runs as extra tiles over all tokens.
@@ -70,17 +70,45 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
     cnt[tid] = c;
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, to = 0;
-    for (int e = 0; e < E; e++) {
-      off[e] = o;
-      toff[e] = to;
-      o += cnt[e];
-      to += (cnt[e] + 15) >> 4;
+  // exclusive scans of the pair counts and of the 16-token tile counts over
+  // the E <= 512 experts: inclusive scans within each wave (shuffles), then
+  // the totals of the waves before it
+  __shared__ int wsum[8], wtsum[8];
+  const int lane = tid & 63, wave = tid >> 6;
+  int v = 0, tv = 0;
+  if (tid < 512) {
+    v = tid < E ? cnt[tid] : 0;
+    tv = (v + 15) >> 4;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int nv = __shfl_up(v, d, 64), ntv = __shfl_up(tv, d, 64);
+      if (lane >= d) {
+        v += nv;
+        tv += ntv;
+      }
     }
-    off[E] = o;
-    toff[E] = to;
-    *ntiles = to;
+    if (lane == 63) {
+      wsum[wave] = v;
+      wtsum[wave] = tv;
+    }
+  }
+  __syncthreads();
+  if (tid < 512) {
+    int o = 0, to = 0;
+    for (int w = 0; w < wave; w++) {
+      o += wsum[w];
+      to += wtsum[w];
+    }
+    const int c = tid < E ? cnt[tid] : 0;
+    if (tid < E) {
+      off[tid] = o + v - c;
+      toff[tid] = to + tv - ((c + 15) >> 4);
+    }
+    if (tid == E - 1) {
+      off[E] = o + v;
+      toff[E] = to + tv;
+      *ntiles = to + tv;
+    }
   }
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];

@@ -181,25 +181,30 @@ __global__ __launch_bounds__(256) void k_router_row1(const float *__restrict__ W
 
 // T > 8: logits = x W^T on v_mfma_f64_16x16x4f64 (f32 inputs are exact in
 // f64, so products are exact and sums are f64, as in the row kernel).  A block
-// takes 16 router rows x 64 tokens; wave w the tokens 16w..16w+15.  Lane l
-// feeds A = x[token l%16][h + l/16] and B = W[row l%16][h + l/16] and holds
-// D[token l/16 + 4i][row l%16], i < 4.  W and x are staged through LDS in
-// chunks of RKT columns (16-byte loads, next chunk prefetched into registers);
-// columns past H, rows past E and tokens past T read as zeros.
+// takes 16 router rows x 32 tokens; wave w the tokens 16 (w & 1) .. +15 over
+// the half w >> 1 of every chunk's columns, so every SIMD of the chip has a
+// wave (split K), with four accumulator chains per wave.  Lane l feeds A =
+// x[token l%16][h + l/16] and B = W[row l%16][h + l/16] and holds
+// D[token l/16 + 4i][row l%16], i < 4.  The two halves' sums are added in a
+// fixed order (reproducible).  W and x are staged through LDS in chunks of RKT
+// columns (16-byte loads, next chunk prefetched into registers); columns past
+// H, rows past E and tokens past T read as zeros.
 constexpr int RKT = 64;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W, const float *__restrict__ x, int H,
                                                      int E, int T, float *__restrict__ logits) {
   __shared__ __attribute__((aligned(16))) float ws[16][RKT + 4];
-  __shared__ __attribute__((aligned(16))) float xs[64][RKT + 4];
+  __shared__ __attribute__((aligned(16))) float xs[32][RKT + 4];
+  __shared__ f64x4 red[2][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 64;
-  const int ne = min(16, E - e0), nt = min(64, T - t0);
+  const int tg = wave & 1, kh = wave >> 1;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 32;
+  const int ne = min(16, E - e0), nt = min(32, T - t0);
   const rsrc_t rW = make_rsrc(W + (size_t)e0 * H, (uint32_t)ne * (uint32_t)H * 4u);
   const rsrc_t rX = make_rsrc(x + (size_t)t0 * H, (uint32_t)nt * (uint32_t)H * 4u);
   // staging roles: W row tid/16, x rows (tid + 256 i)/16; 16-byte column c4 = tid % 16
   const int c4 = tid & 15;
-  u32x4 wr, xr[4];
+  u32x4 wr, xr[2];
   auto issue = [&](int h0) {
     const int h = h0 + 4 * c4;
     {
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
       wr = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < 2; i++) {
       const int r = (tid + 256 * i) >> 4;
       xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
@@ -215,28 +220,38 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
   auto put = [&]() {
     *reinterpret_cast<u32x4 *>(&ws[tid >> 4][4 * c4]) = wr;
 #pragma unroll
-    for (int i = 0; i < 4; i++) *reinterpret_cast<u32x4 *>(&xs[(tid + 256 * i) >> 4][4 * c4]) = xr[i];
+    for (int i = 0; i < 2; i++) *reinterpret_cast<u32x4 *>(&xs[(tid + 256 * i) >> 4][4 * c4]) = xr[i];
   };
-  f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+  f64x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
   const int m = lane & 15, kq = lane >> 4;
+  const float *xrow = xs[16 * tg + m];
+  const float *wrow = ws[m];
   issue(0);
   for (int h0 = 0; h0 < H; h0 += RKT) {
     put();
     __syncthreads();
     if (h0 + RKT < H) issue(h0 + RKT);
 #pragma unroll
-    for (int kk = 0; kk < RKT; kk += 8) {
-      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xs[16 * wave + m][kk + kq], (double)ws[m][kk + kq], acc0, 0,
-                                                  0, 0);
-      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xs[16 * wave + m][kk + 4 + kq], (double)ws[m][kk + 4 + kq],
-                                                  acc1, 0, 0, 0);
+    for (int kk = kh * (RKT / 2); kk < (kh + 1) * (RKT / 2); kk += 16) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xrow[kk + 4 * j + kq], (double)wrow[kk + 4 * j + kq],
+                                                      acc[j], 0, 0, 0);
     }
     __syncthreads();
   }
+  const f64x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  if (kh == 1) red[tg][lane] = sum;
+  __syncthreads();
+  if (kh == 0) {
+    const f64x4 tot = sum + red[tg][lane];
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int t = 16 * wave + kq + 4 * i, e = m;
-    if (t < nt && e < ne) logits[(size_t)(t0 + t) * E + e0 + e] = (float)(acc0[i] + acc1[i]);
+    for (int i = 0; i < 4; i++) {
+      const int t = 16 * tg + kq + 4 * i, e = m;
+      if (t < nt && e < ne) logits[(size_t)(t0 + t) * E + e0 + e] = (float)tot[i];
+    }
   }
 }
 
@@ -331,7 +346,7 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
       MOE_ROUTER_ROWS(2);
 #undef MOE_ROUTER_ROWS
   } else {
-    const dim3 grid((E + 15) / 16, (T + 63) / 64);
+    const dim3 grid((E + 15) / 16, (T + 31) / 32);
     MOE_LAUNCH(1, k_router_mfma, grid, dim3(256), 0u, st, W, x, H, E, T, logits);
   }
   return hipGetLastError();
