@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void k_router_row1(const float *__restrict__ W
 // fixed order (reproducible).  W and x are staged through LDS in chunks of RKT
 // columns (16-byte loads, next chunk prefetched into registers); columns past
 // H, rows past E and tokens past T read as zeros.
-constexpr int RKT = 64;
+constexpr int RKT = 128;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W, const float *__restrict__ x, int H,
                                                      int E, int T, float *__restrict__ logits) {
@@ -202,25 +202,33 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
   const int ne = min(16, E - e0), nt = min(32, T - t0);
   const rsrc_t rW = make_rsrc(W + (size_t)e0 * H, (uint32_t)ne * (uint32_t)H * 4u);
   const rsrc_t rX = make_rsrc(x + (size_t)t0 * H, (uint32_t)nt * (uint32_t)H * 4u);
-  // staging roles: W row tid/16, x rows (tid + 256 i)/16; 16-byte column c4 = tid % 16
-  const int c4 = tid & 15;
-  u32x4 wr, xr[2];
+  // staging roles: piece q = tid + 256 i of a chunk is row q / 32, 16-byte
+  // column q % 32 (W: i < 2, rows 0..15; x: i < 4, rows 0..31)
+  constexpr int CPR = RKT / 4;  // 16-byte columns per staged row
+  u32x4 wr[16 * CPR / 256], xr[32 * CPR / 256];
   auto issue = [&](int h0) {
-    const int h = h0 + 4 * c4;
-    {
-      const int r = tid >> 4;
-      wr = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16 * CPR / 256; i++) {
+      const int q = tid + 256 * i, r = q / CPR, h = h0 + 4 * (q % CPR);
+      wr[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-      const int r = (tid + 256 * i) >> 4;
+    for (int i = 0; i < 32 * CPR / 256; i++) {
+      const int q = tid + 256 * i, r = q / CPR, h = h0 + 4 * (q % CPR);
       xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
   };
   auto put = [&]() {
-    *reinterpret_cast<u32x4 *>(&ws[tid >> 4][4 * c4]) = wr;
 #pragma unroll
-    for (int i = 0; i < 2; i++) *reinterpret_cast<u32x4 *>(&xs[(tid + 256 * i) >> 4][4 * c4]) = xr[i];
+    for (int i = 0; i < 16 * CPR / 256; i++) {
+      const int q = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&ws[q / CPR][4 * (q % CPR)]) = wr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 256; i++) {
+      const int q = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&xs[q / CPR][4 * (q % CPR)]) = xr[i];
+    }
   };
   f64x4 acc[4];
 #pragma unroll
