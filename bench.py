@@ -52,7 +52,8 @@ KERNEL_SOURCES = {
     "gateup_swiglu": ("moe_common.h", "select_block.h", "ffn_decode.h", "ffn_decode_q41.hip", "ffn_decode_q40.hip"),
     "group_gateup": ("moe_common.h", "prefill.hip"),
 }
-KERNEL_SYMBOLS = {"gateup_swiglu": "k_gateup_swiglu", "group_gateup": "k_group_gemm<1, 0>"}
+# (the grouped gate||up at the Flint prefill shape runs as the row-streaming kernel)
+KERNEL_SYMBOLS = {"gateup_swiglu": "k_gateup_swiglu", "group_gateup": "k_group_gateup_rows"}
 
 
 def kernel_source_hash(kernel):
@@ -323,7 +324,7 @@ def main():
         us = kstats["group_gateup"]["mean_us"]
         ach = per_launch / (us * 1e-6) / 1e9
         flops = 2.0 * 2 * T * (wl.top_k * wl.expert_ff + wl.shared_ff) * wl.hidden
-        roofline = {"bound": "hbm", "kernel": "k_group_gemm<GATEUP>", "achieved": round(ach, 1),
+        roofline = {"bound": "hbm", "kernel": "k_group_gateup_rows", "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": load_traffic("group_gateup", wl.name), "algorithmic_bytes_per_launch": int(per_launch),
                     "mean_launch_us": round(us, 3),
