@@ -215,6 +215,24 @@ def test_layer_q4_0_unaligned_rows(gpu, H, F, SF, T):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("qt", [S.Q4_1, S.Q4_0])
+@pytest.mark.parametrize("H", [512, 1024, 1536, 2048])
+def test_grouped_gateup_row_streaming_shapes(gpu, H, qt):
+    # the grouped gate||up's row-streaming form: rows of 16, 32, 48 and 64 blocks
+    # (one compile-time K split each), Q4_1 and Q4_0, routed tiles with 1..3
+    # tiles per expert and a shared expert, a ragged token count, the SwiGLU
+    # clamp active on both
+    import dataclasses
+    wl = S.Workload("rowstream", H, 12, 3, 160, 96, qt, has_bias=True)
+    wl = dataclasses.replace(wl, swiglu_limit=3.0, swiglu_limit_shared=2.0)
+    T = 37
+    _say("grouped gate||up row-streaming", "H", H, "qtype", qt, "T", T)
+    w, x = _layer(wl, seed=H + qt, tokens=T)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    print(f"[result] row-streaming H={H} q={qt} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("name,T", [("lfm25_q8", 1), ("lfm25_q8", 3), ("lfm25_q8", 520)])
 def test_layer_q8_0(gpu, name, T):
     # Q8_0 experts (f16 d, 32 signed bytes; the lfm2_moe_ssd.js page's int8 expert plane), decode and grouped
