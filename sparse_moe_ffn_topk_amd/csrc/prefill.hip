@@ -482,10 +482,10 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // reads 80 bytes from each of 512 rows per chunk, a pattern that a stream
 // probe ran at 3.5 TB/s against 5.7 TB/s for these runs).  Wave w takes K
 // blocks [w KQ, (w+1) KQ): its tokens' inputs for those blocks are held as
-// MFMA A fragments (f16 hi + lo) in registers for the whole block, and its
-// four partial tiles per chunk are added in wave order (fixed: reproducible),
-// then SwiGLU'd and stored.  LDS stays under a third of the CU's, so three
-// blocks fit a CU (fewer left the grid needing a second round of blocks).
+// MFMA A fragments (f16 hi + lo) in registers for the whole block.  The four
+// waves' partial tiles of a chunk are added in wave order (fixed:
+// reproducible), each wave finishing a quarter of the tile's values (SwiGLU
+// and store).  Its registers (about 250 per lane) allow two blocks per CU.
 constexpr int RS_RB = 256;   // rows per block, per matrix
 constexpr int RS_KQM = 16;   // max K blocks per wave
 template <int QT, int KQ>
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   constexpr int MAXDW = KQ * 4 * BS / 4;       // dwords of a row
   constexpr int PADW = MAXDW + 4;              // staged row stride (a 16-byte pad spreads the banks)
   __shared__ __attribute__((aligned(16))) uint32_t bst[2][16][PADW];
-  __shared__ __attribute__((aligned(16))) f32x4 red[3][2][64];  // waves 1..3 (wave 0 adds from registers)
+  __shared__ __attribute__((aligned(16))) float red[4][2][64][4];  // [wave][gate, up][lane][element]
   __shared__ __attribute__((aligned(16))) float asum[4][RS_KQM][16];
   __shared__ int rowid[16], outid[16];
 
@@ -629,29 +629,25 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
         for (int i = 0; i < 4; i++) acc[m][i] = __builtin_fmaf(d, z[i], __builtin_fmaf(mo, sx[i], acc[m][i]));
       }
     }
-    if (wave > 0) {
-      red[wave - 1][0][lane] = acc[0];
-      red[wave - 1][1][lane] = acc[1];
-    }
+    *reinterpret_cast<f32x4 *>(red[wave][0][lane]) = acc[0];
+    *reinterpret_cast<f32x4 *>(red[wave][1][lane]) = acc[1];
     __syncthreads();
-    if (wave == 0) {
-      // D[token 4 kq + i][row r0 + 16 c + n], waves added in order 0..3
-      const f32x4 g = ((acc[0] + red[0][0][lane]) + red[1][0][lane]) + red[2][0][lane];
-      const f32x4 u = ((acc[1] + red[0][1][lane]) + red[1][1][lane]) + red[2][1][lane];
-      const int row = r0 + 16 * c + n;
-      const float L = shared ? a.lim_sh : a.lim;
-      float *dst = shared ? a.out_sh : a.out;
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int o = outid[4 * kq + i];
-        if (o >= 0 && row < R) {
-          float sg = g[i] / (1.0f + __expf(-g[i])), uu = u[i];
-          if (L > 0.f) {
-            uu = fminf(fmaxf(uu, -L), L);
-            sg = fminf(sg, L);
-          }
-          dst[(size_t)o * R + row] = sg * uu;
+    {
+      // wave w finishes element w of every lane's tile values: D[token 4 (l/16) + w][row r0 + 16 c + l%16],
+      // the waves' partials added in order 0..3
+      const int l = lane, i = wave;
+      const float g = ((red[0][0][l][i] + red[1][0][l][i]) + red[2][0][l][i]) + red[3][0][l][i];
+      const float u = ((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i];
+      const int row = r0 + 16 * c + (l & 15);
+      const int o = outid[4 * (l >> 4) + i];
+      if (o >= 0 && row < R) {
+        const float L = shared ? a.lim_sh : a.lim;
+        float sg = g / (1.0f + __expf(-g)), uu = u;
+        if (L > 0.f) {
+          uu = fminf(fmaxf(uu, -L), L);
+          sg = fminf(sg, L);
         }
+        (shared ? a.out_sh : a.out)[(size_t)o * R + row] = sg * uu;
       }
     }
   }
