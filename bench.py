@@ -305,12 +305,16 @@ def main():
                   (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN))
                   + ((("prelude", moe.KERNEL_PRELUDE),) if T > 1 else ()))
         for name, kid in ((dominant[1], dominant[0]),) + others:
-            with moe.KernelTimer(kid, nk * L) as kt:
+            with moe.KernelTimer(kid, 2 * nk * L) as kt:  # (up to two launches per layer)
                 for i in range(nk):
                     stacks[i % nS].step()
                 torch.cuda.synchronize()
-            kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us}
+            # (mean per launch, and the kernel's time per layer step: the grouped down runs as
+            # two launches, routed and shared tiles, where its row-streaming form applies)
+            kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us,
+                            "us_per_layer": 1000.0 * kt.total_ms / (nk * L)}
         log("kernel means (us, eager dispatches): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
+        log("kernel time per layer step (us): " + ", ".join(f"{k}={v['us_per_layer']:.2f}" for k, v in kstats.items()))
 
     roofline = None
     if "group_gateup" in kstats:
@@ -375,6 +379,7 @@ def main():
         "weight_stream_GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "us_per_layer": round(ms_step * 1e3 / L, 3), "tok_s_per_layer": round(tok_s * L, 1),
         "weight_bytes_per_step": int(mean_bytes), "kernels_us": {k: round(v["mean_us"], 3) for k, v in kstats.items()},
+        "kernels_us_per_layer": {k: round(v["us_per_layer"], 3) for k, v in kstats.items()},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

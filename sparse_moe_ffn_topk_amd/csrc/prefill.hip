@@ -653,6 +653,173 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   }
 }
 
+// Grouped down, row-streaming form (Q4 blocks; K = F or SF of 16..64 blocks,
+// rows a multiple of 16 bytes): as k_group_gateup_rows for one matrix.  A
+// block takes one 16-token tile x 256 rows; a chunk is TPC 16-row tiles of
+// whole rows (about 20 KB, one contiguous run); wave w takes K blocks
+// [w KQ, (w+1) KQ) of every tile, with its tokens' act rows held as MFMA A
+// fragments.  The waves' partial tiles are added in wave order and weighted
+// by the pair's routing weight.  Routed and shared tiles run as separate
+// launches (their K differ): tile0 is the first tile index of the launch.
+template <int QT, int KQ>
+__global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile0) {
+  static_assert(KQ <= RS_KQM, "K blocks per wave");
+  constexpr int BS = QBlock<QT>::bytes;
+  constexpr int TPC = KQ <= 4 ? 4 : (KQ <= 8 ? 2 : 1);  // 16-row tiles per chunk
+  constexpr int CR = 16 * TPC;                          // rows per chunk
+  constexpr int ROWDW = KQ * 4 * BS / 4;                // dwords of a row
+  constexpr int PADW = ROWDW + 4;                       // staged row stride (a 16-byte pad spreads the banks)
+  __shared__ __attribute__((aligned(16))) uint32_t bst[CR][PADW];
+  __shared__ __attribute__((aligned(16))) float red[4][TPC][64][4];  // [wave][tile][lane][element]
+  __shared__ __attribute__((aligned(16))) float asum[4][KQ][16];
+  __shared__ int rowid[16], outid[16];
+  __shared__ float outw[16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bx = (int)blockIdx.x + tile0;
+  const bool shared = bx >= a.max_routed_tiles;
+  int e = 0, first = 0, ntok, K;
+  const int R = a.H;
+  const uint8_t *m0p;
+  if (!shared) {
+    if (bx >= __builtin_amdgcn_readfirstlane(*a.ntiles)) return;
+    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * bx]);
+    first = __builtin_amdgcn_readfirstlane(a.offsets[e] + a.tiles[2 * bx + 1]);
+    ntok = min(16, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - first);
+    K = a.F;
+    m0p = a.w0 + (size_t)e * ((size_t)R * (K / 32) * BS);
+  } else {
+    first = 16 * (bx - a.max_routed_tiles);
+    ntok = min(16, a.T - first);
+    K = a.SF;
+    m0p = a.s0;
+  }
+  if (tid < 16) {
+    const bool ok = tid < ntok;
+    const int q = first + tid;
+    rowid[tid] = ok ? q : -1;
+    outid[tid] = ok ? q : -1;
+    outw[tid] = ok && !shared ? a.wts[a.perm[q]] : 1.f;
+  }
+  const int r0 = blockIdx.y * RS_RB;
+  if (r0 >= R) return;
+  const uint32_t rowbytes = (uint32_t)(4 * KQ) * BS;
+  const rsrc_t rw = make_rsrc(m0p, (uint32_t)((size_t)R * rowbytes));
+  const float *arows = shared ? a.act_sh : a.act;
+  const int nrows = shared ? a.T : a.T * a.k;
+  const rsrc_t ra = make_rsrc(arows, (uint32_t)nrows * (uint32_t)K * 4u);
+  const int n = lane & 15, kq = lane >> 4;
+  __syncthreads();  // rowid
+
+  // this wave's A fragments (as in k_group_gateup_rows)
+  half8 xh[KQ], xl[KQ];
+  {
+    const int arow = rowid[n];
+    u32x4 v0[2][2], v1[2][2];
+    auto load_group = [&](int g, u32x4 (&a0)[2], u32x4 (&a1)[2]) {
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        const uint32_t k0 = (uint32_t)((wave * KQ + 2 * g + jj) * 32 + 8 * kq);
+        const uint32_t off = arow >= 0 ? ((uint32_t)arow * (uint32_t)K + k0) * 4u : 0x7ffffff0u;
+        a0[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+        a1[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(arow >= 0 ? off + 16u : off), 0, 0);
+      }
+    };
+    load_group(0, v0[0], v1[0]);
+#pragma unroll
+    for (int g = 0; g < KQ / 2; g++) {
+      if (g + 1 < KQ / 2) load_group(g + 1, v0[(g + 1) & 1], v1[(g + 1) & 1]);
+#pragma unroll
+      for (int jj = 0; jj < 2; jj++) {
+        const int j = 2 * g + jj;
+        float xv[8];
+        const u32x4 a0 = v0[g & 1][jj], a1 = v1[g & 1][jj];
+        xv[0] = __uint_as_float(a0.x); xv[1] = __uint_as_float(a0.y); xv[2] = __uint_as_float(a0.z); xv[3] = __uint_as_float(a0.w);
+        xv[4] = __uint_as_float(a1.x); xv[5] = __uint_as_float(a1.y); xv[6] = __uint_as_float(a1.z); xv[7] = __uint_as_float(a1.w);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          const _Float16 h = (_Float16)xv[i];
+          xh[j][kperm(i)] = h;
+          xl[j][kperm(i)] = (_Float16)(xv[i] - (float)h);
+          sum += xv[i];
+        }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        if (kq == 0) asum[wave][j][n] = sum;
+      }
+    }
+  }
+
+  // staged chunk: CR whole rows, row i at bst[i]
+  constexpr int PMAX = (CR * ROWDW / 4 + 255) / 256;
+  constexpr int PPR = ROWDW / 4;  // 16-byte pieces per row
+  u32x4 breg[PMAX];
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PMAX; i++) {
+      const int q = tid + 256 * i;
+      const uint32_t off = (q < CR * PPR && r0 + CR * c + q / PPR < R)
+                               ? (uint32_t)(r0 + CR * c) * rowbytes + 16u * (uint32_t)q
+                               : 0x7ffffff0u;
+      breg[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < PMAX; i++) {
+      const int q = tid + 256 * i;
+      if (q < CR * PPR) {
+        const int row = q / PPR, pc = q - row * PPR;
+        *reinterpret_cast<u32x4 *>(&bst[row][4 * pc]) = breg[i];
+      }
+    }
+  };
+
+  const int nch = (min(RS_RB, R - r0) + CR - 1) / CR;
+  issue(0);
+  for (int c = 0; c < nch; c++) {
+    stage();
+    __syncthreads();
+    if (c + 1 < nch) issue(c + 1);
+    f32x4 acc[TPC];
+#pragma unroll
+    for (int t = 0; t < TPC; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KQ; j++) {
+      const int jb = wave * KQ + j;
+      const float4 sx4 = *reinterpret_cast<const float4 *>(&asum[wave][j][4 * kq]);
+      const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
+#pragma unroll
+      for (int t = 0; t < TPC; t++) {
+        float d, mo;
+        const half8 q = QStaged<QT>::frag(&bst[16 * t + n][0], 0, jb, kq, d, mo);
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[j], q, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[j], q, z, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[t][i] = __builtin_fmaf(d, z[i], __builtin_fmaf(mo, sx[i], acc[t][i]));
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TPC; t++) *reinterpret_cast<f32x4 *>(red[wave][t][lane]) = acc[t];
+    __syncthreads();
+    {
+      // wave w finishes element w: D[token 4 (l/16) + w][row r0 + CR c + 16 t + l%16], waves added in order
+      const int l = lane, i = wave;
+      const int slot = 4 * (l >> 4) + i, o = outid[slot];
+      const float wgt = outw[slot];
+      float *dst = shared ? a.out_sh : a.out;
+#pragma unroll
+      for (int t = 0; t < TPC; t++) {
+        const float v = ((red[0][t][l][i] + red[1][t][l][i]) + red[2][t][l][i]) + red[3][t][l][i];
+        const int row = r0 + CR * c + 16 * t + (l & 15);
+        if (o >= 0 && row < R) dst[(size_t)o * R + row] = wgt * v;
+      }
+    }
+  }
+}
+
 // resid[t][h] += sum_j Y[pos(t, j)][h] + Ysh[t][h]
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, const float *__restrict__ Ysh,
                                                  const int32_t *__restrict__ pos, int T, int k, int H,
@@ -737,7 +904,35 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   g.s1 = nullptr;
   g.out = p.Y;
   g.out_sh = p.Ysh;
-  {
+  const int nbF = k > 0 ? p.F / 32 : 0, nbS = p.SF / 32;
+  auto rowable = [](int nb) { return nb % 16 == 0 && nb <= 4 * RS_KQM; };
+  if (p.qtype != MOE_Q8_0 && (nbF == 0 || rowable(nbF)) && (nbS == 0 || rowable(nbS))) {
+    // row-streaming form: routed tiles, then shared tiles, one launch each
+    const int ys = (p.H + RS_RB - 1) / RS_RB;
+#define MOE_DR_LAUNCH(QT, NB, NTILES, T0)                                                                    \
+  switch ((NB) / 4) {                                                                                       \
+    case 4: MOE_LAUNCH(7, (k_group_down_rows<QT, 4>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break;   \
+    case 8: MOE_LAUNCH(7, (k_group_down_rows<QT, 8>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break;   \
+    case 12: MOE_LAUNCH(7, (k_group_down_rows<QT, 12>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break; \
+    default: MOE_LAUNCH(7, (k_group_down_rows<QT, 16>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break; \
+  }
+    if (nbF > 0) {
+      if (p.qtype == MOE_Q4_1) {
+        MOE_DR_LAUNCH(MOE_Q4_1, nbF, g.max_routed_tiles, 0)
+      } else {
+        MOE_DR_LAUNCH(MOE_Q4_0, nbF, g.max_routed_tiles, 0)
+      }
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (shtiles > 0) {
+      if (p.qtype == MOE_Q4_1) {
+        MOE_DR_LAUNCH(MOE_Q4_1, nbS, shtiles, g.max_routed_tiles)
+      } else {
+        MOE_DR_LAUNCH(MOE_Q4_0, nbS, shtiles, g.max_routed_tiles)
+      }
+    }
+#undef MOE_DR_LAUNCH
+  } else {
     dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
     if (p.qtype == MOE_Q4_1)
       MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_1, GG_DOWN>), grid, dim3(256), 0u, st, g);
