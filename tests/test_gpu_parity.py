@@ -233,6 +233,21 @@ def test_grouped_gateup_row_streaming_shapes(gpu, H, qt):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("qt", [S.Q4_1, S.Q4_0])
+@pytest.mark.parametrize("F,SF", [(512, 0), (1536, 512), (2048, 1024)])
+def test_grouped_down_row_streaming_shapes(gpu, F, SF, qt):
+    # the grouped down's row-streaming form: routed rows of 16, 48 or 64 blocks
+    # and shared rows of 16 or 32 (a launch each), Q4_1 and Q4_0, a ragged
+    # token count; the gate||up runs its row-streaming form too (H = 512)
+    wl = S.Workload("rowdown", 512, 10, 3, F, SF, qt, has_bias=True)
+    T = 29
+    _say("grouped down row-streaming", "F", F, "SF", SF, "qtype", qt, "T", T)
+    w, x = _layer(wl, seed=F + SF + qt, tokens=T)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    print(f"[result] down row-streaming F={F} SF={SF} q={qt} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("name,T", [("lfm25_q8", 1), ("lfm25_q8", 3), ("lfm25_q8", 520)])
 def test_layer_q8_0(gpu, name, T):
     # Q8_0 experts (f16 d, 32 signed bytes; the lfm2_moe_ssd.js page's int8 expert plane), decode and grouped
