@@ -486,7 +486,8 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // waves' partial tiles of a chunk are added in wave order (fixed:
 // reproducible), each wave finishing a quarter of the tile's values (SwiGLU
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
-constexpr int RS_RB = 256;   // rows per block, per matrix
+constexpr int RS_RB = 256;   // rows per block (down)
+constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
 template <int QT, int KQ>
 __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     rowid[tid] = ok ? (shared ? q : a.perm[q] / a.k) : -1;
     outid[tid] = ok ? q : -1;
   }
-  const int r0 = blockIdx.y * RS_RB;
+  const int r0 = blockIdx.y * RS_GU_RB;
   if (r0 >= R) return;
   const int K = a.H, nbK = 4 * KQ;
   const uint32_t rowbytes = (uint32_t)nbK * BS, rowdw = rowbytes / 4u;
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     }
   };
 
-  const int nch = min(RS_RB, R - r0 + 15) / 16;
+  const int nch = min(RS_GU_RB, R - r0 + 15) / 16;
   issue(0);
   for (int c = 0; c < nch; c++) {
     stage();
@@ -877,6 +878,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     const int nbH = p.H / 32;
     // row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks (whole 16-byte pieces)
     const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
+    if (rowform) grid.y = (rows + RS_GU_RB - 1) / RS_GU_RB;
 #define MOE_RS_LAUNCH(QT)                                                                                \
   switch (nbH / 4) {                                                                                     \
     case 4: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 4>), grid, dim3(256), 0u, st, g); break;             \
