@@ -269,6 +269,7 @@ def main():
         for l in range(L):
             distinct[s, l] = len(np.unique(h[l]))
     step_bytes = [float(L * (router_bytes + shared_bytes) + distinct[s].sum() * per_expert) for s in range(nS)]
+    log(f"distinct picked experts per layer step: mean {distinct.mean():.1f} (T={T} tokens x {wl.top_k} picks)")
 
     grouped = T > moe.load_library().moe_decode_max_tokens()
     dominant = (moe.KERNEL_GROUP_GATEUP, "group_gateup") if grouped else (moe.KERNEL_GATEUP, "gateup_swiglu")
