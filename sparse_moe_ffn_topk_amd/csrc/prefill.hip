@@ -821,16 +821,35 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile
   }
 }
 
-// resid[t][h] += sum_j Y[pos(t, j)][h] + Ysh[t][h]
+// resid[t][h] += sum_j Y[pos(t, j)][h] + Ysh[t][h], the same order for every
+// element; each thread takes four consecutive h (16-byte loads; H % 32 == 0).
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, const float *__restrict__ Ysh,
                                                  const int32_t *__restrict__ pos, int T, int k, int H,
                                                  float *__restrict__ resid) {
-  const int t = blockIdx.y, h = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.y, h = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (h >= H) return;
-  float acc = 0.f;
-  for (int j = 0; j < k; j++) acc += Y[(size_t)pos[t * k + j] * H + h];
-  if (Ysh) acc += Ysh[(size_t)t * H + h];
-  resid[(size_t)t * H + h] += acc;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; j++) {
+    const float4 y = *reinterpret_cast<const float4 *>(Y + (size_t)pos[t * k + j] * H + h);
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  if (Ysh) {
+    const float4 y = *reinterpret_cast<const float4 *>(Ysh + (size_t)t * H + h);
+    acc.x += y.x;
+    acc.y += y.y;
+    acc.z += y.z;
+    acc.w += y.w;
+  }
+  float4 *r = reinterpret_cast<float4 *>(resid + (size_t)t * H + h);
+  float4 v = *r;
+  v.x += acc.x;
+  v.y += acc.y;
+  v.z += acc.z;
+  v.w += acc.w;
+  *r = v;
 }
 
 // ---------------------------------------------------------------- launch --
@@ -944,7 +963,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
       MOE_LAUNCH(7, (k_group_gemm<MOE_Q4_0, GG_DOWN>), grid, dim3(256), 0u, st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  MOE_LAUNCH(8, k_combine, dim3((p.H + 255) / 256, T), dim3(256), 0u, st, (const float *)p.Y,
+  MOE_LAUNCH(8, k_combine, dim3((p.H / 4 + 255) / 256, T), dim3(256), 0u, st, (const float *)p.Y,
              (const float *)(p.SF > 0 ? p.Ysh : nullptr), (const int32_t *)p.pos, T, k, p.H, p.resid);
   return hipGetLastError();
 }
