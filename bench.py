@@ -125,7 +125,7 @@ def write_traffic(args):
         f.write("\n")
     with open(traffic_path(kernel, args.workload, "md"), "w") as f:
         f.write(f"# HBM traffic per dispatch: {rec['kernel']} ({args.workload})\n\n")
-        f.write("Counter passes, each in its own run (repo root on the GPU box, TMPDIR=/tmp):\n\n")
+        f.write("Counter passes, each in its own run (repo root on the MI355X host, TMPDIR=/tmp):\n\n")
         for c in cmds:
             f.write(f"    {c}\n")
         f.write(f"\nCopy calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE = {cf:.0f} KiB and "

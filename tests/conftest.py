@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu():
-    """Skip unless a GPU is present; on a GPU machine the HIP library must load (no fallback)."""
+    """Skip unless a GPU is present; where one is, the HIP library must load (no fallback)."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
