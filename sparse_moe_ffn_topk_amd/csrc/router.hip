@@ -181,52 +181,53 @@ __global__ __launch_bounds__(256) void k_router_row1(const float *__restrict__ W
 
 // T > 8: logits = x W^T on v_mfma_f64_16x16x4f64 (f32 inputs are exact in
 // f64, so products are exact and sums are f64, as in the row kernel).  A block
-// takes 16 router rows x 32 tokens; wave w the tokens 16 (w & 1) .. +15 over
-// the half w >> 1 of every chunk's columns, so every SIMD of the chip has a
-// wave (split K), with four accumulator chains per wave.  Lane l feeds A =
+// takes 16 router rows x 32 tokens with eight waves: wave w the tokens
+// 16 (w & 1) .. +15 over the quarter w >> 1 of every chunk's columns (split
+// K: two waves per SIMD of the chip), with four accumulator chains per wave.  Lane l feeds A =
 // x[token l%16][h + l/16] and B = W[row l%16][h + l/16] and holds
-// D[token l/16 + 4i][row l%16], i < 4.  The two halves' sums are added in a
-// fixed order (reproducible).  W and x are staged through LDS in chunks of RKT
+// D[token l/16 + 4i][row l%16], i < 4.  The four quarters' sums are added in
+// a fixed order (reproducible).  W and x are staged through LDS in chunks of RKT
 // columns (16-byte loads, next chunk prefetched into registers); columns past
 // H, rows past E and tokens past T read as zeros.
 constexpr int RKT = 128;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
-__global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W, const float *__restrict__ x, int H,
+__global__ __launch_bounds__(512) void k_router_mfma(const float *__restrict__ W, const float *__restrict__ x, int H,
                                                      int E, int T, float *__restrict__ logits) {
   __shared__ __attribute__((aligned(16))) float ws[16][RKT + 4];
   __shared__ __attribute__((aligned(16))) float xs[32][RKT + 4];
-  __shared__ f64x4 red[2][64];
+  __shared__ f64x4 red[3][2][64];  // quarters 1..3
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tg = wave & 1, kh = wave >> 1;
+  const int tg = wave & 1, kh = wave >> 1;  // token group, K quarter
   const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 32;
   const int ne = min(16, E - e0), nt = min(32, T - t0);
   const rsrc_t rW = make_rsrc(W + (size_t)e0 * H, (uint32_t)ne * (uint32_t)H * 4u);
   const rsrc_t rX = make_rsrc(x + (size_t)t0 * H, (uint32_t)nt * (uint32_t)H * 4u);
-  // staging roles: piece q = tid + 256 i of a chunk is row q / 32, 16-byte
-  // column q % 32 (W: i < 2, rows 0..15; x: i < 4, rows 0..31)
+  // staging roles: piece q = tid + 512 i of a chunk is row q / 32, 16-byte
+  // column q % 32 (W: i < 1, rows 0..15; x: i < 2, rows 0..31)
   constexpr int CPR = RKT / 4;  // 16-byte columns per staged row
-  u32x4 wr[16 * CPR / 256], xr[32 * CPR / 256];
+  constexpr int NT = 512;
+  u32x4 wr[16 * CPR / NT], xr[32 * CPR / NT];
   auto issue = [&](int h0) {
 #pragma unroll
-    for (int i = 0; i < 16 * CPR / 256; i++) {
-      const int q = tid + 256 * i, r = q / CPR, h = h0 + 4 * (q % CPR);
+    for (int i = 0; i < 16 * CPR / NT; i++) {
+      const int q = tid + NT * i, r = q / CPR, h = h0 + 4 * (q % CPR);
       wr[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 32 * CPR / 256; i++) {
-      const int q = tid + 256 * i, r = q / CPR, h = h0 + 4 * (q % CPR);
+    for (int i = 0; i < 32 * CPR / NT; i++) {
+      const int q = tid + NT * i, r = q / CPR, h = h0 + 4 * (q % CPR);
       xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, (int)(h < H ? (uint32_t)(r * H + h) * 4u : 0x7ffffff0u), 0, 0);
     }
   };
   auto put = [&]() {
 #pragma unroll
-    for (int i = 0; i < 16 * CPR / 256; i++) {
-      const int q = tid + 256 * i;
+    for (int i = 0; i < 16 * CPR / NT; i++) {
+      const int q = tid + NT * i;
       *reinterpret_cast<u32x4 *>(&ws[q / CPR][4 * (q % CPR)]) = wr[i];
     }
 #pragma unroll
-    for (int i = 0; i < 32 * CPR / 256; i++) {
-      const int q = tid + 256 * i;
+    for (int i = 0; i < 32 * CPR / NT; i++) {
+      const int q = tid + NT * i;
       *reinterpret_cast<u32x4 *>(&xs[q / CPR][4 * (q % CPR)]) = xr[i];
     }
   };
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
     __syncthreads();
     if (h0 + RKT < H) issue(h0 + RKT);
 #pragma unroll
-    for (int kk = kh * (RKT / 2); kk < (kh + 1) * (RKT / 2); kk += 16) {
+    for (int kk = kh * (RKT / 4); kk < (kh + 1) * (RKT / 4); kk += 16) {
 #pragma unroll
       for (int j = 0; j < 4; j++)
         acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xrow[kk + 4 * j + kq], (double)wrow[kk + 4 * j + kq],
@@ -251,10 +252,10 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float *__restrict__ W
     __syncthreads();
   }
   const f64x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  if (kh == 1) red[tg][lane] = sum;
+  if (kh > 0) red[kh - 1][tg][lane] = sum;
   __syncthreads();
   if (kh == 0) {
-    const f64x4 tot = sum + red[tg][lane];
+    const f64x4 tot = ((sum + red[0][tg][lane]) + red[1][tg][lane]) + red[2][tg][lane];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int t = 16 * tg + kq + 4 * i, e = m;
@@ -355,7 +356,7 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
 #undef MOE_ROUTER_ROWS
   } else {
     const dim3 grid((E + 15) / 16, (T + 31) / 32);
-    MOE_LAUNCH(1, k_router_mfma, grid, dim3(256), 0u, st, W, x, H, E, T, logits);
+    MOE_LAUNCH(1, k_router_mfma, grid, dim3(512), 0u, st, W, x, H, E, T, logits);
   }
   return hipGetLastError();
 }
