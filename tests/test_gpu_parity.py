@@ -248,6 +248,22 @@ def test_grouped_down_row_streaming_shapes(gpu, F, SF, qt):
     assert err <= REL_TOL
 
 
+@pytest.mark.parametrize("T", [100, 600])
+def test_row_streaming_many_tiles_and_chunks(gpu, T):
+    # the row-streaming grouped kernels with every token on two experts (a
+    # selection bias forces them): 7 to 32 16-token tiles per expert, and
+    # with T = 600 two chunks of the grouped path one after another
+    wl = S.Workload("rowtiles", 512, 16, 2, 512, 512, S.Q4_1, has_bias=True)
+    _say("row-streaming many tiles per expert, T", T)
+    w, x = _layer(wl, seed=31 + T, tokens=T)
+    w["bias"] = torch.zeros(16)
+    w["bias"][[3, 11]] = 10.0
+    sample = None if T <= 128 else list(range(0, T, 23)) + [T - 1]
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w), sample=sample)
+    print(f"[result] row-streaming many tiles T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
+    assert err <= REL_TOL
+
+
 @pytest.mark.parametrize("name,T", [("lfm25_q8", 1), ("lfm25_q8", 3), ("lfm25_q8", 520)])
 def test_layer_q8_0(gpu, name, T):
     # Q8_0 experts (f16 d, 32 signed bytes; the lfm2_moe_ssd.js page's int8 expert plane), decode and grouped
