@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // waves' partial tiles of a chunk are added in wave order (fixed:
 // reproducible), each wave finishing a quarter of the tile's values (SwiGLU
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
-constexpr int RS_RB = 256;   // rows per block (down)
+constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
 constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
 template <int QT, int KQ>
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   const int r0 = blockIdx.y * RS_GU_RB;
   if (r0 >= R) return;
   const int K = a.H, nbK = 4 * KQ;
-  const uint32_t rowbytes = (uint32_t)nbK * BS, rowdw = rowbytes / 4u;
+  const uint32_t rowbytes = (uint32_t)nbK * BS;
   const uint32_t mbytes = (uint32_t)((size_t)R * rowbytes);
   const rsrc_t rg = make_rsrc(g0, mbytes), ru = make_rsrc(u0, mbytes);
   const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)K * 4u);
@@ -654,30 +654,47 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   }
 }
 
+// LDS of one k_group_down_rows tile (bytes; every part a multiple of 16).
+template <int QT, int KQ>
+struct DownRowsLds {
+  static constexpr int TPC = KQ <= 4 ? 4 : (KQ <= 8 ? 2 : 1);  // 16-row tiles per chunk
+  static constexpr int PADW = KQ * QBlock<QT>::bytes + 4;     // staged row stride, dwords
+  static constexpr size_t bst = 4 * 16 * TPC * PADW;          // staged chunk
+  static constexpr size_t red = 4 * 4 * TPC * 64 * 4;         // waves' partial tiles
+  static constexpr size_t asum = 4 * 4 * KQ * 16;             // input sums per K block
+  static constexpr size_t bytes = bst + red + asum + 3 * 4 * 16;
+};
+
 // Grouped down, row-streaming form (Q4 blocks; K = F or SF of 16..64 blocks,
 // rows a multiple of 16 bytes): as k_group_gateup_rows for one matrix.  A
-// block takes one 16-token tile x 256 rows; a chunk is TPC 16-row tiles of
+// block takes one 16-token tile x rb rows; a chunk is TPC 16-row tiles of
 // whole rows (about 20 KB, one contiguous run); wave w takes K blocks
 // [w KQ, (w+1) KQ) of every tile, with its tokens' act rows held as MFMA A
 // fragments.  The waves' partial tiles are added in wave order and weighted
-// by the pair's routing weight.  Routed and shared tiles run as separate
-// launches (their K differ): tile0 is the first tile index of the launch.
+// by the pair's routing weight.  One block runs tile bx (routed tiles first,
+// then shared ones) over rows [by rb, (by + 1) rb); rb is a multiple of the
+// chunk's rows.
+
 template <int QT, int KQ>
-__global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile0) {
+__device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by, int rb, char *smem) {
   static_assert(KQ <= RS_KQM, "K blocks per wave");
   constexpr int BS = QBlock<QT>::bytes;
-  constexpr int TPC = KQ <= 4 ? 4 : (KQ <= 8 ? 2 : 1);  // 16-row tiles per chunk
-  constexpr int CR = 16 * TPC;                          // rows per chunk
-  constexpr int ROWDW = KQ * 4 * BS / 4;                // dwords of a row
-  constexpr int PADW = ROWDW + 4;                       // staged row stride (a 16-byte pad spreads the banks)
-  __shared__ __attribute__((aligned(16))) uint32_t bst[CR][PADW];
-  __shared__ __attribute__((aligned(16))) float red[4][TPC][64][4];  // [wave][tile][lane][element]
-  __shared__ __attribute__((aligned(16))) float asum[4][KQ][16];
-  __shared__ int rowid[16], outid[16];
-  __shared__ float outw[16];
+  constexpr int TPC = DownRowsLds<QT, KQ>::TPC;  // 16-row tiles per chunk
+  constexpr int CR = 16 * TPC;                   // rows per chunk
+  constexpr int ROWDW = KQ * 4 * BS / 4;         // dwords of a row
+  constexpr int PADW = ROWDW + 4;                // staged row stride (a 16-byte pad spreads the banks)
+  static_assert(PADW == DownRowsLds<QT, KQ>::PADW, "row stride");
+  // LDS, carved from the kernel's buffer (16-byte aligned; every part a multiple of 16 bytes)
+  auto &bst = *reinterpret_cast<uint32_t (*)[CR][PADW]>(smem);
+  auto &red = *reinterpret_cast<float (*)[4][TPC][64][4]>(smem + DownRowsLds<QT, KQ>::bst);  // [wave][tile][lane][element]
+  auto &asum = *reinterpret_cast<float (*)[4][KQ][16]>(smem + DownRowsLds<QT, KQ>::bst + DownRowsLds<QT, KQ>::red);
+  int *rowid = reinterpret_cast<int *>(smem + DownRowsLds<QT, KQ>::bst + DownRowsLds<QT, KQ>::red +
+                                       DownRowsLds<QT, KQ>::asum);
+  int *outid = rowid + 16;
+  float *outw = reinterpret_cast<float *>(rowid + 32);
+  static_assert(DownRowsLds<QT, KQ>::bst % 16 == 0 && DownRowsLds<QT, KQ>::red % 16 == 0, "alignment");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bx = (int)blockIdx.x + tile0;
   const bool shared = bx >= a.max_routed_tiles;
   int e = 0, first = 0, ntok, K;
   const int R = a.H;
@@ -702,7 +719,7 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile
     outid[tid] = ok ? q : -1;
     outw[tid] = ok && !shared ? a.wts[a.perm[q]] : 1.f;
   }
-  const int r0 = blockIdx.y * RS_RB;
+  const int r0 = by * rb;
   if (r0 >= R) return;
   const uint32_t rowbytes = (uint32_t)(4 * KQ) * BS;
   const rsrc_t rw = make_rsrc(m0p, (uint32_t)((size_t)R * rowbytes));
@@ -777,7 +794,7 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile
     }
   };
 
-  const int nch = (min(RS_RB, R - r0) + CR - 1) / CR;
+  const int nch = (min(rb, R - r0) + CR - 1) / CR;
   issue(0);
   for (int c = 0; c < nch; c++) {
     stage();
@@ -821,6 +838,25 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int tile
   }
 }
 
+// Grouped down, both kinds of tile in one launch: the first ns blocks take
+// the shared tiles (K = SF, KQS blocks per wave, rbs rows each), so that
+// their longer blocks start first and overlap the routed ones (K = F, KQF
+// blocks per wave, RS_RB rows each) that follow.  KQF or KQS is 0 where the
+// layer has no routed or no shared expert.
+template <int QT, int KQF, int KQS>
+__global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles, int rbs) {
+  constexpr size_t lf = KQF > 0 ? DownRowsLds<QT, KQF>::bytes : 0, ls = KQS > 0 ? DownRowsLds<QT, KQS>::bytes : 0;
+  __shared__ __attribute__((aligned(16))) char smem[lf > ls ? lf : (ls > 0 ? ls : 16)];  // one tile's LDS, either kind
+  const int b = (int)blockIdx.x;
+  const int ns = KQS > 0 ? shtiles * ((a.H + rbs - 1) / rbs) : 0;
+  if (b < ns) {
+    if constexpr (KQS > 0) down_rows_tile<QT, KQS>(a, a.max_routed_tiles + b % shtiles, b / shtiles, rbs, smem);
+  } else {
+    const int r = b - ns;
+    if constexpr (KQF > 0) down_rows_tile<QT, KQF>(a, r % a.max_routed_tiles, r / a.max_routed_tiles, RS_RB, smem);
+  }
+}
+
 // resid[t][h] += sum_j Y[pos(t, j)][h] + Ysh[t][h], the same order for every
 // element; each thread takes four consecutive h (16-byte loads; H % 32 == 0).
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, const float *__restrict__ Ysh,
@@ -855,6 +891,30 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, co
 // ---------------------------------------------------------------- launch --
 
 size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * (4 + 2); }
+
+template <int QT, int KQF>
+static void launch_down_rows_s(int kqs, const GemmArgs &g, int shtiles, int rbs, int nblk, hipStream_t st) {
+  switch (kqs) {
+    case 0: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 0>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
+    case 4: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 4>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
+    case 8: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 8>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
+    case 12: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 12>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
+    default: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 16>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
+  }
+}
+
+// K blocks per wave of the routed (kqf) and shared (kqs) down matrices: 0
+// (none), 4, 8, 12 or 16.
+template <int QT>
+static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, int rbs, int nblk, hipStream_t st) {
+  switch (kqf) {
+    case 0: launch_down_rows_s<QT, 0>(kqs, g, shtiles, rbs, nblk, st); break;
+    case 4: launch_down_rows_s<QT, 4>(kqs, g, shtiles, rbs, nblk, st); break;
+    case 8: launch_down_rows_s<QT, 8>(kqs, g, shtiles, rbs, nblk, st); break;
+    case 12: launch_down_rows_s<QT, 12>(kqs, g, shtiles, rbs, nblk, st); break;
+    default: launch_down_rows_s<QT, 16>(kqs, g, shtiles, rbs, nblk, st); break;
+  }
+}
 
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
@@ -928,31 +988,14 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int nbF = k > 0 ? p.F / 32 : 0, nbS = p.SF / 32;
   auto rowable = [](int nb) { return nb % 16 == 0 && nb <= 4 * RS_KQM; };
   if (p.qtype != MOE_Q8_0 && (nbF == 0 || rowable(nbF)) && (nbS == 0 || rowable(nbS))) {
-    // row-streaming form: routed tiles, then shared tiles, one launch each
-    const int ys = (p.H + RS_RB - 1) / RS_RB;
-#define MOE_DR_LAUNCH(QT, NB, NTILES, T0)                                                                    \
-  switch ((NB) / 4) {                                                                                       \
-    case 4: MOE_LAUNCH(7, (k_group_down_rows<QT, 4>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break;   \
-    case 8: MOE_LAUNCH(7, (k_group_down_rows<QT, 8>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break;   \
-    case 12: MOE_LAUNCH(7, (k_group_down_rows<QT, 12>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break; \
-    default: MOE_LAUNCH(7, (k_group_down_rows<QT, 16>), dim3(NTILES, ys), dim3(256), 0u, st, g, T0); break; \
-  }
-    if (nbF > 0) {
-      if (p.qtype == MOE_Q4_1) {
-        MOE_DR_LAUNCH(MOE_Q4_1, nbF, g.max_routed_tiles, 0)
-      } else {
-        MOE_DR_LAUNCH(MOE_Q4_0, nbF, g.max_routed_tiles, 0)
-      }
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
-    if (shtiles > 0) {
-      if (p.qtype == MOE_Q4_1) {
-        MOE_DR_LAUNCH(MOE_Q4_1, nbS, shtiles, g.max_routed_tiles)
-      } else {
-        MOE_DR_LAUNCH(MOE_Q4_0, nbS, shtiles, g.max_routed_tiles)
-      }
-    }
-#undef MOE_DR_LAUNCH
+    // row-streaming form: shared tiles (64 rows a block), then routed tiles, in one launch
+    const int rbs = 64;
+    const int nblk = (shtiles > 0 ? shtiles * ((p.H + rbs - 1) / rbs) : 0) +
+                     (nbF > 0 ? g.max_routed_tiles * ((p.H + RS_RB - 1) / RS_RB) : 0);
+    if (nblk > 0 && p.qtype == MOE_Q4_1)
+      launch_down_rows<MOE_Q4_1>(nbF / 4, nbS / 4, g, shtiles, rbs, nblk, st);
+    else if (nblk > 0)
+      launch_down_rows<MOE_Q4_0>(nbF / 4, nbS / 4, g, shtiles, rbs, nblk, st);
   } else {
     dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
     if (p.qtype == MOE_Q4_1)
