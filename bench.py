@@ -306,12 +306,12 @@ def main():
                   (("router", moe.KERNEL_ROUTER), ("down_accum", moe.KERNEL_DOWN))
                   + ((("prelude", moe.KERNEL_PRELUDE),) if T > 1 else ()))
         for name, kid in ((dominant[1], dominant[0]),) + others:
-            with moe.KernelTimer(kid, 2 * nk * L) as kt:  # (up to two launches per layer)
+            with moe.KernelTimer(kid, 2 * nk * L) as kt:  # (room for two launches per layer)
                 for i in range(nk):
                     stacks[i % nS].step()
                 torch.cuda.synchronize()
-            # (mean per launch, and the kernel's time per layer step: the grouped down runs as
-            # two launches, routed and shared tiles, where its row-streaming form applies)
+            # (mean per launch, and the kernel's time per layer step: the two differ where a
+            # kernel runs more than once per layer)
             kstats[name] = {"launches": kt.count, "mean_us": kt.mean_us,
                             "us_per_layer": 1000.0 * kt.total_ms / (nk * L)}
         log("kernel means (us, eager dispatches): " + ", ".join(f"{k}={v['mean_us']:.2f}" for k, v in kstats.items()))
