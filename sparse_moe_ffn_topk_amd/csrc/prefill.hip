@@ -486,6 +486,9 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // waves' partial tiles of a chunk are added in wave order (fixed:
 // reproducible), each wave finishing a quarter of the tile's values (SwiGLU
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
+// The grid is one-dimensional: the shared expert's tiles x row slices come
+// first, then the routed tiles x the routed row slices, so no block is
+// launched for a slice past a matrix's rows.
 constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
 constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
@@ -501,8 +504,11 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   __shared__ int rowid[16], outid[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int bx = blockIdx.x;
-  const bool shared = bx >= a.max_routed_tiles;
+  const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0, b = (int)blockIdx.x;
+  const int ns = shtiles * ((a.SF + RS_GU_RB - 1) / RS_GU_RB);
+  const bool shared = b < ns;
+  const int bx = shared ? a.max_routed_tiles + b % shtiles : (b - ns) % a.max_routed_tiles;
+  const int by = shared ? b / shtiles : (b - ns) / a.max_routed_tiles;
   int e = 0, first = 0, ntok, R;
   const uint8_t *g0, *u0;
   if (!shared) {
@@ -527,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     rowid[tid] = ok ? (shared ? q : a.perm[q] / a.k) : -1;
     outid[tid] = ok ? q : -1;
   }
-  const int r0 = blockIdx.y * RS_GU_RB;
+  const int r0 = by * RS_GU_RB;
   if (r0 >= R) return;
   const int K = a.H, nbK = 4 * KQ;
   const uint32_t rowbytes = (uint32_t)nbK * BS;
@@ -957,7 +963,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     const int nbH = p.H / 32;
     // row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks (whole 16-byte pieces)
     const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
-    if (rowform) grid.y = (rows + RS_GU_RB - 1) / RS_GU_RB;
+    if (rowform)  // (shared tiles x slices, then routed tiles x slices)
+      grid = dim3(shtiles * ((p.SF + RS_GU_RB - 1) / RS_GU_RB) +
+                  (k > 0 && p.F > 0 ? g.max_routed_tiles * ((p.F + RS_GU_RB - 1) / RS_GU_RB) : 0));
 #define MOE_RS_LAUNCH(QT)                                                                                \
   switch (nbH / 4) {                                                                                     \
     case 4: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 4>), grid, dim3(256), 0u, st, g); break;             \
