@@ -488,10 +488,22 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
 // The grid is one-dimensional: the shared expert's tiles x row slices come
 // first, then the routed tiles x the routed row slices, so no block is
-// launched for a slice past a matrix's rows.
+// launched for a slice past a matrix's rows.  Within each part, work is
+// ordered slice-major and dealt to the XCDs in runs (xcd_run): one XCD
+// takes every tile of a shared slice, and an expert's tiles share an L2.
 constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
 constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
+
+// Blocks are dealt to the chip's eight XCDs (each with its own L2) in turn:
+// block i runs on XCD i % 8.  For i in [0, n) this returns a work index in
+// [0, n), one to one, such that the blocks of XCD x take the contiguous run
+// [x q + min(x, r), ...) of work indices (q = n / 8, r = n % 8), so tiles
+// that read the same rows run behind one L2.
+__device__ __forceinline__ int xcd_run(int i, int n) {
+  const int x = i & 7, q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + (i >> 3);
+}
 template <int QT, int KQ>
 __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   static_assert(KQ <= RS_KQM, "K blocks per wave");
@@ -507,8 +519,20 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0, b = (int)blockIdx.x;
   const int ns = shtiles * ((a.SF + RS_GU_RB - 1) / RS_GU_RB);
   const bool shared = b < ns;
-  const int bx = shared ? a.max_routed_tiles + b % shtiles : (b - ns) % a.max_routed_tiles;
-  const int by = shared ? b / shtiles : (b - ns) / a.max_routed_tiles;
+  int bx, by;
+  if (shared) {
+    const int l = xcd_run(b, ns);
+    bx = a.max_routed_tiles + l % shtiles;
+    by = l / shtiles;
+  } else {
+    // routed: only the ntiles tiles the sort produced, times the F slices
+    const int nt = __builtin_amdgcn_readfirstlane(*a.ntiles);
+    const int v = nt * ((a.F + RS_GU_RB - 1) / RS_GU_RB);
+    if (b - ns >= v) return;
+    const int l = xcd_run(b - ns, v);
+    bx = l % nt;
+    by = l / nt;
+  }
   int e = 0, first = 0, ntok, R;
   const uint8_t *g0, *u0;
   if (!shared) {
@@ -848,7 +872,8 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
 // the shared tiles (K = SF, KQS blocks per wave, rbs rows each), so that
 // their longer blocks start first and overlap the routed ones (K = F, KQF
 // blocks per wave, RS_RB rows each) that follow.  KQF or KQS is 0 where the
-// layer has no routed or no shared expert.
+// layer has no routed or no shared expert.  Each part is dealt to the XCDs
+// in slice-major runs, as in k_group_gateup_rows.
 template <int QT, int KQF, int KQS>
 __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles, int rbs) {
   constexpr size_t lf = KQF > 0 ? DownRowsLds<QT, KQF>::bytes : 0, ls = KQS > 0 ? DownRowsLds<QT, KQS>::bytes : 0;
@@ -856,10 +881,19 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shti
   const int b = (int)blockIdx.x;
   const int ns = KQS > 0 ? shtiles * ((a.H + rbs - 1) / rbs) : 0;
   if (b < ns) {
-    if constexpr (KQS > 0) down_rows_tile<QT, KQS>(a, a.max_routed_tiles + b % shtiles, b / shtiles, rbs, smem);
+    if constexpr (KQS > 0) {
+      const int l = xcd_run(b, ns);
+      down_rows_tile<QT, KQS>(a, a.max_routed_tiles + l % shtiles, l / shtiles, rbs, smem);
+    }
   } else {
-    const int r = b - ns;
-    if constexpr (KQF > 0) down_rows_tile<QT, KQF>(a, r % a.max_routed_tiles, r / a.max_routed_tiles, RS_RB, smem);
+    if constexpr (KQF > 0) {
+      // routed: only the ntiles tiles the sort produced, times the H slices
+      const int nt = __builtin_amdgcn_readfirstlane(*a.ntiles);
+      const int v = nt * ((a.H + RS_RB - 1) / RS_RB);
+      if (b - ns >= v) return;
+      const int l = xcd_run(b - ns, v);
+      down_rows_tile<QT, KQF>(a, l % nt, l / nt, RS_RB, smem);
+    }
   }
 }
 
