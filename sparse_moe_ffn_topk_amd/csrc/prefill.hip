@@ -1030,8 +1030,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int nbF = k > 0 ? p.F / 32 : 0, nbS = p.SF / 32;
   auto rowable = [](int nb) { return nb % 16 == 0 && nb <= 4 * RS_KQM; };
   if (p.qtype != MOE_Q8_0 && (nbF == 0 || rowable(nbF)) && (nbS == 0 || rowable(nbS))) {
-    // row-streaming form: shared tiles (64 rows a block), then routed tiles, in one launch
-    const int rbs = 64;
+    // row-streaming form: shared tiles (128 rows a block), then routed tiles, in one launch
+    const int rbs = 128;
     const int nblk = (shtiles > 0 ? shtiles * ((p.H + rbs - 1) / rbs) : 0) +
                      (nbF > 0 ? g.max_routed_tiles * ((p.H + RS_RB - 1) / RS_RB) : 0);
     if (nblk > 0 && p.qtype == MOE_Q4_1)
