@@ -139,6 +139,288 @@ def write_traffic(args):
     print(json.dumps(rec))
 
 
+def stream_peak(moe, torch, reps=5, gib=4):
+    """Achievable streaming-read rate: the probe kernel reading `gib` GiB with 16-byte loads, for a few grid
+    sizes; returns (best median GB/s, {blocks: median GB/s})."""
+    import ctypes as C
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    L = moe.load_library()
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        L.moe_probe_stream(C.c_void_p(buf.data_ptr()), nbytes, blocks, None, st)  # warm
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = L.moe_probe_stream(C.c_void_p(buf.data_ptr()), nbytes, blocks, None, st)
+            b.record()
+            torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"moe_probe_stream rc {rc}")
+            times.append(a.elapsed_time(b))
+        times.sort()
+        res[blocks] = nbytes / (times[len(times) // 2] * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return max(res.values()), res
+
+
+def run_probes(args):
+    """Chip probes: the achievable streaming rate, the per-launch floor of a streaming kernel, the kernel
+    boundary in a graph, and the cost of an in-kernel all-to-all exchange between blocks."""
+    import ctypes as C
+
+    import torch
+
+    import sparse_moe_ffn_topk_amd as moe
+    L = moe.load_library()
+    out = {"probe": "mi355x"}
+    peak, by_blocks = stream_peak(moe, torch)
+    out["stream_4GiB_GBps"] = round(peak, 1)
+    out["stream_4GiB_by_blocks"] = {str(k): round(v, 1) for k, v in by_blocks.items()}
+    log(f"streaming read of 4 GiB: {peak:.1f} GB/s (best grid); by blocks {out['stream_4GiB_by_blocks']}")
+
+    # per-launch floor: N launches over distinct regions of a 4 GiB ring (far beyond the 256 MB MALL, so a
+    # launch never finds its bytes cached), captured as one graph and replayed
+    ring = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    base = ring.data_ptr()
+    floor = {}
+    for mb in (2, 5, 10, 17.8, 20):
+        nbytes = int(mb * 1e6) // 16 * 16
+        stride = (nbytes + 4095) // 4096 * 4096
+        per = (4 << 30) // stride
+        n = min(per, max(100, -(-(1 << 30) // nbytes)))  # at least 1 GiB of distinct regions per graph
+        best = None
+        for blocks in (256, 512, 1024, 2048):
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for i in range(3):
+                    L.moe_probe_stream(C.c_void_p(base + (i % per) * stride), nbytes, blocks, None,
+                                       C.c_void_p(s.cuda_stream))
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(n):
+                        L.moe_probe_stream(C.c_void_p(base + (i % per) * stride), nbytes, blocks, None,
+                                           C.c_void_p(s.cuda_stream))
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (5 * n)
+            if best is None or us < best[0]:
+                best = (us, blocks)
+            del g
+        floor[str(mb)] = {"us_per_launch": round(best[0], 3), "blocks": best[1],
+                          "GBps": round(nbytes / (best[0] * 1e-6) / 1e9, 1)}
+        log(f"per-launch floor {mb} MB: {best[0]:.2f} us ({best[1]} blocks, {floor[str(mb)]['GBps']} GB/s)")
+    out["launch_floor"] = floor
+    del ring
+    torch.cuda.empty_cache()
+
+    # kernel boundary: empty kernels back to back in a graph
+    gaps = {}
+    n = 200
+    for blocks in (1, 256, 1024):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            L.moe_probe_empty(blocks, C.c_void_p(s.cuda_stream))
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(n):
+                    L.moe_probe_empty(blocks, C.c_void_p(s.cuda_stream))
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gaps[str(blocks)] = round(a.elapsed_time(b) * 1e3 / (10 * n), 3)
+        del g
+    out["empty_kernel_us_in_graph"] = gaps
+    log(f"empty kernels in a graph, us per launch by blocks: {gaps}")
+
+    # in-kernel all-to-all exchange between co-resident blocks (bounded waits)
+    ex = {}
+    rounds = 2000
+    for blocks in (8, 64, 256, 512):
+        slots = torch.zeros(blocks, dtype=torch.int64, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        cyc = torch.zeros(2, dtype=torch.int64, device="cuda")
+        rc = L.moe_probe_exchange(blocks, rounds, 20000, C.c_void_p(slots.data_ptr()), C.c_void_p(status.data_ptr()),
+                                  C.c_void_p(cyc.data_ptr()), C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        if rc:
+            ex[str(blocks)] = {"error": f"launch rc {rc}"}
+            continue
+        c = cyc.cpu().tolist()
+        ok = int(status.item()) == 0
+        ex[str(blocks)] = {"us_per_round": round((c[1] - c[0]) * 0.01 / rounds, 3), "completed": ok}
+    out["exchange_all_to_all"] = ex
+    log(f"all-to-all exchange, us per round by blocks: {ex}")
+    print(json.dumps(out), flush=True)
+    if args.probe_out:
+        write_probe_md(out, args.probe_out)
+
+
+def write_probe_md(d, path):
+    with open(path, "w") as f:
+        f.write("# Chip probes: streaming rate, launch floor, kernel boundary, in-kernel exchange (MI355X)\n\n")
+        f.write("Command (repo root on the MI355X host):\n\n    python bench.py --probe --probe-out " + path + "\n\n")
+        f.write(f"Streaming read of 4 GiB with 16-byte loads (best grid, median of 5): "
+                f"**{d['stream_4GiB_GBps']} GB/s** ({100 * d['stream_4GiB_GBps'] / HBM_PEAK_GBPS:.1f} % of 8 TB/s); "
+                f"by blocks of 256 threads: {d['stream_4GiB_by_blocks']}.\n\n")
+        f.write("Per-launch floor: launches of the streaming kernel, each over a distinct region of a 4 GiB ring, "
+                "at least 100 and at least 1 GiB of regions per graph (so no launch finds its bytes in the 256 MB "
+                "MALL), captured in one graph and replayed 5 times; best grid of 256-2048 blocks.\n\n| MB per launch | us per launch | blocks | GB/s |\n|---|---|---|---|\n")
+        for mb, v in d["launch_floor"].items():
+            f.write(f"| {mb} | {v['us_per_launch']} | {v['blocks']} | {v['GBps']} |\n")
+        f.write("\nEmpty kernels back to back in a graph, us per launch (by blocks of 64 threads): "
+                f"{d['empty_kernel_us_in_graph']}.\n\n")
+        f.write("In-kernel all-to-all exchange (cooperative launch, blocks of 256 threads, 2000 rounds; each round "
+                "every block publishes a 64-bit word with a device-scope store and waits until every block's word "
+                "of the round is visible through device-scope loads):\n\n| blocks | us per round | completed |\n"
+                "|---|---|---|\n")
+        for b, v in d["exchange_all_to_all"].items():
+            f.write(f"| {b} | {v.get('us_per_round', '-')} | {v.get('completed', v.get('error'))} |\n")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_leg(args, wl, cfg, layers, xs, resid, ws, L, T):
+    """The f64 oracle on the host cores, on the same inputs as one GPU step.
+
+    One eager step on the GPU records every layer's input and FFN output (the chained stack: the running
+    residual before and after the layer).  The oracle then recomputes each layer from the GPU's own input:
+    that gives the parity figures (max row relative error of the FFN delta, ids bit-exact up to certified
+    near-ties) and the timing.  Timing: one thread over the whole step (every layer, every token), and
+    N threads running the same work concurrently (N sequences, one per thread), median of 3 each.  Where a
+    whole step would take longer than the budget, a token sample of every layer is run and scaled."""
+    import concurrent.futures as cf
+
+    import numpy as np
+    import torch
+
+    import moe_synth as S
+    import oracle as O
+    import sparse_moe_ffn_topk_amd as moe
+
+    ocfg = O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
+                      wl.groups_used, wl.weights_scale, swiglu_limit=wl.swiglu_limit,
+                      swiglu_limit_shared=wl.swiglu_limit_shared, norm_eps=float(np.float32(wl.norm_eps or 1e-5)))
+    # one eager step on the GPU, layer by layer, inputs and outputs kept
+    k = max(wl.top_k, 1)
+    ids_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    h = resid.clone()
+    rec = []
+    for l in range(L):
+        if args.chained:
+            x_in = h.cpu().numpy().copy()
+            moe.layer_step(cfg, layers[l], h, h, ids_d, wts_d, workspace=ws)
+            torch.cuda.synchronize()
+            rec.append((x_in, h.cpu().numpy() - x_in, ids_d.cpu().numpy().copy()))
+        else:
+            x_l = xs[0][l]
+            out = torch.zeros_like(x_l)
+            moe.layer_step(cfg, layers[l], x_l, out, ids_d, wts_d, workspace=ws)
+            torch.cuda.synchronize()
+            rec.append((x_l.cpu().numpy(), out.cpu().numpy(), ids_d.cpu().numpy().copy()))
+    t_copy = time.perf_counter()
+    host = [S.to_numpy(w) for w in layers]
+    log(f"cpu leg: {L} layers copied to the host in {time.perf_counter() - t_copy:.1f}s")
+
+    # tokens per layer: all of them unless one thread would exceed the budget
+    t0 = time.perf_counter()
+    O.layer(ocfg, host[0], rec[0][0][:1])
+    per_tl = time.perf_counter() - t0
+    n_tok = max(1, min(T, int(args.cpu_seconds / 4 / (per_tl * L))))
+    rows = np.unique(np.linspace(0, T - 1, n_tok).round().astype(int))
+    n_tok = len(rows)
+
+    def one_pass():
+        res = []
+        for l in range(L):
+            res.append(O.layer(ocfg, host[l], rec[l][0][rows]))
+        return res
+
+    t1s, results = [], None
+    for rep in range(3):
+        c0 = time.perf_counter()
+        results = one_pass()
+        t1s.append(time.perf_counter() - c0)
+        if t1s[-1] > args.cpu_seconds / 3:
+            break
+    t1 = sorted(t1s)[len(t1s) // 2]
+    N = max(1, min(16, os.cpu_count() or 1))
+    tNs = []
+    for rep in range(3):
+        c0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(N) as ex:
+            list(ex.map(lambda _: one_pass(), range(N)))
+        tNs.append(time.perf_counter() - c0)
+        if tNs[-1] > args.cpu_seconds / 3:
+            break
+    tN = sorted(tNs)[len(tNs) // 2]
+    scale = T / n_tok
+    oracle_1t_s = t1 * scale                    # one full step (T tokens, L layers) on one thread
+    oracle_Nt_s = tN * scale / N                # the same, amortised over N concurrent sequences
+    cpu = {"value": round(T / oracle_Nt_s, 4), "unit": "tokens/s", "cores": N, "kind": "oracle",
+           "sample": (f"one full step ({L} layers x {T} tokens)" if n_tok == T else
+                      f"{n_tok} of the {T} tokens of every layer ({L} layers), scaled x{scale:g}")
+                     + f"; 1 thread and {N} threads each running that work concurrently, median of "
+                       f"{len(t1s)} / {len(tNs)}",
+           "value_1thread": round(T / oracle_1t_s, 4), "oracle_1t_s": round(oracle_1t_s, 4),
+           "oracle_Nt_s": round(oracle_Nt_s, 4), "N": N, "cpu": cpu_model()}
+    log(f"cpu baseline: 1 thread {oracle_1t_s:.3f} s per step ({cpu['value_1thread']} tok/s), {N} threads "
+        f"{cpu['value']} tok/s; {cpu['cpu']}")
+
+    # parity of the GPU step against the oracle, layer by layer on the GPU's own inputs
+    worst, mism, ties = 0.0, 0, 0
+    for l in range(L):
+        ref, ids_ref, _ = results[l]
+        x_in, delta, ids_g = rec[l]
+        x_in, delta, ids_g = x_in[rows], delta[rows], ids_g[rows]
+        ref_delta = ref - (x_in if args.chained else 0.0)
+        for i in range(len(rows)):
+            if wl.top_k > 0 and not np.array_equal(ids_g[i], ids_ref[i]):
+                mism += 1
+                xn = O.rmsnorm(x_in[i], host[l]["ffn_norm"], ocfg.norm_eps) if args.chained else x_in[i]
+                sc = 1.0 / (1.0 + np.exp(-O.router_logits(host[l]["router_w"], xn)))
+                if host[l].get("bias") is not None:
+                    sc = sc + host[l]["bias"].astype(np.float64)
+                dis = sorted(set(ids_g[i].tolist()) ^ set(ids_ref[i].tolist())) or \
+                    [int(a) for a, b in zip(ids_g[i], ids_ref[i]) if a != b]
+                if max(sc[dis]) - min(sc[dis]) < 1e-6:
+                    ties += 1
+                continue  # (the output under another routing is not comparable)
+            e = np.abs(delta[i] - ref_delta[i]).max() / max(np.abs(ref_delta[i]).max(), 1e-300)
+            worst = max(worst, float(e))
+    parity = {"max_rel_err": float(f"{worst:.3e}"), "ids_match": mism == 0, "ids_mismatch_tokens": mism,
+              "near_ties": ties, "checked": f"{L} layers x {n_tok} tokens, each layer on the GPU's own input"}
+    log(f"parity vs oracle: {parity}")
+    return cpu, parity
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +446,11 @@ def main():
                     help="write profiles/<kernel>_<workload>_traffic.{json,md} from rocprofv3 --pmc output folders "
                          "(runs nothing on the GPU)")
     ap.add_argument("--traffic-commands", nargs="*", help="the commands that made the --write-traffic folders")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the chip probes (streaming rate, per-launch floor, kernel boundary, in-kernel "
+                         "exchange) and print them as one JSON line")
+    ap.add_argument("--probe-out", help="with --probe: also write this markdown summary (e.g. profiles/...)")
+    ap.add_argument("--no-stream-peak", action="store_true", help="skip the measured streaming peak")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 8 device-to-device copies of 1 GiB (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -187,6 +474,9 @@ def main():
         sys.exit(1)
     moe.load_library()
     dev = "cuda"
+    if args.probe:
+        run_probes(args)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -348,24 +638,14 @@ def main():
                     "algorithmic_bytes_per_launch": int(per_launch),
                     "mean_launch_us": round(kstats["gateup_swiglu"]["mean_us"], 3)}
 
-    cpu = None
+    peak = None
+    if not args.no_stream_peak:
+        peak, _ = stream_peak(moe, torch)
+        log(f"measured streaming peak (4 GiB, 16-byte loads): {peak:.1f} GB/s")
+
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        import oracle as O
-        nl = min(3, L)
-        host = [S.to_numpy(layers[l]) for l in range(nl)]
-        xh = [xs[0][l].cpu().numpy() for l in range(nl)]
-        ocfg = O.make_cfg(wl.hidden, wl.n_experts, wl.top_k, wl.expert_ff, wl.shared_ff, wl.qtype, wl.n_groups,
-                          wl.groups_used, wl.weights_scale)
-        log(f"cpu baseline: f64 oracle, 1 thread, ~{args.cpu_seconds:.0f}s")
-        n, c0 = 0, time.perf_counter()
-        while n < nl or time.perf_counter() - c0 < args.cpu_seconds:
-            O.layer(ocfg, host[n % nl], xh[n % nl])
-            n += 1
-        per_layer = (time.perf_counter() - c0) / n
-        cpu = {"value": round(T / (per_layer * L), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{n} oracle layer-steps (T={T}) cycling {nl} of the {L} generated layers, "
-                         f"{per_layer * 1e3:.1f} ms each, scaled to the {L}-layer stack"}
-        log(f"cpu baseline: {per_layer * 1e3:.1f} ms per layer-step -> {cpu['value']} tok/s")
+        cpu, parity = cpu_leg(args, wl, cfg, layers, xs, resid, ws, L, T)
 
     out = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -381,7 +661,9 @@ def main():
         "us_per_layer": round(ms_step * 1e3 / L, 3), "tok_s_per_layer": round(tok_s * L, 1),
         "weight_bytes_per_step": int(mean_bytes), "kernels_us": {k: round(v["mean_us"], 3) for k, v in kstats.items()},
         "kernels_us_per_layer": {k: round(v["us_per_layer"], 3) for k, v in kstats.items()},
-        "roofline": roofline, "cpu_baseline": cpu,
+        "roofline": roofline, "cpu_baseline": cpu, "parity": parity,
+        "measured_peak_GBps": None if peak is None else round(peak, 1),
+        "pct_measured_peak": None if peak is None else round(100 * gbps / peak, 2),
     }
     print(json.dumps(out), flush=True)
 

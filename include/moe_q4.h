@@ -162,13 +162,39 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
  *   layers:      host array of L weight sets
  *   x:           host array of L device pointers, each [T][H] f32
  *   ids_out / weights_out: [L][T][k] or NULL
- * The workspace is reused by every layer (moe_workspace_bytes(cfg, T)). */
+ * The workspace is reused by every layer (moe_workspace_bytes(cfg, T)).
+ * Every layer's arguments are checked before the first layer is enqueued, so
+ * an invalid layer l returns an error naming it with nothing enqueued. */
 int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32_t L, const float *const *x,
                    int32_t T, float *resid, int32_t *ids_out, float *weights_out, void *workspace,
                    size_t workspace_bytes, moe_stream_t stream);
 
-/* Message for the last non-zero return on this thread ("" if none). */
+/* Message for the last non-zero return on this thread ("" if none).  This is
+ * the C form of the pages' error convention: their engines refuse a model
+ * shape or setting they do not implement by throwing an Error whose message
+ * names the offending value (flint_moe_ssd.js page, configFromGgufFlint;
+ * lfm2_moe_ssd.js page, initBuffers with its top-k and expert-count limits).
+ * Here the call returns a MOE_E* code instead and this string carries the
+ * message. */
 const char *moe_last_error(void);
+
+/* Diagnostics: where, in a workspace of moe_workspace_bytes(cfg, T) bytes, a
+ * call over T tokens leaves an intermediate result (tests read them back).
+ *   MOE_WS_IDS, MOE_WS_WEIGHTS: [T][k] routing of moe_layer_step when its
+ *     ids_out / weights_out are NULL;
+ *   grouped path only (T > moe_decode_max_tokens(), or shapes whose act row
+ *   does not fit the decode kernels), for the last chunk of at most 512
+ *   tokens: MOE_WS_OFFSETS [E+1] int32 (expert e's pairs are sorted positions
+ *   offsets[e] .. offsets[e+1]-1), MOE_WS_PERM [Tc*k] int32 (the pair
+ *   p = t*k + j at each sorted position; pairs ascend within an expert),
+ *   MOE_WS_POS [Tc*k] int32 (the inverse of perm), MOE_WS_TILES [n][2] int32
+ *   (expert, first position within it, of each 16-pair tile) and
+ *   MOE_WS_NTILES (n, one int32).
+ * Writes the byte offset and size; MOE_EINVAL if the region is not used for
+ * this configuration and T. */
+enum { MOE_WS_IDS = 1, MOE_WS_WEIGHTS = 2, MOE_WS_OFFSETS = 3, MOE_WS_PERM = 4, MOE_WS_POS = 5,
+       MOE_WS_TILES = 6, MOE_WS_NTILES = 7 };
+int moe_workspace_region(const moe_config *cfg, int32_t T, int32_t region, size_t *offset, size_t *bytes);
 
 /* Largest T that takes the decode (GEMV) path; larger T takes the grouped
  * GEMM path. */
@@ -196,6 +222,28 @@ enum {
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
 int moe_kernel_timer_end(int32_t *count, double *total_ms);
+
+/* Probes of the chip (diagnostics; no part of the MoE step uses them).  They
+ * measure what bounds the decode path: the rate of a plain streaming read,
+ * the cost of a kernel boundary and the cost of an exchange between blocks
+ * of one kernel across the XCDs.  Return MOE_OK, MOE_EINVAL or MOE_ELAUNCH.
+ *   moe_probe_stream:   one launch of `blocks` x 256 threads reading `bytes`
+ *                       (a multiple of 16, 16-byte aligned) of buf with
+ *                       16-byte loads; sink (>= 256 words, or NULL) is
+ *                       never written in practice.
+ *   moe_probe_empty:    one launch of an empty kernel of `blocks` x 64.
+ *   moe_probe_exchange: a cooperative launch of `blocks` x 256 threads that
+ *                       run `rounds` all-to-all exchanges through slots
+ *                       ([blocks] 64-bit words, zero before the launch):
+ *                       each block publishes a word per round, then waits
+ *                       until every block's word of that round is visible.
+ *                       A wait that reads one slot spin_limit times gives up
+ *                       and sets status[0] = 1.  cycles[0..1]: the 100 MHz
+ *                       real-time counter at the start and end (block 0). */
+int moe_probe_stream(const void *buf, size_t bytes, int32_t blocks, uint32_t *sink, moe_stream_t stream);
+int moe_probe_empty(int32_t blocks, moe_stream_t stream);
+int moe_probe_exchange(int32_t blocks, int32_t rounds, uint32_t spin_limit, void *slots, uint32_t *status,
+                       unsigned long long *cycles, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

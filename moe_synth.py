@@ -50,6 +50,13 @@ class Workload:
     bias_std: float = 0.1
     scale_lo: float = 0.001
     scale_hi: float = 0.02
+    # wide-range variants (off by default): d (and Q4_1 m) of either sign, m ~ U(-hi, hi); a fraction of
+    # blocks with an f16-subnormal d; x scaled, and a fraction of x entries replaced by +-x_outlier
+    signed_scales: bool = False
+    subnormal_frac: float = 0.0
+    x_scale: float = 1.0
+    x_outlier_frac: float = 0.0
+    x_outlier: float = 30.0
 
 
 WORKLOADS = {
@@ -87,12 +94,14 @@ def normal(shape, std, device, seed):
     return t * std if std != 1.0 else t
 
 
-def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24):
+def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24, signed=False, subnormal_frac=0.0):
     """n_blocks random GGUF blocks as a uint8 tensor [n_blocks, 18|20|34].
 
     Byte layout: f16 d (little endian), for Q4_1 also f16 m, then 16 bytes of
     nibbles (Q4) or 32 signed bytes (Q8_0).  d, m ~ U(lo, hi) rounded to f16;
-    nibble and int8 bytes uniform 0..255."""
+    nibble and int8 bytes uniform 0..255.  With signed: d takes a random sign
+    and m ~ U(-hi, hi); with subnormal_frac > 0 that fraction of the blocks
+    gets a d drawn uniformly from the nonzero f16 subnormals (either sign)."""
     bs = BLOCK_BYTES[qtype]
     out = torch.empty((n_blocks, bs), dtype=torch.uint8, device=device)
     g = _gen(device, seed)
@@ -100,13 +109,25 @@ def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24):
         n = min(chunk, n_blocks - s)
         o = out[s:s + n]
         d = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo).to(torch.float16)
-        o[:, 0:2] = d.view(torch.uint8).view(n, 2)
         q0 = 2
         if qtype == Q4_1:
             m = (torch.rand(n, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo).to(torch.float16)
-            o[:, 2:4] = m.view(torch.uint8).view(n, 2)
             q0 = 4
         o[:, q0:] = torch.randint(0, 256, (n, bs - q0), generator=g, device=device, dtype=torch.uint8)
+        if signed:
+            sign = torch.randint(0, 2, (n,), generator=g, device=device).to(torch.float16) * 2 - 1
+            d = d * sign
+            if qtype == Q4_1:
+                m = ((torch.rand(n, generator=g, device=device, dtype=torch.float32) * 2 - 1) * hi).to(torch.float16)
+        if subnormal_frac > 0:
+            pick = torch.rand(n, generator=g, device=device) < subnormal_frac
+            bits = torch.randint(1, 1024, (n,), generator=g, device=device, dtype=torch.int32)
+            bits = bits | (torch.randint(0, 2, (n,), generator=g, device=device, dtype=torch.int32) << 15)
+            sub = bits.to(torch.int16).view(torch.float16)
+            d = torch.where(pick, sub, d)
+        o[:, 0:2] = d.view(torch.uint8).view(n, 2)
+        if qtype == Q4_1:
+            o[:, 2:4] = m.view(torch.uint8).view(n, 2)
     return out
 
 
@@ -114,7 +135,9 @@ def expert_tensor(n_experts, rows, cols, qtype, device, seed, wl=None):
     """E experts of `rows` rows, each a row of cols/32 blocks: uint8 [E, rows, cols/32*bs]."""
     nb = cols // 32
     lo, hi = (wl.scale_lo, wl.scale_hi) if wl else (0.001, 0.02)
-    b = q4_blocks(n_experts * rows * nb, qtype, device, seed, lo, hi)
+    signed = wl.signed_scales if wl else False
+    subn = wl.subnormal_frac if wl else 0.0
+    b = q4_blocks(n_experts * rows * nb, qtype, device, seed, lo, hi, signed=signed, subnormal_frac=subn)
     return b.view(n_experts, rows, nb * BLOCK_BYTES[qtype])
 
 
@@ -143,7 +166,16 @@ def make_layer(wl, layer=0, device="cpu", master=0):
 def make_x(wl, tokens=None, layer=0, step=0, device="cpu", master=0):
     """FFN input (already normalised by the caller's RMSNorm): [T, H] ~ N(0, 1)."""
     T = wl.tokens if tokens is None else tokens
-    return normal((T, wl.hidden), 1.0, device, seed_for(master, wl.name, layer, f"x/{step}/{T}"))
+    seed = seed_for(master, wl.name, layer, f"x/{step}/{T}")
+    x = normal((T, wl.hidden), 1.0, device, seed)
+    if wl.x_scale != 1.0:
+        x = x * wl.x_scale
+    if wl.x_outlier_frac > 0:
+        g = _gen(device, seed ^ 0x5A5A5A5A)
+        pick = torch.rand(x.shape, generator=g, device=device) < wl.x_outlier_frac
+        sign = torch.randint(0, 2, x.shape, generator=g, device=device).to(torch.float32) * 2 - 1
+        x = torch.where(pick, sign * wl.x_outlier, x)
+    return x
 
 
 def layer_weight_bytes(wl):

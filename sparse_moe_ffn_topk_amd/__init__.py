@@ -66,12 +66,23 @@ def load_library(path=LIB_PATH):
     L.moe_kernel_timer_begin.argtypes = [C.c_int32, C.c_int32]
     L.moe_kernel_timer_end.restype = C.c_int
     L.moe_kernel_timer_end.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_double)]
+    L.moe_workspace_region.restype = C.c_int
+    L.moe_workspace_region.argtypes = [C.POINTER(MoeConfig), C.c_int32, C.c_int32, C.POINTER(C.c_size_t),
+                                       C.POINTER(C.c_size_t)]
+    L.moe_probe_stream.restype = C.c_int
+    L.moe_probe_stream.argtypes = [P, S, C.c_int32, P, P]
+    L.moe_probe_empty.restype = C.c_int
+    L.moe_probe_empty.argtypes = [C.c_int32, P]
+    L.moe_probe_exchange.restype = C.c_int
+    L.moe_probe_exchange.argtypes = [C.c_int32, C.c_int32, C.c_uint32, P, P, P, P]
     _lib = L
     return L
 
 
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
-            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step")
+            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step",
+            "moe_workspace_region", "moe_probe_stream", "moe_probe_empty", "moe_probe_exchange")
+WS_IDS, WS_WEIGHTS, WS_OFFSETS, WS_PERM, WS_POS, WS_TILES, WS_NTILES = 1, 2, 3, 4, 5, 6, 7
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
 KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE, KERNEL_RMSNORM = 5, 6, 7, 8, 9
 KERNEL_PRELUDE = 10
@@ -99,6 +110,17 @@ def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
+
+
+def _keep_for(stream, *temps):
+    """Temporaries allocated here on the current stream but used by kernels on `stream`: tell torch's caching
+    allocator, so it does not hand their memory to other work before those kernels finish."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in temps:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _check(t, name, dtype=None):
@@ -134,6 +156,13 @@ def workspace_bytes(cfg, T):
     return load_library().moe_workspace_bytes(C.byref(cfg), T)
 
 
+def workspace_region(cfg, T, region):
+    """(byte offset, bytes) of a workspace region (diagnostics: WS_* constants)."""
+    off, n = C.c_size_t(0), C.c_size_t(0)
+    _raise(load_library().moe_workspace_region(C.byref(cfg), T, region, C.byref(off), C.byref(n)))
+    return off.value, n.value
+
+
 def alloc_workspace(cfg, T, device="cuda"):
     import torch
     n = workspace_bytes(cfg, T)
@@ -148,12 +177,17 @@ def router_topk(cfg, w, x, logits_in=None, ids=None, weights=None, workspace=Non
     dev = (logits_in if x is None else x).device
     _check(x, "x", torch.float32)
     _check(logits_in, "logits_in", torch.float32)
+    temps = []
     if ids is None:
         ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+        temps.append(ids)
     if weights is None:
         weights = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+        temps.append(weights)
     if workspace is None:
         workspace = alloc_workspace(cfg, T, dev)
+        temps.append(workspace)
+    _keep_for(stream, *temps)
     lw = lw if lw is not None else layer_weights(w)
     _raise(load_library().moe_router_topk(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(logits_in), _ptr(ids),
                                           _ptr(weights), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -169,6 +203,7 @@ def expert_ffn_q4(cfg, w, x, ids, weights, resid, workspace=None, stream=None, l
     _check(resid, "resid", torch.float32)
     if workspace is None:
         workspace = alloc_workspace(cfg, T, x.device)
+        _keep_for(stream, workspace)
     lw = lw if lw is not None else layer_weights(w)
     _raise(load_library().moe_expert_ffn_q4(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(ids), _ptr(weights),
                                             _ptr(resid), _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -184,6 +219,7 @@ def layer_step(cfg, w, x, resid, ids_out=None, weights_out=None, workspace=None,
     _check(weights_out, "weights_out", torch.float32)
     if workspace is None:
         workspace = alloc_workspace(cfg, T, x.device)
+        _keep_for(stream, workspace)
     lw = lw if lw is not None else layer_weights(w)
     _raise(load_library().moe_layer_step(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
                                          _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -259,6 +259,66 @@ int check_norm(const moe_config &c, const moe_layer_weights *w) {
 // row does not fit take the grouped path at any T.
 bool decode_fits(const moe_config &c) { return moe::decode_down_lds_bytes(c.top_k, c.expert_ff, c.shared_ff) <= 65536; }
 
+// Every argument rule of one moe_layer_step (cfg already checked); enqueues
+// nothing.
+int check_layer_args(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, float *resid,
+                     int32_t *ids_out, float *weights_out, void *workspace, size_t workspace_bytes) {
+  int rc;
+  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if (T == 0) return MOE_OK;
+  if (!w) return fail(MOE_EINVAL, "weights is NULL");
+  const bool dense = c.n_experts == 0;
+  if ((rc = check_ptr(w->router_w, "router_w", !dense))) return rc;
+  if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
+  if ((rc = check_expert_ptrs(c, w))) return rc;
+  if ((rc = check_ptr(x, "x", true))) return rc;
+  if ((rc = check_ptr(resid, "resid", true))) return rc;
+  if ((rc = check_norm(c, w))) return rc;
+  if (resid == x && !w->ffn_norm) return fail(MOE_EINVAL, "resid must not alias x (unless ffn_norm is given)");
+  if ((rc = check_ptr4(ids_out, "ids_out", false))) return rc;
+  if ((rc = check_ptr4(weights_out, "weights_out", false))) return rc;
+  return check_ws(c, T, workspace, workspace_bytes);
+}
+
+// The layer step on checked arguments (T > 0).
+int layer_step_impl(const moe_config &c, const moe_layer_weights *w, const float *x, int32_t T, float *resid,
+                    int32_t *ids_out, float *weights_out, void *workspace, hipStream_t st) {
+  int rc;
+  const Layout L = layout(c, T);
+  const bool dense = c.n_experts == 0;
+  int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
+  float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
+  const bool decode = T <= kDecodeMaxT && decode_fits(c);
+  if (decode && !dense && w->ffn_norm && moe::router_fuses_norm(c.hidden, T)) {
+    // decode with a norm: the router kernel normalises x and writes xn; the
+    // gate||up kernel routes a single token in its prologue, more tokens are
+    // routed once each in the decode prelude
+    float *lg = (float *)((char *)workspace + L.logits);
+    float *xn = (float *)((char *)workspace + L.xn);
+    if ((rc = launched(moe::launch_router_logits(w->router_w, x, c.hidden, c.n_experts, T, lg, st, w->ffn_norm,
+                                                 c.norm_eps, xn),
+                       "router logits + rmsnorm")))
+      return rc;
+    return expert_ffn_impl(c, w, xn, T, ids, wts, lg, resid, workspace, st);
+  }
+  if ((rc = prologue_norm(c, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
+  if (dense) {  // no router: only the FFN held in the shared-expert tensors
+    if (decode) return expert_ffn_impl(c, w, x, T, ids, wts, nullptr, resid, workspace, st);
+    return prefill_ffn_impl(c, w, x, T, ids, wts, resid, workspace, st);
+  }
+  if (decode) {
+    // decode: router logits, then the gate||up kernel routes one token in its
+    // prologue (more tokens: the decode prelude routes each once)
+    float *lg = (float *)((char *)workspace + L.logits);
+    if ((rc = launched(moe::launch_router_logits(w->router_w, x, c.hidden, c.n_experts, T, lg, st),
+                       "router logits")))
+      return rc;
+    return expert_ffn_impl(c, w, x, T, ids, wts, lg, resid, workspace, st);
+  }
+  if ((rc = router_topk_impl(c, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
+  return prefill_ffn_impl(c, w, x, T, ids, wts, resid, workspace, st);
+}
+
 // ---- kernel timer (diagnostics) ----
 struct Timer {
   int kernel = 0, capacity = 0, count = 0;
@@ -332,6 +392,32 @@ size_t moe_workspace_bytes(const moe_config *cfg, int32_t T) {
 
 const char *moe_last_error(void) { return g_err.c_str(); }
 
+int moe_workspace_region(const moe_config *cfg, int32_t T, int32_t region, size_t *offset, size_t *bytes) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (T < 1) return fail(MOE_EINVAL, "T %d < 1", T);
+  if (!offset || !bytes) return fail(MOE_EINVAL, "offset or bytes is NULL");
+  const Layout L = layout(*cfg, T);
+  const bool grouped = L.offsets != 0;
+  const size_t k = cfg->top_k, E = cfg->n_experts;
+  const size_t Tc = T < moe::PREFILL_CHUNK ? (size_t)T : (size_t)moe::PREFILL_CHUNK;
+  switch (region) {
+    case MOE_WS_IDS: *offset = L.ids; *bytes = (size_t)T * k * 4; return MOE_OK;
+    case MOE_WS_WEIGHTS: *offset = L.wts; *bytes = (size_t)T * k * 4; return MOE_OK;
+    default: break;
+  }
+  if (!grouped || k == 0) return fail(MOE_EINVAL, "region %d: not used for T %d with this configuration", region, T);
+  switch (region) {
+    case MOE_WS_OFFSETS: *offset = L.offsets; *bytes = (E + 1) * 4; return MOE_OK;
+    case MOE_WS_POS: *offset = L.pos; *bytes = Tc * k * 4; return MOE_OK;
+    case MOE_WS_PERM: *offset = L.perm; *bytes = Tc * k * 4; return MOE_OK;
+    case MOE_WS_NTILES: *offset = L.ntiles; *bytes = 4; return MOE_OK;
+    case MOE_WS_TILES: *offset = L.tiles; *bytes = ((Tc * k + 15) / 16 + E) * 2 * 4; return MOE_OK;
+    default: return fail(MOE_EINVAL, "region %d: unknown", region);
+  }
+}
+
 int32_t moe_decode_max_tokens(void) { return kDecodeMaxT; }
 
 int moe_router_topk(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
@@ -389,54 +475,9 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   g_err.clear();
   int rc;
   if ((rc = check_cfg(cfg))) return rc;
-  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if ((rc = check_layer_args(*cfg, w, x, T, resid, ids_out, weights_out, workspace, workspace_bytes))) return rc;
   if (T == 0) return MOE_OK;
-  if (!w) return fail(MOE_EINVAL, "weights is NULL");
-  const bool dense = cfg->n_experts == 0;
-  if ((rc = check_ptr(w->router_w, "router_w", !dense))) return rc;
-  if ((rc = check_ptr4(w->router_bias, "router_bias", false))) return rc;
-  if ((rc = check_expert_ptrs(*cfg, w))) return rc;
-  if ((rc = check_ptr(x, "x", true))) return rc;
-  if ((rc = check_ptr(resid, "resid", true))) return rc;
-  if ((rc = check_norm(*cfg, w))) return rc;
-  if (resid == x && !w->ffn_norm) return fail(MOE_EINVAL, "resid must not alias x (unless ffn_norm is given)");
-  if ((rc = check_ptr4(ids_out, "ids_out", false))) return rc;
-  if ((rc = check_ptr4(weights_out, "weights_out", false))) return rc;
-  if ((rc = check_ws(*cfg, T, workspace, workspace_bytes))) return rc;
-  const Layout L = layout(*cfg, T);
-  int32_t *ids = ids_out ? ids_out : (int32_t *)((char *)workspace + L.ids);
-  float *wts = weights_out ? weights_out : (float *)((char *)workspace + L.wts);
-  hipStream_t st = (hipStream_t)stream;
-  const bool decode = T <= kDecodeMaxT && decode_fits(*cfg);
-  if (decode && !dense && w->ffn_norm && moe::router_fuses_norm(cfg->hidden, T)) {
-    // decode with a norm: the router kernel normalises x and writes xn; the
-    // gate||up kernel routes a single token in its prologue, more tokens are
-    // routed once each in the decode prelude
-    float *lg = (float *)((char *)workspace + L.logits);
-    float *xn = (float *)((char *)workspace + L.xn);
-    if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st,
-                                                 w->ffn_norm, cfg->norm_eps, xn),
-                       "router logits + rmsnorm")))
-      return rc;
-    return expert_ffn_impl(*cfg, w, xn, T, ids, wts, lg, resid, workspace, st);
-  }
-  if ((rc = prologue_norm(*cfg, w, x, T, workspace, st, &x))) return rc;  // x: the FFN input from here on
-  if (dense) {  // no router: only the FFN held in the shared-expert tensors
-    if (T <= kDecodeMaxT && decode_fits(*cfg)) return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
-    return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
-  }
-  if (T <= kDecodeMaxT && decode_fits(*cfg)) {
-    // decode: router logits, then the gate||up kernel routes one token in its
-    // prologue (more tokens: the decode prelude routes each once)
-    float *lg = (float *)((char *)workspace + L.logits);
-    if ((rc = launched(moe::launch_router_logits(w->router_w, x, cfg->hidden, cfg->n_experts, T, lg, st),
-                       "router logits")))
-      return rc;
-    return expert_ffn_impl(*cfg, w, x, T, ids, wts, lg, resid, workspace, st);
-  }
-  if ((rc = router_topk_impl(*cfg, w, x, T, nullptr, ids, wts, workspace, st))) return rc;
-  if (T > kDecodeMaxT || !decode_fits(*cfg)) return prefill_ffn_impl(*cfg, w, x, T, ids, wts, resid, workspace, st);
-  return expert_ffn_impl(*cfg, w, x, T, ids, wts, nullptr, resid, workspace, st);
+  return layer_step_impl(*cfg, w, x, T, resid, ids_out, weights_out, workspace, (hipStream_t)stream);
 }
 
 int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32_t L, const float *const *x,
@@ -448,9 +489,20 @@ int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32
   int rc;
   if ((rc = check_cfg(cfg))) return rc;
   const size_t per = (size_t)T * cfg->top_k;
+  // every layer is checked before the first one is enqueued: on an error
+  // nothing runs
   for (int32_t l = 0; l < L; l++) {
-    rc = moe_layer_step(cfg, &layers[l], x[l], T, resid, ids_out ? ids_out + l * per : nullptr,
-                        weights_out ? weights_out + l * per : nullptr, workspace, workspace_bytes, stream);
+    rc = check_layer_args(*cfg, &layers[l], x[l], T, resid, ids_out ? ids_out + l * per : nullptr,
+                          weights_out ? weights_out + l * per : nullptr, workspace, workspace_bytes);
+    if (rc) {
+      std::string m = g_err;
+      return fail(rc, "layer %d: %s", l, m.c_str());
+    }
+  }
+  if (T == 0) return MOE_OK;
+  for (int32_t l = 0; l < L; l++) {
+    rc = layer_step_impl(*cfg, &layers[l], x[l], T, resid, ids_out ? ids_out + l * per : nullptr,
+                         weights_out ? weights_out + l * per : nullptr, workspace, (hipStream_t)stream);
     if (rc) {
       std::string m = g_err;
       return fail(rc, "layer %d: %s", l, m.c_str());

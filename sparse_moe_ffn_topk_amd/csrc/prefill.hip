@@ -12,8 +12,8 @@
 //
 // Steps:
 //  1. k_sort_by_expert (one block): a stable counting sort of the pairs by
-//     expert, tokens ascending within an expert: per-expert token bit sets,
-//     popcount prefixes, an exclusive scan (wave shuffles) -> offsets, pos[p],
+//     expert, pair order (tokens ascending) within an expert: per-expert
+//     token bit sets, popcount prefixes, an exclusive scan (wave shuffles) -> offsets, pos[p],
 //     perm[pos], and the list of 16-token tiles of every expert.
 //  2. k_group_gemm<GATEUP>: per (tile, 256-row slice): g and u for 16 tokens
 //     x 256 rows, SwiGLU in registers, act rows written in sorted order; the
@@ -41,8 +41,21 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ sort --
 
-// One block of 1024 threads; T <= PREFILL_CHUNK, E <= 512.
-// bits[e][w]: bit t%32 of word t/32 set when token t picked e.
+// One block of 1024 threads; T <= PREFILL_CHUNK, E <= 512.  The rank of pair
+// p = (t, j) of expert e is the number of pairs of e that come before it in
+// pair order: those of earlier tokens, then token t's own earlier picks of e.
+//   bits[e][w]: bit t%32 of word w = t/32 set when token t picked e at all;
+//   pre[e][w]:  pairs of e in the words before w.
+// A token that lists an expert more than once (only ids a caller passes in
+// can: the router never does) has one bit but several pairs; when the chunk
+// holds such a token, the prefix and the rank add each earlier token's extra
+// picks (a slower path).
+__device__ __forceinline__ int earlier_picks(const int32_t *__restrict__ ids, int t, int k, int j, int e) {
+  int n = 0;
+  for (int i = 0; i < j; i++) n += ids[t * k + i] == e;
+  return n;
+}
+
 __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ ids, int T, int k, int E,
                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ tiles,
@@ -50,22 +63,31 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
   extern __shared__ uint32_t lds[];
   const int W = (T + 31) >> 5;
   uint32_t *bits = lds;                       // [E][W]
-  uint16_t *pre = (uint16_t *)(lds + E * W);  // [E][W] exclusive popcount prefix
+  uint16_t *pre = (uint16_t *)(lds + E * W);  // [E][W] (T * k <= 16384 pairs)
   __shared__ int cnt[512], off[513], toff[513];
+  __shared__ int repeats;
   const int tid = threadIdx.x;
   for (int i = tid; i < E * W; i += 1024) bits[i] = 0u;
+  if (tid == 0) repeats = 0;
   __syncthreads();
   const int np = T * k;
   for (int p = tid; p < np; p += 1024) {
     const int e = ids[p], t = p / k;
-    atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+    if (earlier_picks(ids, t, k, p - t * k, e) == 0)
+      atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+    else
+      repeats = 1;
   }
   __syncthreads();
+  const bool rep = repeats != 0;
   if (tid < E) {
     int c = 0;
     for (int w = 0; w < W; w++) {
       pre[tid * W + w] = (uint16_t)c;
-      c += __popc(bits[tid * W + w]);
+      const uint32_t b = bits[tid * W + w];
+      c += __popc(b);
+      if (rep)
+        for (uint32_t m = b; m; m &= m - 1) c += earlier_picks(ids, 32 * w + __builtin_ctz(m), k, k, tid) - 1;
     }
     cnt[tid] = c;
   }
@@ -120,9 +142,15 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
     }
   }
   for (int p = tid; p < np; p += 1024) {
-    const int e = ids[p], t = p / k;
-    const uint32_t wbits = bits[e * W + (t >> 5)];
-    const int r = pre[e * W + (t >> 5)] + __popc(wbits & ((1u << (t & 31)) - 1u));
+    const int e = ids[p], t = p / k, j = p - t * k;
+    const uint32_t below = bits[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u);
+    int r = pre[e * W + (t >> 5)] + __popc(below) + earlier_picks(ids, t, k, j, e);
+    if (rep) {  // earlier tokens of the word that picked e more than once
+      for (uint32_t m = below; m; m &= m - 1) {
+        const int t2 = (t & ~31) + __builtin_ctz(m);
+        r += earlier_picks(ids, t2, k, k, e) - 1;
+      }
+    }
     const int q = off[e] + r;
     pos[p] = q;
     perm[q] = p;

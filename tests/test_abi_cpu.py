@@ -147,3 +147,54 @@ def test_wide_configs_take_the_grouped_path_workspace():
     assert L.moe_workspace_bytes(C.byref(narrow), 1) > 0
     # many tokens: the grouped path's chunked regions
     assert L.moe_workspace_bytes(C.byref(narrow), 4096) > L.moe_workspace_bytes(C.byref(narrow), 8)
+
+
+def _stack_args(n=3):
+    good = [0x10000] * 8
+    good[1] = 0  # no bias
+    good[5] = good[6] = good[7] = 0  # no shared expert
+    layers = (moe.LayerWeights * n)(*[moe.LayerWeights(*good) for _ in range(n)])
+    xs = (C.c_void_p * n)(*([0x20000] * n))
+    return layers, xs
+
+
+def test_stack_checks_every_layer_before_enqueueing():
+    # an invalid layer 1 of 3: the stack call fails naming layer 1 before it enqueues layer 0 (without a
+    # GPU, enqueueing layer 0 would have failed first, with MOE_ELAUNCH)
+    L = moe.load_library()
+    cfg = _cfg()
+    ws = L.moe_workspace_bytes(C.byref(cfg), 1)
+    layers, xs = _stack_args()
+    layers[1].down_exps = None
+    rc = L.moe_stack_step(C.byref(cfg), layers, 3, xs, 1, C.c_void_p(0x30000), None, None, C.c_void_p(0x40000), ws,
+                          None)
+    msg = L.moe_last_error().decode()
+    assert rc == -1 and msg.startswith("layer 1:") and "down_exps" in msg, (rc, msg)
+    layers, xs = _stack_args()
+    xs[2] = 0x20004  # misaligned input of layer 2
+    rc = L.moe_stack_step(C.byref(cfg), layers, 3, xs, 1, C.c_void_p(0x30000), None, None, C.c_void_p(0x40000), ws,
+                          None)
+    msg = L.moe_last_error().decode()
+    assert rc == -2 and msg.startswith("layer 2:"), (rc, msg)
+    # T = 0: every layer is still checked, then nothing runs
+    layers, xs = _stack_args()
+    assert L.moe_stack_step(C.byref(cfg), layers, 3, xs, 0, C.c_void_p(0x30000), None, None, None, 0, None) == 0
+
+
+def test_workspace_regions():
+    L = moe.load_library()
+    cfg = _cfg(shared_ff=64)
+    for T in (9, 512, 700):
+        total = L.moe_workspace_bytes(C.byref(cfg), T)
+        seen = []
+        for region in (moe.WS_IDS, moe.WS_WEIGHTS, moe.WS_OFFSETS, moe.WS_PERM, moe.WS_POS, moe.WS_TILES,
+                       moe.WS_NTILES):
+            off, n = moe.workspace_region(cfg, T, region)
+            assert off % 256 == 0 and off + n <= total
+            seen.append((off, off + n))
+        seen.sort()
+        assert all(a[1] <= b[0] for a, b in zip(seen, seen[1:])), "regions overlap"
+    # the decode path keeps no sort results
+    with pytest.raises(moe.MoeError):
+        moe.workspace_region(cfg, 8, moe.WS_PERM)
+    assert moe.workspace_region(cfg, 8, moe.WS_IDS)[1] == 8 * cfg.top_k * 4

@@ -9,13 +9,21 @@ import torch
 
 import moe_synth as S
 import oracle as O
-from moe_testlib import REL_TOL, oracle_cfg, row_rel_err, run_layer_parity, to_device
+from moe_testlib import (REG_TOL, REL_TOL, oracle_cfg, oracle_given_routing, oracle_layer, row_rel_err,
+                         run_layer_parity, to_device)
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(*a):
     print("[case]", *a, flush=True)
+
+
+def _ok(err, what, guard=REG_TOL):
+    """The 1e-3 gate, then the regression guard (see moe_testlib)."""
+    print(f"[result] {what} max_row_rel_err={err:.3e}", flush=True)
+    assert err <= REL_TOL, f"{what}: {err:.3e} above the 1e-3 gate"
+    assert err <= guard, f"{what}: {err:.3e} above the regression guard {guard:g}"
 
 
 def _layer(wl, seed=0, tokens=None, step=0):
@@ -89,20 +97,17 @@ def test_layer_step_parity(gpu, name, composed):
     wd, xd = to_device(w), x.cuda()
     resid = xd.clone() if composed else None
     err, ties = run_layer_parity(wl, wd, xd, resid, wnp=S.to_numpy(w))
-    print(f"[result] {name} composed={composed} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    _ok(err, f"{name} composed={composed} near_ties={ties}")
 
 
 def test_layer_prefill_chunk(gpu):
-    # 512 tokens through one Flint-shaped layer (grouped MFMA path); the oracle
-    # checks a spread sample of tokens (tokens are independent)
+    # 512 tokens through one Flint-shaped layer (grouped MFMA path), every
+    # token row against the oracle, and the sort of the pairs bit-exact
     wl = S.WORKLOADS["prefill"]
-    _say("layer prefill T=512 (sampled oracle rows)")
+    _say("layer prefill T=512 (all rows)")
     w, x = _layer(wl, seed=7)
-    sample = list(range(0, 512, 11)) + [511]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
-    print(f"[result] prefill max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"prefill near_ties={ties}")
 
 
 @pytest.mark.parametrize("name,T", [("flint_dense", 1), ("flint_dense", 8), ("flint_dense", 40),
@@ -112,10 +117,8 @@ def test_dense_ffn_layer(gpu, name, T):
     wl = S.WORKLOADS[name]
     _say(f"dense layer {name} SF={wl.shared_ff} Q4_{wl.qtype} T={T}")
     w, x = _layer(wl, seed=17, tokens=T)
-    sample = None if T <= 40 else list(range(0, T, 29)) + [T - 1]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
-    print(f"[result] dense {name} T={T} max_row_rel_err={err:.3e}", flush=True)
-    assert err <= REL_TOL
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"dense {name} T={T}")
 
 
 @pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512), ("flint_dense", 2),
@@ -127,10 +130,8 @@ def test_layer_rmsnorm(gpu, name, T):
     _say(f"layer {name} T={T} with ffn_norm")
     w, x = _layer(wl, seed=19, tokens=T)
     x = x * 3.0 + 0.5  # a residual stream that is not already normalised
-    sample = None if T <= 8 else list(range(0, T, 41)) + [T - 1]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=S.to_numpy(w), sample=sample)
-    print(f"[result] rmsnorm {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=S.to_numpy(w))
+    _ok(err, f"rmsnorm {name} T={T} near_ties={ties}")
 
 
 @pytest.mark.parametrize("name", ["flint", "flint8"])
@@ -153,8 +154,7 @@ def test_chained_stack_with_rmsnorm(gpu, name):
         torch.cuda.synchronize()
         ref, _, _ = O.layer(oracle_cfg(wl), S.to_numpy(layers[l]), before, resid=before)
         err = row_rel_err(resid.cpu().numpy() - before, ref - before).max()
-        print(f"[result] chained {name} layer {l} max_row_rel_err={err:.3e}", flush=True)
-        assert err <= REL_TOL
+        _ok(err, f"chained {name} layer {l}")
     stacked = h0.cuda().clone()
     st = moe.Stack(cfg, dev, [stacked] * L, stacked)
     st.step()
@@ -172,16 +172,14 @@ def test_layer_swiglu_clamp(gpu, name, T):
     _say(f"layer {name} T={T} with SwiGLU clamps 3.0 / 2.0")
     w, x = _layer(wl, seed=13)
     wnp = S.to_numpy(w)
-    sample = None if T <= 8 else list(range(0, T, 37)) + [T - 1]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=wnp, sample=sample)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), None, wnp=wnp)
     # the clamps change the layer's output (so the test exercises them)
-    rows = [0] if sample is None else sample[:2]
+    rows = [0, T - 1]
     ref_c = O.layer(oracle_cfg(wl), wnp, x.numpy()[rows])[0]
     ref_u = O.layer(oracle_cfg(dataclasses.replace(wl, swiglu_limit=0.0, swiglu_limit_shared=0.0)), wnp,
                     x.numpy()[rows])[0]
     assert row_rel_err(ref_c, ref_u).max() > 0.05
-    print(f"[result] clamp {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    _ok(err, f"clamp {name} T={T} near_ties={ties}")
 
 
 @pytest.mark.parametrize("T", [600, 1100])
@@ -190,9 +188,8 @@ def test_layer_prefill_multi_chunk(gpu, T):
     wl = S.Workload("chunks", 256, 16, 3, 64, 96, S.Q4_1, has_bias=True)
     _say("prefill chunks T", T)
     w, x = _layer(wl, seed=T, tokens=T)
-    sample = list(range(0, T, 37)) + [T - 1]
-    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w), sample=sample)
-    assert err <= REL_TOL
+    err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"prefill chunks T={T}")
 
 
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13, 40])
@@ -201,7 +198,7 @@ def test_layer_token_counts_ragged(gpu, T):
     _say("ragged T", T)
     w, x = _layer(wl, seed=T, tokens=T)
     err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    assert err <= REL_TOL
+    _ok(err, f"ragged T={T}")
 
 
 @pytest.mark.parametrize("T", [3, 20])
@@ -212,7 +209,7 @@ def test_layer_q4_0_unaligned_rows(gpu, H, F, SF, T):
     _say("q4_0 odd rows", H, F, SF, "T", T)
     w, x = _layer(wl, seed=H + F, tokens=T)
     err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    assert err <= REL_TOL
+    _ok(err, f"q4_0 odd rows H={H} F={F} SF={SF} T={T}")
 
 
 @pytest.mark.parametrize("qt", [S.Q4_1, S.Q4_0])
@@ -229,8 +226,7 @@ def test_grouped_gateup_row_streaming_shapes(gpu, H, qt):
     _say("grouped gate||up row-streaming", "H", H, "qtype", qt, "T", T)
     w, x = _layer(wl, seed=H + qt, tokens=T)
     err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    print(f"[result] row-streaming H={H} q={qt} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    _ok(err, f"row-streaming H={H} q={qt} near_ties={ties}")
 
 
 @pytest.mark.parametrize("qt", [S.Q4_1, S.Q4_0])
@@ -244,8 +240,7 @@ def test_grouped_down_row_streaming_shapes(gpu, F, SF, qt):
     _say("grouped down row-streaming", "F", F, "SF", SF, "qtype", qt, "T", T)
     w, x = _layer(wl, seed=F + SF + qt, tokens=T)
     err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    print(f"[result] down row-streaming F={F} SF={SF} q={qt} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    _ok(err, f"down row-streaming F={F} SF={SF} q={qt} near_ties={ties}")
 
 
 @pytest.mark.parametrize("T", [100, 600])
@@ -258,10 +253,8 @@ def test_row_streaming_many_tiles_and_chunks(gpu, T):
     w, x = _layer(wl, seed=31 + T, tokens=T)
     w["bias"] = torch.zeros(16)
     w["bias"][[3, 11]] = 10.0
-    sample = None if T <= 128 else list(range(0, T, 23)) + [T - 1]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w), sample=sample)
-    print(f"[result] row-streaming many tiles T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"row-streaming many tiles T={T} near_ties={ties}")
 
 
 @pytest.mark.parametrize("name,T", [("lfm25_q8", 1), ("lfm25_q8", 3), ("lfm25_q8", 520)])
@@ -270,10 +263,8 @@ def test_layer_q8_0(gpu, name, T):
     wl = S.WORKLOADS[name]
     _say(f"layer {name} Q8_0 T={T}")
     w, x = _layer(wl, seed=23, tokens=T)
-    sample = None if T <= 8 else list(range(0, T, 31)) + [T - 1]
-    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w), sample=sample)
-    print(f"[result] q8_0 {name} T={T} max_row_rel_err={err:.3e} near_ties={ties}", flush=True)
-    assert err <= REL_TOL
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"q8_0 {name} T={T} near_ties={ties}")
 
 
 @pytest.mark.parametrize("H,F,SF,T", [(96, 96, 64, 3), (96, 96, 64, 20), (2080, 160, 224, 1), (2080, 160, 224, 9)])
@@ -283,7 +274,7 @@ def test_layer_q8_0_odd_rows_and_shared(gpu, H, F, SF, T):
     _say("q8_0 odd rows", H, F, SF, "T", T)
     w, x = _layer(wl, seed=H + F + T, tokens=T)
     err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    assert err <= REL_TOL
+    _ok(err, f"q8_0 odd rows H={H} F={F} SF={SF} T={T}")
 
 
 def test_layer_single_expert_and_k_equals_E(gpu):
@@ -292,7 +283,7 @@ def test_layer_single_expert_and_k_equals_E(gpu):
         _say("k=E", E)
         w, x = _layer(wl, seed=E, tokens=4)
         err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-        assert err <= REL_TOL
+        _ok(err, f"k=E={E}")
 
 
 def test_layer_all_tokens_on_one_expert(gpu):
@@ -303,7 +294,7 @@ def test_layer_all_tokens_on_one_expert(gpu):
     w["bias"][[5, 17]] = 10.0  # bias forces experts 5 and 17 for every token
     wd = to_device(w)
     err, _ = run_layer_parity(wl, wd, x.cuda(), wnp=S.to_numpy(w))
-    assert err <= REL_TOL
+    _ok(err, "all tokens on experts 5 and 17")
 
 
 def test_layer_large_shape(gpu):
@@ -313,7 +304,7 @@ def test_layer_large_shape(gpu):
     _say("large H=8192 E=512 k=32")
     w, x = _layer(wl, seed=1, tokens=2)
     err, _ = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
-    assert err <= REL_TOL
+    _ok(err, "large H=8192 E=512 k=32")
 
 
 def test_expert_ffn_zero_offsets_give_exact_zero(gpu):
@@ -374,3 +365,78 @@ def test_split_calls_equal_layer_step(gpu, name, T):
     moe.expert_ffn_q4(cfg, wd, xd, ids2, wts2, b)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(wts, wts2) and torch.equal(a, b)
+
+
+# ------------------------------------------------- wide input distributions --
+
+WIDE_CASES = [(qt, T) for qt in (S.Q4_0, S.Q4_1, S.Q8_0) for T in (1, 5, 40)]
+
+
+@pytest.mark.parametrize("qt,T", WIDE_CASES)
+def test_layer_wide_block_scales_and_outliers(gpu, qt, T):
+    # block scales d of either sign, 5% of them f16 subnormals, Q4_1 offsets m of either sign, and 2% of the
+    # inputs replaced by +-30: decode (T = 1, 5) and grouped (T = 40) paths, with a shared expert
+    wl = S.Workload("wide", 512, 16, 3, 160, 96, qt, has_bias=True, signed_scales=True, subnormal_frac=0.05,
+                    x_outlier_frac=0.02, x_outlier=30.0,
+                    scale_lo=0.0001 if qt == S.Q8_0 else 0.001, scale_hi=0.0004 if qt == S.Q8_0 else 0.02)
+    _say("wide scales and outliers", "qtype", qt, "T", T)
+    w, x = _layer(wl, seed=41 + qt, tokens=T)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"wide qtype={qt} T={T} near_ties={ties}")
+
+
+@pytest.mark.parametrize("scale", [1e-4, 1e3])
+@pytest.mark.parametrize("T", [1, 40])
+def test_layer_input_scale(gpu, scale, T):
+    # FFN inputs far from unit scale: 1e-4 puts the act values of the grouped path's f16 MFMA operands in
+    # the f16 subnormal range unless they are rescaled; 1e3 tests the upper side
+    wl = S.Workload("xscale", 512, 16, 3, 160, 96, S.Q4_1, has_bias=True, x_scale=scale)
+    _say("input scale", scale, "T", T)
+    w, x = _layer(wl, seed=43, tokens=T)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"input scale {scale:g} T={T} near_ties={ties}")
+
+
+@pytest.mark.parametrize("T", [8, 9, 40])
+def test_expert_ffn_repeated_ids(gpu, T):
+    # caller-given ids in which a token lists one expert twice (or three times): the decode path (T = 8)
+    # and the grouped path (T = 9, 40) must both add every pick with its own weight, as the oracle does
+    moe = gpu
+    wl = S.Workload("rep", 256, 12, 4, 96, 64, S.Q4_1)
+    _say("repeated ids", "T", T)
+    w, x = _layer(wl, seed=47, tokens=T)
+    g = torch.Generator().manual_seed(T)
+    ids = torch.randint(0, 12, (T, 4), generator=g, dtype=torch.int32)
+    ids[0, 1] = ids[0, 0]
+    ids[T - 1, 3] = ids[T - 1, 2] = ids[T - 1, 0]
+    ids[T // 2, 2] = ids[T // 2, 1]
+    wts = torch.rand((T, 4), generator=g) + 0.1
+    wd = to_device(w)
+    out = torch.zeros((T, 256), device="cuda")
+    moe.expert_ffn_q4(moe.config_for(wl), wd, x.cuda(), ids.cuda(), wts.cuda(), out)
+    torch.cuda.synchronize()
+    wnp = S.to_numpy(w)
+    ref = np.stack([oracle_given_routing(wl, wnp, x[t].numpy(), ids[t].numpy(), wts[t].numpy())
+                    for t in range(T)])
+    _ok(row_rel_err(out.cpu().numpy(), ref).max(), f"repeated ids T={T}")
+
+
+def test_grouped_sort_with_repeated_ids_bit_exact(gpu):
+    # the grouped path's sort of caller-given ids with repeats, read back from the workspace
+    from moe_testlib import check_sort
+    moe = gpu
+    wl = S.Workload("rep", 256, 12, 4, 96, 64, S.Q4_1)
+    T = 70
+    _say("sort with repeated ids T", T)
+    w, x = _layer(wl, seed=53, tokens=T)
+    g = torch.Generator().manual_seed(5)
+    ids = torch.randint(0, 12, (T, 4), generator=g, dtype=torch.int32)
+    ids[::3, 1] = ids[::3, 0]
+    ids[::7, 3] = ids[::7, 0]
+    cfg = moe.config_for(wl)
+    ws = moe.alloc_workspace(cfg, T)
+    out = torch.zeros((T, 256), device="cuda")
+    moe.expert_ffn_q4(cfg, to_device(w), x.cuda(), ids.cuda(), torch.ones((T, 4), device="cuda"), out,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    check_sort(cfg, ws, ids.numpy(), T)
