@@ -150,38 +150,43 @@ static float score32(float l32, const float *bias, int e) {
   return s;
 }
 
-/* Group-limited selection ([LING] routeLing): a group's score is the sum of
- * its two largest selection scores (an equal value counts as the second);
- * the groups_used best groups are kept, scanning groups in index order with a
- * strict '>' so the lower index wins ties; experts of the other groups are
- * excluded.  keep[g] = 1 for kept groups. */
+/* Group-limited selection ([LING] routeLing and its file header: groups are
+ * ranked by the sum of their two best selection scores and only the
+ * groups_used best groups stay selectable).  Written from that rule:
+ *   gscore[g] = f32 sum of the two largest values of group g's scores (a
+ *               sorted copy; an equal value counts as the second);
+ *   the kept groups are the first groups_used of the groups ordered by
+ *   (gscore descending, group index ascending), i.e. the lower index wins a
+ *   tie.
+ * keep[g] = 1 for kept groups. */
+static int desc_f32(const void *a, const void *b) {
+  float x = *(const float *)a, y = *(const float *)b;
+  return (x < y) - (x > y);
+}
+static const float *g_order_scores; /* (qsort has no context argument) */
+static int by_score_then_index(const void *a, const void *b) {
+  int i = *(const int *)a, j = *(const int *)b;
+  float x = g_order_scores[i], y = g_order_scores[j];
+  if (x != y) return x > y ? -1 : 1;
+  return (i > j) - (i < j);
+}
 void mo_group_keep(const float *s32, int32_t E, int32_t G, int32_t Gu, int32_t *keep, float *gscore) {
   int P = E / G;
+  float *copy = (float *)malloc(sizeof(float) * (size_t)P);
+  int *order = (int *)malloc(sizeof(int) * (size_t)G);
   for (int g = 0; g < G; g++) {
-    float a = -INFINITY, b = -INFINITY;
-    for (int e = g * P; e < (g + 1) * P; e++) {
-      float v = s32[e];
-      if (v > a) {
-        b = a;
-        a = v;
-      } else if (v > b) {
-        b = v;
-      }
-    }
-    volatile float sum = a + b;
+    memcpy(copy, s32 + (size_t)g * P, sizeof(float) * (size_t)P);
+    qsort(copy, (size_t)P, sizeof(float), desc_f32);
+    volatile float sum = copy[0] + copy[1]; /* one f32 rounding, as the page's kernel */
     gscore[g] = sum;
     keep[g] = 0;
+    order[g] = g;
   }
-  for (int r = 0; r < Gu; r++) {
-    int best = -1;
-    float bv = -INFINITY;
-    for (int g = 0; g < G; g++)
-      if (!keep[g] && (best < 0 || gscore[g] > bv)) {
-        bv = gscore[g];
-        best = g;
-      }
-    keep[best] = 1;
-  }
+  g_order_scores = gscore;
+  qsort(order, (size_t)G, sizeof(int), by_score_then_index);
+  for (int r = 0; r < Gu; r++) keep[order[r]] = 1;
+  free(copy);
+  free(order);
 }
 
 /* Top-k over the allowed experts: k rounds, each picking the largest f32
