@@ -400,7 +400,7 @@ def cpu_leg(args, wl, cfg, layers, xs, resid, ws, L, T):
         ref, ids_ref, _ = results[l]
         x_in, delta, ids_g = rec[l]
         x_in, delta, ids_g = x_in[rows], delta[rows], ids_g[rows]
-        ref_delta = ref - (x_in if args.chained else 0.0)
+        ref_delta = ref  # (the oracle ran without a residual: its output is the FFN delta)
         for i in range(len(rows)):
             if wl.top_k > 0 and not np.array_equal(ids_g[i], ids_ref[i]):
                 mism += 1

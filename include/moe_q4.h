@@ -217,8 +217,10 @@ enum {
   MOE_KERNEL_GROUP_DOWN = 7,   /* grouped down MFMA GEMM, weighted        */
   MOE_KERNEL_COMBINE = 8,      /* per-token sum into the residual         */
   MOE_KERNEL_RMSNORM = 9,      /* pre-FFN RMSNorm (when ffn_norm is given) */
-  MOE_KERNEL_PRELUDE = 10      /* decode of 2+ tokens: per-token select and
+  MOE_KERNEL_PRELUDE = 10,     /* decode of 2+ tokens: per-token select and
                                   the shared expert's gate||up for all tokens */
+  MOE_KERNEL_ROW_SCALE = 11    /* grouped path: the input rows' power-of-two
+                                  scales for the f16 MFMA operands           */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
 int moe_kernel_timer_end(int32_t *count, double *total_ms);

@@ -85,7 +85,7 @@ EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_
 WS_IDS, WS_WEIGHTS, WS_OFFSETS, WS_PERM, WS_POS, WS_TILES, WS_NTILES = 1, 2, 3, 4, 5, 6, 7
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
 KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE, KERNEL_RMSNORM = 5, 6, 7, 8, 9
-KERNEL_PRELUDE = 10
+KERNEL_PRELUDE, KERNEL_ROW_SCALE = 10, 11
 
 
 def make_config(hidden, n_experts, top_k, expert_ff, shared_ff=0, qtype=MOE_Q4_1, n_groups=1, groups_used=None,

@@ -6,7 +6,6 @@
 #include <string.h>
 
 #include <cmath>
-
 #include <string>
 
 #include "../../include/moe_q4.h"
@@ -37,7 +36,7 @@ size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 // uses logits/ids/wts/act; the grouped path works on chunks of at most
 // PREFILL_CHUNK tokens and adds the sort results and its act and Y rows.
 struct Layout {
-  size_t logits, ids, wts, act, xn, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, total;
+  size_t logits, ids, wts, act, xn, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, xexp, aexp, total;
 };
 
 Layout layout(const moe_config &c, int32_t T) {
@@ -67,8 +66,10 @@ Layout layout(const moe_config &c, int32_t T) {
     L.pact_sh = take(Tc * SF * 4);
     L.Y = take(Tc * k * H * 4);
     L.Ysh = take(Tc * H * 4);
+    L.xexp = take(Tc * 4);
+    L.aexp = take(Tc * (k + 1) * 4);
   } else {
-    L.offsets = L.pos = L.perm = L.tiles = L.ntiles = L.pact = L.pact_sh = L.Y = L.Ysh = 0;
+    L.offsets = L.pos = L.perm = L.tiles = L.ntiles = L.pact = L.pact_sh = L.Y = L.Ysh = L.xexp = L.aexp = 0;
   }
   L.total = o;
   return L;
@@ -230,6 +231,8 @@ int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const floa
     p.Y = (float *)(b + L.Y);
     p.Ysh = (float *)(b + L.Ysh);
     p.resid = resid + (size_t)t0 * c.hidden;
+    p.xexp = (int32_t *)(b + L.xexp);
+    p.aexp = (int32_t *)(b + L.aexp);
     p.lim = c.swiglu_limit;
     p.lim_sh = c.swiglu_limit_shared;
     int rc = launched(moe::launch_prefill_ffn(p, st), "grouped expert FFN");
@@ -345,7 +348,7 @@ int moe_kernel_timer_end(int32_t *count, double *total_ms);
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
   g_err.clear();
   if (g_timer.kernel) moe_kernel_timer_end(nullptr, nullptr);
-  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_PRELUDE || capacity < 1 || capacity > (1 << 20))
+  if (kernel < MOE_KERNEL_ROUTER || kernel > MOE_KERNEL_ROW_SCALE || capacity < 1 || capacity > (1 << 20))
     return fail(MOE_EINVAL, "kernel timer: bad kernel %d or capacity %d", kernel, capacity);
   g_timer.start = new hipEvent_t[capacity];
   g_timer.stop = new hipEvent_t[capacity];

@@ -67,6 +67,7 @@ struct PrefillArgs {
   float *Y, *Ysh;          // [T*k][H] sorted and weighted, [T][H]
   float *resid;            // [T][H] in/out
   float lim, lim_sh;       // SwiGLU clamp of the routed and of the shared experts (0: none)
+  int32_t *xexp, *aexp;    // [T], [T*k + T]: the rows' largest f32 exponents (scales of the f16 MFMA inputs)
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
 size_t prefill_sort_lds_bytes(int T, int E);

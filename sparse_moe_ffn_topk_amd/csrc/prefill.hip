@@ -30,6 +30,14 @@
 // (value d*q + m; Q4_0 is m = -8d).  The nibbles enter the MFMA as exact f16
 // values: a mask-or builds the f16 1024 + q, a packed f16 subtract removes
 // the 1024.
+//
+// f16 has a narrow exponent range, so every input row (a token's x, a pair's
+// or a token's act) is first scaled by a power of two that puts its largest
+// |value| in [2^14, 2^15): the hi + lo split then neither overflows nor drops
+// into f16 subnormals at the top of the row, at any input scale.  The scale
+// is exact; each tile's result is scaled back before the epilogue.  The
+// exponents come from k_row_exp (x) and from the gate||up epilogue
+// (atomicMax over the act values it writes).
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -211,7 +219,35 @@ struct GemmArgs {
   float *out_sh;             // GATEUP: act_sh; DOWN: Ysh [T][H]
   int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
   float lim, lim_sh;         // GATEUP: SwiGLU clamp of routed / shared experts (0: none)
+  const int32_t *xexp;       // [T] largest biased f32 exponent of |x| per token (k_row_exp)
+  int32_t *aexp;             // [T*k] then [T]: the same for the act rows (sorted, then shared);
+                             // GATEUP raises them with atomicMax, DOWN reads them
 };
+
+// Biased f32 exponent of |v|, and the power-of-two shift that puts a row
+// whose largest biased exponent is eb in [2^14, 2^15) (2^(eb - 127) <= max
+// < 2^(eb - 126)).
+__device__ __forceinline__ int bexp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
+__device__ __forceinline__ int row_shift(int eb) { return 141 - eb; }
+
+// Largest biased exponent of |x| over each of nrows rows of K floats (one
+// wave per row); the grid also zeroes nzero words at zero (the act rows'
+// exponents, raised later by atomicMax).
+__global__ __launch_bounds__(256) void k_row_exp(const float *__restrict__ rows, int nrows, int K,
+                                                 int32_t *__restrict__ eb, int32_t *__restrict__ zero, int nzero) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < nzero; i += gridDim.x * 256) zero[i] = 0;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= nrows) return;
+  const float4 *p = reinterpret_cast<const float4 *>(rows + (size_t)r * K);
+  int m = 0;
+  for (int i = lane; i < K / 4; i += 64) {
+    const float4 v = p[i];
+    m = max(m, max(max(bexp(v.x), bexp(v.y)), max(bexp(v.z), bexp(v.w))));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
+  if (lane == 0) eb[r] = m;
+}
 
 // K is walked in chunks of KB blocks.  Per chunk a block stages, in LDS, the
 // raw bytes of its 256 weight rows (brow<QT>() bytes each: 4 x 20; 4 x 18 or
@@ -247,7 +283,8 @@ __device__ __forceinline__ void a_load(AStage &st, rsrc_t r, int K, int row, int
 }
 // k within the block kk = (seg%4)*8 + i; the lane holding it has k-octet
 // (kk%16)/8 + 2*(kk/16) and slot kperm(kk%8).  asum[block][token].
-__device__ __forceinline__ void a_store(const AStage &st, _Float16 (*ahi)[APAD], _Float16 (*alo)[APAD],
+// sh: the row's power-of-two shift (row_shift).
+__device__ __forceinline__ void a_store(const AStage &st, int sh, _Float16 (*ahi)[APAD], _Float16 (*alo)[APAD],
                                         float (*asum)[16]) {
   const int m = threadIdx.x >> 4, seg = threadIdx.x & 15;
   const int blk = seg >> 2;
@@ -257,10 +294,11 @@ __device__ __forceinline__ void a_store(const AStage &st, _Float16 (*ahi)[APAD],
     const int kk = (seg & 3) * 8 + i;
     const int q8 = ((kk & 15) >> 3) + 2 * (kk >> 4);
     const int col = blk * 32 + q8 * 8 + kperm(kk & 7);
-    const _Float16 h = (_Float16)st.v[i];
+    const float v = __builtin_ldexpf(st.v[i], sh);
+    const _Float16 h = (_Float16)v;
     ahi[m][col] = h;
-    alo[m][col] = (_Float16)(st.v[i] - (float)h);
-    s += st.v[i];
+    alo[m][col] = (_Float16)(v - (float)h);
+    s += v;
   }
   s += __shfl_xor(s, 1, 64);  // the four threads of one block
   s += __shfl_xor(s, 2, 64);
@@ -342,6 +380,7 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   __shared__ int rowid[16];  // A row per tile token (-1: none)
   __shared__ int outid[16];  // output row per tile token
   __shared__ float outw[16];
+  __shared__ int rsh[16];    // the A row's power-of-two shift
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bx = blockIdx.x;
@@ -380,6 +419,9 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
       outid[tid] = ok ? first + tid : -1;
       outw[tid] = 1.f;
     }
+    const int ar = rowid[tid];
+    const int32_t *ex = MODE == GG_GATEUP ? a.xexp : (shared ? a.aexp + (size_t)a.T * a.k : a.aexp);
+    rsh[tid] = ar >= 0 ? row_shift(ex[ar]) : 0;
   }
   const int r0 = blockIdx.y * 256;
   if (r0 >= R) return;
@@ -433,14 +475,14 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   for (int c = 0; c < 4; c++) o0[c] = (int)(((uint32_t)(r0 + wave * 64 + 16 * c + n) * rowbytes) & 3u);
 
   __syncthreads();  // rowid
-  const int arow = rowid[tid >> 4];
+  const int arow = rowid[tid >> 4], ash = rsh[tid >> 4];
   AStage ast;
   b_issue(0);
   a_load(ast, ra, K, arow, 0);
 
   for (int kc = 0; kc < nbK; kc += KB) {
     b_store();
-    a_store(ast, ahi, alo, asum);
+    a_store(ast, ash, ahi, alo, asum);
     __syncthreads();
     if (kc + KB < nbK) {
       b_issue(kc + KB);
@@ -474,7 +516,9 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
   }
 
   // epilogue: this lane holds D[token 4*kq + i][row r0 + wave*64 + 16c + n]
+  // (scaled by 2^rsh[token]: scaled back first)
   const int rbase = r0 + wave * 64;
+  int emax[4] = {0, 0, 0, 0};  // GATEUP: largest exponent of the act values this lane writes, per token
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const int row = rbase + 16 * c + n;
@@ -487,18 +531,30 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
       float v;
       if (MODE == GG_GATEUP) {
         // SwiGLU, clamped when L > 0 (the ling_moe_ssd.js page's swiglu kernel)
-        const float g = acc[0][c][i], L = shared ? a.lim_sh : a.lim;
-        float u = acc[NM - 1][c][i], sg = g / (1.0f + __expf(-g));
+        const float g = __builtin_ldexpf(acc[0][c][i], -rsh[m]), L = shared ? a.lim_sh : a.lim;
+        float u = __builtin_ldexpf(acc[NM - 1][c][i], -rsh[m]), sg = g / (1.0f + __expf(-g));
         if (L > 0.f) {
           u = fminf(fmaxf(u, -L), L);
           sg = fminf(sg, L);
         }
         v = sg * u;
+        emax[i] = max(emax[i], bexp(v));
       } else {
-        v = outw[m] * acc[0][c][i];
+        v = outw[m] * __builtin_ldexpf(acc[0][c][i], -rsh[m]);
       }
       float *dst = shared ? a.out_sh : a.out;
       dst[(size_t)o * R + row] = v;
+    }
+  }
+  if constexpr (MODE == GG_GATEUP) {
+    // the act rows' exponents: the 16 lanes of one k-octet share their tokens
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      int e = emax[i];
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) e = max(e, __shfl_xor(e, d, 64));
+      const int o = outid[4 * kq + i];
+      if (n == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, e);
     }
   }
 }
@@ -541,7 +597,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t bst[2][16][PADW];
   __shared__ __attribute__((aligned(16))) float red[4][2][64][4];  // [wave][gate, up][lane][element]
   __shared__ __attribute__((aligned(16))) float asum[4][RS_KQM][16];
-  __shared__ int rowid[16], outid[16];
+  __shared__ int rowid[16], outid[16], rsh[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0, b = (int)blockIdx.x;
@@ -582,8 +638,10 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   if (tid < 16) {
     const bool ok = tid < ntok;
     const int q = first + tid;
-    rowid[tid] = ok ? (shared ? q : a.perm[q] / a.k) : -1;
+    const int ar = ok ? (shared ? q : a.perm[q] / a.k) : -1;
+    rowid[tid] = ar;
     outid[tid] = ok ? q : -1;
+    rsh[tid] = ar >= 0 ? row_shift(a.xexp[ar]) : 0;
   }
   const int r0 = by * RS_GU_RB;
   if (r0 >= R) return;
@@ -602,7 +660,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   // current one is converted)
   half8 xh[KQ], xl[KQ];
   {
-    const int arow = rowid[n];
+    const int arow = rowid[n], ash = rsh[n];
     u32x4 v0[2][4], v1[2][4];
     auto load_group = [&](int g, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
 #pragma unroll
@@ -627,10 +685,11 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const _Float16 h = (_Float16)xv[i];
+          const float v = __builtin_ldexpf(xv[i], ash);
+          const _Float16 h = (_Float16)v;
           xh[j][kperm(i)] = h;
-          xl[j][kperm(i)] = (_Float16)(xv[i] - (float)h);
-          sum += xv[i];
+          xl[j][kperm(i)] = (_Float16)(v - (float)h);
+          sum += v;
         }
         sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
         sum += __shfl_xor(sum, 32, 64);
@@ -694,11 +753,14 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     {
       // wave w finishes element w of every lane's tile values: D[token 4 (l/16) + w][row r0 + 16 c + l%16],
       // the waves' partials added in order 0..3
-      const int l = lane, i = wave;
-      const float g = ((red[0][0][l][i] + red[1][0][l][i]) + red[2][0][l][i]) + red[3][0][l][i];
-      const float u = ((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i];
+      // (the tile values are scaled by 2^rsh[token]: scaled back first)
+      const int l = lane, i = wave, slot = 4 * (l >> 4) + i;
+      const int sh = rsh[slot];
+      const float g = __builtin_ldexpf(((red[0][0][l][i] + red[1][0][l][i]) + red[2][0][l][i]) + red[3][0][l][i], -sh);
+      const float u = __builtin_ldexpf(((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i], -sh);
       const int row = r0 + 16 * c + (l & 15);
-      const int o = outid[4 * (l >> 4) + i];
+      const int o = outid[slot];
+      int e = 0;
       if (o >= 0 && row < R) {
         const float L = shared ? a.lim_sh : a.lim;
         float sg = g / (1.0f + __expf(-g)), uu = u;
@@ -706,8 +768,14 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
           uu = fminf(fmaxf(uu, -L), L);
           sg = fminf(sg, L);
         }
-        (shared ? a.out_sh : a.out)[(size_t)o * R + row] = sg * uu;
+        const float v = sg * uu;
+        (shared ? a.out_sh : a.out)[(size_t)o * R + row] = v;
+        e = bexp(v);
       }
+      // the act row's exponent: the 16 lanes of l / 16 share the token
+#pragma unroll
+      for (int d = 8; d >= 1; d >>= 1) e = max(e, __shfl_xor(e, d, 64));
+      if ((l & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, e);
     }
   }
 }
@@ -720,7 +788,7 @@ struct DownRowsLds {
   static constexpr size_t bst = 4 * 16 * TPC * PADW;          // staged chunk
   static constexpr size_t red = 4 * 4 * TPC * 64 * 4;         // waves' partial tiles
   static constexpr size_t asum = 4 * 4 * KQ * 16;             // input sums per K block
-  static constexpr size_t bytes = bst + red + asum + 3 * 4 * 16;
+  static constexpr size_t bytes = bst + red + asum + 4 * 4 * 16;  // + rowid, outid, outw, rsh
 };
 
 // Grouped down, row-streaming form (Q4 blocks; K = F or SF of 16..64 blocks,
@@ -750,6 +818,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
                                        DownRowsLds<QT, KQ>::asum);
   int *outid = rowid + 16;
   float *outw = reinterpret_cast<float *>(rowid + 32);
+  int *rsh = rowid + 48;
   static_assert(DownRowsLds<QT, KQ>::bst % 16 == 0 && DownRowsLds<QT, KQ>::red % 16 == 0, "alignment");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -776,6 +845,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     rowid[tid] = ok ? q : -1;
     outid[tid] = ok ? q : -1;
     outw[tid] = ok && !shared ? a.wts[a.perm[q]] : 1.f;
+    rsh[tid] = ok ? row_shift((shared ? a.aexp + (size_t)a.T * a.k : a.aexp)[q]) : 0;
   }
   const int r0 = by * rb;
   if (r0 >= R) return;
@@ -790,7 +860,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
   // this wave's A fragments (as in k_group_gateup_rows)
   half8 xh[KQ], xl[KQ];
   {
-    const int arow = rowid[n];
+    const int arow = rowid[n], ash = rsh[n];
     u32x4 v0[2][2], v1[2][2];
     auto load_group = [&](int g, u32x4 (&a0)[2], u32x4 (&a1)[2]) {
 #pragma unroll
@@ -815,10 +885,11 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-          const _Float16 h = (_Float16)xv[i];
+          const float v = __builtin_ldexpf(xv[i], ash);
+          const _Float16 h = (_Float16)v;
           xh[j][kperm(i)] = h;
-          xl[j][kperm(i)] = (_Float16)(xv[i] - (float)h);
-          sum += xv[i];
+          xl[j][kperm(i)] = (_Float16)(v - (float)h);
+          sum += v;
         }
         sum += __shfl_xor(sum, 16, 64);
         sum += __shfl_xor(sum, 32, 64);
@@ -883,12 +954,12 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     {
       // wave w finishes element w: D[token 4 (l/16) + w][row r0 + CR c + 16 t + l%16], waves added in order
       const int l = lane, i = wave;
-      const int slot = 4 * (l >> 4) + i, o = outid[slot];
+      const int slot = 4 * (l >> 4) + i, o = outid[slot], sh = rsh[slot];
       const float wgt = outw[slot];
       float *dst = shared ? a.out_sh : a.out;
 #pragma unroll
       for (int t = 0; t < TPC; t++) {
-        const float v = ((red[0][t][l][i] + red[1][t][l][i]) + red[2][t][l][i]) + red[3][t][l][i];
+        const float v = __builtin_ldexpf(((red[0][t][l][i] + red[1][t][l][i]) + red[2][t][l][i]) + red[3][t][l][i], -sh);
         const int row = r0 + CR * c + 16 * t + (l & 15);
         if (o >= 0 && row < R) dst[(size_t)o * R + row] = wgt * v;
       }
@@ -993,10 +1064,19 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
                p.perm, p.tiles, p.ntiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // the rows' power-of-two scales: x now, the act rows' exponents zeroed for the gate||up epilogue
+  {
+    const int nzero = T * (k + 1);
+    const int nblk = max((T + 3) / 4, (nzero + 255) / 256);
+    MOE_LAUNCH(11, k_row_exp, dim3(nblk), dim3(256), 0u, st, p.x, T, p.H, p.xexp, p.aexp, nzero);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   GemmArgs g{};
   g.T = T;
   g.k = k;
   g.H = p.H;
+  g.xexp = p.xexp;
+  g.aexp = p.aexp;
   g.F = p.F;
   g.SF = p.SF;
   g.E = E;
