@@ -156,6 +156,21 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
                    float *resid, int32_t *ids_out, float *weights_out, void *workspace,
                    size_t workspace_bytes, moe_stream_t stream);
 
+/* moe_layer_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of MOE_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends;
+ * the call allocates nothing.  A T whose moe_workspace_bytes(cfg, T) exceeds
+ * it is rejected with MOE_EWORKSPACE (16 MiB covers decode at every shape
+ * and the grouped path up to about 128 tokens at the Flint and LFM2.5
+ * shapes, about 100 at the Ling shape).  Every call on one GPU uses that
+ * GPU's one array, so calls that overlap on a GPU (other streams, other
+ * threads) race and must be ordered by the caller.  No kernel needs the
+ * array zeroed.  Otherwise as moe_layer_step. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16 << 20)
+int moe_layer_step_noalloc(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                           float *resid, int32_t *ids_out, float *weights_out, moe_stream_t stream);
+
 /* L MoE layers of one shape run in order on one stream, each a
  * moe_layer_step: layer l reads x[l] and adds its FFN output to the shared
  * residual, so layer l+1's expert reads start only after layer l finished.

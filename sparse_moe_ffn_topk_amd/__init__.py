@@ -69,6 +69,8 @@ def load_library(path=LIB_PATH):
     L.moe_workspace_region.restype = C.c_int
     L.moe_workspace_region.argtypes = [C.POINTER(MoeConfig), C.c_int32, C.c_int32, C.POINTER(C.c_size_t),
                                        C.POINTER(C.c_size_t)]
+    L.moe_layer_step_noalloc.restype = C.c_int
+    L.moe_layer_step_noalloc.argtypes = [C.POINTER(MoeConfig), C.POINTER(LayerWeights), P, C.c_int32, P, P, P, P]
     L.moe_probe_stream.restype = C.c_int
     L.moe_probe_stream.argtypes = [P, S, C.c_int32, P, P]
     L.moe_probe_empty.restype = C.c_int
@@ -81,7 +83,9 @@ def load_library(path=LIB_PATH):
 
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
             "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step",
-            "moe_workspace_region", "moe_probe_stream", "moe_probe_empty", "moe_probe_exchange")
+            "moe_workspace_region", "moe_probe_stream", "moe_probe_empty", "moe_probe_exchange",
+            "moe_layer_step_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 WS_IDS, WS_WEIGHTS, WS_OFFSETS, WS_PERM, WS_POS, WS_TILES, WS_NTILES = 1, 2, 3, 4, 5, 6, 7
 KERNEL_ROUTER, KERNEL_SELECT, KERNEL_GATEUP, KERNEL_DOWN = 1, 2, 3, 4
 KERNEL_SORT, KERNEL_GROUP_GATEUP, KERNEL_GROUP_DOWN, KERNEL_COMBINE, KERNEL_RMSNORM = 5, 6, 7, 8, 9
@@ -223,6 +227,20 @@ def layer_step(cfg, w, x, resid, ids_out=None, weights_out=None, workspace=None,
     lw = lw if lw is not None else layer_weights(w)
     _raise(load_library().moe_layer_step(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
                                          _ptr(weights_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return resid
+
+
+def layer_step_noalloc(cfg, w, x, resid, ids_out=None, weights_out=None, stream=None, lw=None):
+    """moe_layer_step_noalloc: the layer step on the library's static device scratch (no workspace)."""
+    import torch
+    T = x.shape[0]
+    _check(x, "x", torch.float32)
+    _check(resid, "resid", torch.float32)
+    _check(ids_out, "ids_out", torch.int32)
+    _check(weights_out, "weights_out", torch.float32)
+    lw = lw if lw is not None else layer_weights(w)
+    _raise(load_library().moe_layer_step_noalloc(C.byref(cfg), C.byref(lw), _ptr(x), T, _ptr(resid), _ptr(ids_out),
+                                                 _ptr(weights_out), _stream(stream)))
     return resid
 
 

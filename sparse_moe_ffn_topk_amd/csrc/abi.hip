@@ -6,10 +6,18 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_q4.h"
 #include "moe_launch.h"
+
+// Workspace of moe_layer_step_noalloc: a fixed array in device memory that
+// every GPU the library runs on holds from module load to process end.  In
+// host code `scratch` names a host-side stand-in, not the device array: host
+// code only ever uses the device address hipGetSymbolAddress returns for the
+// current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -322,6 +330,29 @@ int layer_step_impl(const moe_config &c, const moe_layer_weights *w, const float
   return prefill_ffn_impl(c, w, x, T, ids, wts, resid, workspace, st);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int noalloc_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 // ---- kernel timer (diagnostics) ----
 struct Timer {
   int kernel = 0, capacity = 0, count = 0;
@@ -481,6 +512,24 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
   if ((rc = check_layer_args(*cfg, w, x, T, resid, ids_out, weights_out, workspace, workspace_bytes))) return rc;
   if (T == 0) return MOE_OK;
   return layer_step_impl(*cfg, w, x, T, resid, ids_out, weights_out, workspace, (hipStream_t)stream);
+}
+
+int moe_layer_step_noalloc(const moe_config *cfg, const moe_layer_weights *w, const float *x, int32_t T,
+                           float *resid, int32_t *ids_out, float *weights_out, moe_stream_t stream) {
+  g_err.clear();
+  int rc;
+  if ((rc = check_cfg(cfg))) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T %d < 0", T);
+  if (T == 0) return MOE_OK;
+  const size_t need = layout(*cfg, T).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE, "T %d needs %zu bytes of workspace, above the %d-byte static scratch of "
+                "moe_layer_step_noalloc (use moe_layer_step with a workspace, or fewer tokens)",
+                T, need, MOE_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if ((rc = noalloc_scratch(&ws))) return rc;
+  if ((rc = check_layer_args(*cfg, w, x, T, resid, ids_out, weights_out, ws, need))) return rc;
+  return layer_step_impl(*cfg, w, x, T, resid, ids_out, weights_out, ws, (hipStream_t)stream);
 }
 
 int moe_stack_step(const moe_config *cfg, const moe_layer_weights *layers, int32_t L, const float *const *x,
