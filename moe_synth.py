@@ -57,6 +57,9 @@ class Workload:
     x_scale: float = 1.0
     x_outlier_frac: float = 0.0
     x_outlier: float = 30.0
+    # Q4_1 offsets centred on the block: m = -c * d, c ~ U(7, 8) (rounded to f16), so a block spans about
+    # [-7.5 d, 7.5 d] as when zero-mean weights are quantised (m is the block minimum); off: m ~ U(lo, hi)
+    centred: bool = False
 
 
 WORKLOADS = {
@@ -94,14 +97,16 @@ def normal(shape, std, device, seed):
     return t * std if std != 1.0 else t
 
 
-def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24, signed=False, subnormal_frac=0.0):
+def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24, signed=False, subnormal_frac=0.0,
+              centred=False):
     """n_blocks random GGUF blocks as a uint8 tensor [n_blocks, 18|20|34].
 
     Byte layout: f16 d (little endian), for Q4_1 also f16 m, then 16 bytes of
     nibbles (Q4) or 32 signed bytes (Q8_0).  d, m ~ U(lo, hi) rounded to f16;
     nibble and int8 bytes uniform 0..255.  With signed: d takes a random sign
     and m ~ U(-hi, hi); with subnormal_frac > 0 that fraction of the blocks
-    gets a d drawn uniformly from the nonzero f16 subnormals (either sign)."""
+    gets a d drawn uniformly from the nonzero f16 subnormals (either sign).
+    With centred (Q4_1): m = -c d with c ~ U(7, 8), rounded to f16."""
     bs = BLOCK_BYTES[qtype]
     out = torch.empty((n_blocks, bs), dtype=torch.uint8, device=device)
     g = _gen(device, seed)
@@ -119,6 +124,9 @@ def q4_blocks(n_blocks, qtype, device, seed, lo=0.001, hi=0.02, chunk=1 << 24, s
             d = d * sign
             if qtype == Q4_1:
                 m = ((torch.rand(n, generator=g, device=device, dtype=torch.float32) * 2 - 1) * hi).to(torch.float16)
+        if centred and qtype == Q4_1:
+            c = torch.rand(n, generator=g, device=device, dtype=torch.float32) + 7.0
+            m = (-(c * d.to(torch.float32))).to(torch.float16)
         if subnormal_frac > 0:
             pick = torch.rand(n, generator=g, device=device) < subnormal_frac
             bits = torch.randint(1, 1024, (n,), generator=g, device=device, dtype=torch.int32)
@@ -137,7 +145,8 @@ def expert_tensor(n_experts, rows, cols, qtype, device, seed, wl=None):
     lo, hi = (wl.scale_lo, wl.scale_hi) if wl else (0.001, 0.02)
     signed = wl.signed_scales if wl else False
     subn = wl.subnormal_frac if wl else 0.0
-    b = q4_blocks(n_experts * rows * nb, qtype, device, seed, lo, hi, signed=signed, subnormal_frac=subn)
+    cen = wl.centred if wl else False
+    b = q4_blocks(n_experts * rows * nb, qtype, device, seed, lo, hi, signed=signed, subnormal_frac=subn, centred=cen)
     return b.view(n_experts, rows, nb * BLOCK_BYTES[qtype])
 
 

@@ -58,13 +58,16 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // can: the router never does) has one bit but several pairs; when the chunk
 // holds such a token, the prefix and the rank add each earlier token's extra
 // picks (a slower path).
-__device__ __forceinline__ int earlier_picks(const int32_t *__restrict__ ids, int t, int k, int j, int e) {
+template <typename P>
+__device__ __forceinline__ int earlier_picks(P ids, int t, int k, int j, int e) {
   int n = 0;
   for (int i = 0; i < j; i++) n += ids[t * k + i] == e;
   return n;
 }
 
-__global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ ids, int T, int k, int E,
+// STAGE: the ids are first copied to LDS (after bits and pre) and read there.
+template <bool STAGE>
+__global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ gids, int T, int k, int E,
                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ tiles,
                                                          int32_t *__restrict__ ntiles) {
@@ -72,13 +75,17 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
   const int W = (T + 31) >> 5;
   uint32_t *bits = lds;                       // [E][W]
   uint16_t *pre = (uint16_t *)(lds + E * W);  // [E][W] (T * k <= 16384 pairs)
+  int32_t *sids = (int32_t *)(lds + E * W + (E * W + 1) / 2);  // [T * k] (STAGE)
   __shared__ int cnt[512], off[513], toff[513];
   __shared__ int repeats;
   const int tid = threadIdx.x;
+  const int np = T * k;
   for (int i = tid; i < E * W; i += 1024) bits[i] = 0u;
+  if constexpr (STAGE)
+    for (int i = tid; i < np; i += 1024) sids[i] = gids[i];
   if (tid == 0) repeats = 0;
   __syncthreads();
-  const int np = T * k;
+  const int32_t *ids = STAGE ? sids : gids;
   for (int p = tid; p < np; p += 1024) {
     const int e = ids[p], t = p / k;
     if (earlier_picks(ids, t, k, p - t * k, e) == 0)
@@ -725,6 +732,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   };
 
   const int nch = min(RS_GU_RB, R - r0 + 15) / 16;
+  int emax = 0;  // largest exponent of the act values this lane writes (one token slot, every chunk)
   issue(0);
   for (int c = 0; c < nch; c++) {
     stage();
@@ -760,7 +768,6 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
       const float u = __builtin_ldexpf(((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i], -sh);
       const int row = r0 + 16 * c + (l & 15);
       const int o = outid[slot];
-      int e = 0;
       if (o >= 0 && row < R) {
         const float L = shared ? a.lim_sh : a.lim;
         float sg = g / (1.0f + __expf(-g)), uu = u;
@@ -770,14 +777,16 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
         }
         const float v = sg * uu;
         (shared ? a.out_sh : a.out)[(size_t)o * R + row] = v;
-        e = bexp(v);
+        emax = max(emax, bexp(v));
       }
-      // the act row's exponent: the 16 lanes of l / 16 share the token
-#pragma unroll
-      for (int d = 8; d >= 1; d >>= 1) e = max(e, __shfl_xor(e, d, 64));
-      if ((l & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, e);
     }
   }
+  // the act row's exponent: lane l served token slot 4 (l / 16) + wave in
+  // every chunk; the 16 lanes of l / 16 share it
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) emax = max(emax, __shfl_xor(emax, d, 64));
+  const int o = outid[4 * (lane >> 4) + wave];
+  if ((lane & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, emax);
 }
 
 // LDS of one k_group_down_rows tile (bytes; every part a multiple of 16).
@@ -1029,7 +1038,9 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ Y, co
 
 // ---------------------------------------------------------------- launch --
 
-size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * (4 + 2); }
+size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32) * (4 + 2) + 4; }
+// The sort stages the ids in LDS while the whole stays within 56 KB.
+static bool sort_stages_ids(int T, int k, int E) { return prefill_sort_lds_bytes(T, E) + (size_t)T * k * 4 <= 56 * 1024; }
 
 template <int QT, int KQF>
 static void launch_down_rows_s(int kqs, const GemmArgs &g, int shtiles, int rbs, int nblk, hipStream_t st) {
@@ -1059,9 +1070,12 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
   hipError_t err;
   if (k > 0) {  // (a dense layer, k == 0, has no routed pairs to sort)
-    const size_t lds = prefill_sort_lds_bytes(T, E);
-    MOE_LAUNCH(5, k_sort_by_expert, dim3(1), dim3(1024), (uint32_t)lds, st, p.ids, T, k, E, p.offsets, p.pos,
-               p.perm, p.tiles, p.ntiles);
+    if (sort_stages_ids(T, k, E))
+      MOE_LAUNCH(5, k_sort_by_expert<true>, dim3(1), dim3(1024), (uint32_t)(prefill_sort_lds_bytes(T, E) + T * k * 4),
+                 st, p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
+    else
+      MOE_LAUNCH(5, k_sort_by_expert<false>, dim3(1), dim3(1024), (uint32_t)prefill_sort_lds_bytes(T, E), st,
+                 p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // the rows' power-of-two scales: x now, the act rows' exponents zeroed for the gate||up epilogue

@@ -134,15 +134,16 @@ def test_layer_rmsnorm(gpu, name, T):
     _ok(err, f"rmsnorm {name} T={T} near_ties={ties}")
 
 
-@pytest.mark.parametrize("name", ["flint", "flint8"])
-def test_chained_stack_with_rmsnorm(gpu, name):
+@pytest.mark.parametrize("name,centred", [("flint", False), ("flint8", False), ("flint", True), ("ling", True)])
+def test_chained_stack_with_rmsnorm(gpu, name, centred):
     # the chained form: each layer's input is the running residual, resid += FFN(rms_norm(resid) * w);
     # per layer against the oracle given that layer's input, and one stack call against per-layer calls
+    # (centred: the Q4_1 offsets of the chained benchmark stack)
     import dataclasses
     moe = gpu
-    wl = dataclasses.replace(S.WORKLOADS[name], norm_eps=1e-5)
+    wl = dataclasses.replace(S.WORKLOADS[name], norm_eps=1e-5, centred=centred)
     L = 3
-    _say(f"chained stack {name} L={L}")
+    _say(f"chained stack {name} L={L} centred={centred}")
     layers = [S.make_layer(wl, layer=100 + l, device="cpu") for l in range(L)]
     dev = [to_device(w) for w in layers]
     h0 = S.make_x(wl, layer=99, device="cpu") * 2.0
@@ -440,3 +441,46 @@ def test_grouped_sort_with_repeated_ids_bit_exact(gpu):
                       workspace=ws)
     torch.cuda.synchronize()
     check_sort(cfg, ws, ids.numpy(), T)
+
+
+# ------------------------------------------------ one-token routing, exact ties --
+
+TIE_CASES = {
+    "flint": dict(E=256, k=6, G=1, Gu=1, bias=False),
+    "lfm25": dict(E=64, k=4, G=1, Gu=1, bias=True),
+    "ling": dict(E=512, k=8, G=8, Gu=4, bias=True),
+    "odd_E": dict(E=100, k=5, G=1, Gu=1, bias=False),
+    "k32": dict(E=64, k=32, G=1, Gu=1, bias=False),
+    "groups_small": dict(E=128, k=6, G=16, Gu=5, bias=True),  # groups of 8: the block router
+}
+
+
+@pytest.mark.parametrize("name", sorted(TIE_CASES))
+def test_one_token_routing_exact_ties(gpu, name):
+    # identical router rows give bitwise equal logits, so the lowest expert index (and, with groups, the lowest
+    # group index) decides: the GPU's picks must equal the oracle's exactly (a near-tie certificate would accept
+    # any order here, so the ids are compared strictly), and so must the layer output
+    moe = gpu
+    c = TIE_CASES[name]
+    E, k = c["E"], c["k"]
+    wl = S.Workload("ties", 256, E, k, 64, 32, S.Q4_1, n_groups=c["G"], groups_used=c["Gu"],
+                    weights_scale=2.5 if c["G"] > 1 else 1.0, has_bias=c["bias"])
+    _say("one-token routing with exact ties", name)
+    w, x = _layer(wl, seed=71 + E, tokens=1)
+    g = torch.Generator().manual_seed(E + k)
+    tied = torch.randperm(E, generator=g)[: 2 * k + 3]
+    v = x[0] / x[0].norm() * 0.25
+    w["router_w"][tied] = v  # every tied expert scores above the rest, all equally
+    if c["bias"]:
+        w["bias"][tied] = 0.0  # the tied experts also tie on the selection bias
+    wd = to_device(w)
+    cfg = moe.config_for(wl)
+    out = torch.zeros((1, 256), device="cuda")
+    ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    moe.layer_step(cfg, wd, x.cuda(), out, ids, wts)
+    torch.cuda.synchronize()
+    ref, ids_ref, w_ref = O.layer(oracle_cfg(wl), S.to_numpy(w), x.numpy())
+    assert np.array_equal(ids.cpu().numpy(), ids_ref), (ids.cpu().numpy(), ids_ref)
+    assert np.allclose(wts.cpu().numpy(), w_ref, rtol=2e-6, atol=1e-7)
+    _ok(row_rel_err(out.cpu().numpy(), ref).max(), f"ties {name}")

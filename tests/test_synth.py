@@ -74,3 +74,23 @@ def test_wide_variants():
     out = np.abs(x) == 30.0
     assert 0.015 < out.mean() < 0.025
     assert np.array_equal(x[~out], S.make_x(S.Workload("w", 256, 8, 2, 64, 32), 64).numpy()[~out])
+
+
+def test_centred_offsets():
+    # centred Q4_1 blocks: m = -c d with c ~ U(7, 8), rounded to f16, so the block's values straddle zero;
+    # d keeps its U(lo, hi) draw and the nibbles their uniform bytes (the same stream as without centring)
+    n = 1 << 14
+    b = S.q4_blocks(n, S.Q4_1, "cpu", 5, 0.001, 0.02, centred=True).numpy()
+    plain = S.q4_blocks(n, S.Q4_1, "cpu", 5, 0.001, 0.02).numpy()
+    assert np.array_equal(b[:, 0:2], plain[:, 0:2]) and np.array_equal(b[:, 4:], plain[:, 4:])
+    d = b[:, 0:2].copy().view(np.float16).astype(np.float64).ravel()
+    m = b[:, 2:4].copy().view(np.float16).astype(np.float64).ravel()
+    c = -m / d
+    assert c.min() >= 7.0 - 1e-2 and c.max() <= 8.0 + 1e-2
+    assert abs(c.mean() - 7.5) < 0.02
+    # the mean weight of a block, d * 7.5 + m, is centred on zero
+    assert abs((d * 7.5 + m).mean()) < 2e-4
+    # Q4_0 and Q8_0 blocks carry no offset: centring leaves them as they are
+    for qt in (S.Q4_0, S.Q8_0):
+        assert np.array_equal(S.q4_blocks(256, qt, "cpu", 5, centred=True).numpy(),
+                              S.q4_blocks(256, qt, "cpu", 5).numpy())
