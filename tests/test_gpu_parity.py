@@ -163,6 +163,56 @@ def test_chained_stack_with_rmsnorm(gpu, name, centred):
     assert torch.equal(stacked, resid)
 
 
+STACK_CASES = [("flint", "chained"), ("ling", "chained"), ("lfm25", "independent_norm"), ("tiny", "independent"),
+               ("flint", "independent")]
+
+
+@pytest.mark.parametrize("name,mode", STACK_CASES)
+def test_stack_against_oracle_chain(gpu, name, mode):
+    # one token through L layers in one stack call (chained: each layer's input is the running residual;
+    # independent: given inputs, the residual accumulates), against the oracle run as the same chain on the
+    # host: every layer's ids and weights, and the final residual
+    import dataclasses
+    moe = gpu
+    norm = mode in ("chained", "independent_norm")
+    wl = dataclasses.replace(S.WORKLOADS[name], norm_eps=1e-5 if norm else 0.0, centred=True, tokens=1)
+    L, H, k = 4, wl.hidden, wl.top_k
+    _say(f"stack with carried router {name} {mode} L={L}")
+    layers = [S.make_layer(wl, layer=200 + l, device="cpu") for l in range(L)]
+    dev = [to_device(w) for w in layers]
+    cfg = moe.config_for(wl)
+    ocfg = oracle_cfg(wl)
+    ids = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((L, 1, k), device="cuda")
+    h0 = S.make_x(wl, 1, layer=199)
+    if mode == "chained":
+        resid = h0.cuda().clone()
+        xs = [resid] * L
+    else:
+        resid = torch.zeros((1, H), device="cuda")
+        xs = [S.make_x(wl, 1, layer=300 + l).cuda() for l in range(L)]
+    moe.Stack(cfg, dev, xs, resid, ids, wts).step()
+    torch.cuda.synchronize()
+    # the oracle chain, each layer on the f32 input the GPU layer saw (f32 residual between layers)
+    h = h0.numpy().astype(np.float32) if mode == "chained" else np.zeros((1, H), np.float32)
+    tot = np.zeros((1, H))
+    for l in range(L):
+        wnp = S.to_numpy(layers[l])
+        if mode == "chained":
+            out, rid, rw = O.layer(ocfg, wnp, h, resid=h)
+            tot = out
+            h = out.astype(np.float32)
+        else:
+            out, rid, rw = O.layer(ocfg, wnp, xs[l].cpu().numpy())
+            tot = tot + out
+        gi = ids[l].cpu().numpy()
+        assert np.array_equal(gi, rid), f"layer {l}: ids {gi} vs oracle {rid}"
+        assert np.allclose(wts[l].cpu().numpy(), rw, rtol=2e-6, atol=1e-7), f"layer {l} weights"
+    got = resid.cpu().numpy().astype(np.float64)
+    base = h0.numpy() if mode == "chained" else 0.0
+    _ok(row_rel_err(got - base, tot - base).max(), f"stack {name} {mode} final residual", guard=1e-5)
+
+
 @pytest.mark.parametrize("name,T", [("flint", 1), ("flint8", 8), ("prefill", 512)])
 def test_layer_swiglu_clamp(gpu, name, T):
     # SwiGLU clamp (ling_moe_ssd.js page: min(silu(g), L) * clamp(u, -L, L)),
