@@ -238,6 +238,13 @@ enum {
                                   scales for the f16 MFMA operands           */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
+/* Timer mode (before moe_kernel_timer_begin; kept until changed): drain 1
+ * (the default) first waits for the stream to go idle, so the interval holds
+ * the kernel and its dispatch from an idle queue; drain 0 records the events
+ * in stream order, so the interval also holds the wait for the previous
+ * kernel's end and the dispatch after it.  MOE_EINVAL while the timer is
+ * armed. */
+int moe_kernel_timer_drain(int32_t drain);
 int moe_kernel_timer_end(int32_t *count, double *total_ms);
 
 /* Probes of the chip (diagnostics; no part of the MoE step uses them).  They

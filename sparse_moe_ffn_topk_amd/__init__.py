@@ -64,6 +64,8 @@ def load_library(path=LIB_PATH):
                                  C.c_int32, P, P, P, P, S, P]
     L.moe_kernel_timer_begin.restype = C.c_int
     L.moe_kernel_timer_begin.argtypes = [C.c_int32, C.c_int32]
+    L.moe_kernel_timer_drain.restype = C.c_int
+    L.moe_kernel_timer_drain.argtypes = [C.c_int32]
     L.moe_kernel_timer_end.restype = C.c_int
     L.moe_kernel_timer_end.argtypes = [C.POINTER(C.c_int32), C.POINTER(C.c_double)]
     L.moe_workspace_region.restype = C.c_int
@@ -82,7 +84,7 @@ def load_library(path=LIB_PATH):
 
 
 EXPORTED = ("moe_workspace_bytes", "moe_router_topk", "moe_expert_ffn_q4", "moe_layer_step", "moe_last_error",
-            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_stack_step",
+            "moe_decode_max_tokens", "moe_kernel_timer_begin", "moe_kernel_timer_end", "moe_kernel_timer_drain", "moe_stack_step",
             "moe_workspace_region", "moe_probe_stream", "moe_probe_empty", "moe_probe_exchange",
             "moe_layer_step_noalloc")
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -263,12 +265,14 @@ class Stack:
 
 
 class KernelTimer:
-    """Times every launch of one kernel with HIP events on its own stream (diagnostics)."""
+    """Times every launch of one kernel with HIP events on its own stream (diagnostics).  drain (default): wait
+    for the stream to go idle before each timed launch; otherwise the events are recorded in stream order."""
 
-    def __init__(self, kernel, capacity):
-        self.kernel, self.capacity = kernel, capacity
+    def __init__(self, kernel, capacity, drain=True):
+        self.kernel, self.capacity, self.drain = kernel, capacity, drain
 
     def __enter__(self):
+        _raise(load_library().moe_kernel_timer_drain(1 if self.drain else 0))
         _raise(load_library().moe_kernel_timer_begin(self.kernel, self.capacity))
         return self
 

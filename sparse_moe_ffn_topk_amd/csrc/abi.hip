@@ -356,6 +356,7 @@ int noalloc_scratch(void **ptr) {
 // ---- kernel timer (diagnostics) ----
 struct Timer {
   int kernel = 0, capacity = 0, count = 0;
+  bool drain = true;
   hipEvent_t *start = nullptr, *stop = nullptr;
 } g_timer;
 
@@ -367,6 +368,7 @@ TimerSlot timer_slot(int id) {
   if (g_timer.kernel == id && g_timer.count < g_timer.capacity) {
     t.start = g_timer.start[g_timer.count];
     t.stop = g_timer.stop[g_timer.count++];
+    t.drain = g_timer.drain;
   }
   return t;
 }
@@ -375,6 +377,13 @@ TimerSlot timer_slot(int id) {
 extern "C" {
 
 int moe_kernel_timer_end(int32_t *count, double *total_ms);
+
+int moe_kernel_timer_drain(int32_t drain) {
+  g_err.clear();
+  if (g_timer.kernel) return fail(MOE_EINVAL, "kernel timer: set the drain mode before moe_kernel_timer_begin");
+  g_timer.drain = drain != 0;
+  return MOE_OK;
+}
 
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity) {
   g_err.clear();
@@ -412,7 +421,9 @@ int moe_kernel_timer_end(int32_t *count, double *total_ms) {
   }
   delete[] g_timer.start;
   delete[] g_timer.stop;
+  const bool drain = g_timer.drain;
   g_timer = Timer();
+  g_timer.drain = drain;
   if (count) *count = n;
   if (total_ms) *total_ms = total;
   return rc;

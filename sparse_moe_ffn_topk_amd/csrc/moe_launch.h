@@ -75,11 +75,12 @@ size_t prefill_sort_lds_bytes(int T, int E);
 // Kernel timer (diagnostics, eager launches only): when armed for kernel `id`,
 // timer_slot() hands out the next (start, stop) event pair, which the launch
 // attaches to the kernel's own dispatch (hipExtLaunchKernelGGL), so the events
-// time that kernel's execution on its stream; otherwise both are NULL.  The
-// stream is drained before a timed launch so that its start stamp is not
-// taken while earlier work on the stream is still running.
+// time that kernel's execution on its stream; otherwise both are NULL.  With
+// drain set (moe_kernel_timer_begin's mode 1) the stream is drained before a
+// timed launch, so the interval also holds the dispatch from an idle queue.
 struct TimerSlot {
   hipEvent_t start = nullptr, stop = nullptr;
+  bool drain = false;
 };
 TimerSlot timer_slot(int id);
 
@@ -87,7 +88,7 @@ TimerSlot timer_slot(int id);
 #define MOE_LAUNCH(ID, KERNEL, GRID, BLOCK, LDS, ST, ...)                                                 \
   do {                                                                                                   \
     const ::moe::TimerSlot ts_ = ::moe::timer_slot(ID);                                                  \
-    if (ts_.start) (void)hipStreamSynchronize(ST);                                                       \
+    if (ts_.start && ts_.drain) (void)hipStreamSynchronize(ST);                                          \
     hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, ts_.start, ts_.stop, 0, __VA_ARGS__);            \
   } while (0)
 
