@@ -371,6 +371,27 @@ template <> struct QStaged<MOE_Q8_0> {
   }
 };
 
+// Per-block factor of the input-sum term of a staged block: m for Q4_1
+// (w = d q + m), d for Q4_0 (w = d q - 8 d: the term is -8 d sum(x), the -8
+// applied by the caller).  factor_word() is the dword holding its f16 bits;
+// factor_pair() packs the factors of blocks j - 1 (low half) and j (high half),
+// j odd and the wave's first block even: Q4_1's m is the high half of its
+// block's first dword, Q4_0's d the low half for an even block, the high half
+// for an odd one (18-byte blocks).
+template <int QT> struct QFactor;
+template <> struct QFactor<MOE_Q4_1> {
+  static __device__ __forceinline__ uint32_t word(const uint32_t *w, int jb) { return w[5 * jb]; }
+  static __device__ __forceinline__ uint32_t pair(uint32_t wj, uint32_t wprev) {
+    return __builtin_amdgcn_perm(wj, wprev, 0x07060302u);
+  }
+};
+template <> struct QFactor<MOE_Q4_0> {
+  static __device__ __forceinline__ uint32_t word(const uint32_t *w, int jb) { return w[(18 * jb) >> 2]; }
+  static __device__ __forceinline__ uint32_t pair(uint32_t wj, uint32_t wprev) {
+    return __builtin_amdgcn_perm(wj, wprev, 0x07060100u);
+  }
+};
+
 // grid.x: routed tiles (16 tokens of one expert) then shared tiles (16 tokens);
 // grid.y: slices of 256 output rows; 4 waves x 64 rows (4 MFMA tiles of 16).
 // Each chunk: registers -> LDS, barrier, issue the next chunk's loads, MFMAs
@@ -597,13 +618,15 @@ __device__ __forceinline__ int xcd_run(int i, int n) {
 }
 template <int QT, int KQ>
 __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
-  static_assert(KQ <= RS_KQM, "K blocks per wave");
+  static_assert(KQ <= RS_KQM && KQ % 2 == 0, "K blocks per wave");
   constexpr int BS = QBlock<QT>::bytes;
   constexpr int MAXDW = KQ * 4 * BS / 4;       // dwords of a row
   constexpr int PADW = MAXDW + 4;              // staged row stride (a 16-byte pad spreads the banks)
   __shared__ __attribute__((aligned(16))) uint32_t bst[2][16][PADW];
   __shared__ __attribute__((aligned(16))) float red[4][2][64][4];  // [wave][gate, up][lane][element]
-  __shared__ __attribute__((aligned(16))) float asum[4][RS_KQM][16];
+  // the input-sum MFMA operand of each wave, 2^-6 sum(x) of token lane % 16 over
+  // the wave's K blocks 8 (lane / 16) + i, as f16 hi and lo parts
+  __shared__ __attribute__((aligned(16))) half8 amt[4][2][64];
   __shared__ int rowid[16], outid[16], rsh[16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -668,6 +691,7 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   half8 xh[KQ], xl[KQ];
   {
     const int arow = rowid[n], ash = rsh[n];
+    float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // this lane's A operand of the input-sum MFMA
     u32x4 v0[2][4], v1[2][4];
     auto load_group = [&](int g, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
 #pragma unroll
@@ -700,9 +724,21 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
         }
         sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
         sum += __shfl_xor(sum, 32, 64);
-        if (kq == 0) asum[wave][j][n] = sum;
+        if ((j >> 3) == kq) am[j & 7] = sum;
       }
     }
+    // |sum| < 32 * 2^15 (the row shift puts |x| below 2^15): 2^-6 sum fits f16;
+    // hi + lo carry 22 of its bits
+    half8 ah, al;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float v = __builtin_ldexpf(am[i], -6);
+      const _Float16 h = (_Float16)v;
+      ah[i] = h;
+      al[i] = (_Float16)(v - (float)h);
+    }
+    amt[wave][0][lane] = ah;
+    amt[wave][1][lane] = al;
   }
 
   // staged chunk: 16 rows of gate (m = 0) and of up (m = 1), row i at bst[m][i]
@@ -739,20 +775,46 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     __syncthreads();
     if (c + 1 < nch) issue(c + 1);
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // B operand of the input-sum MFMA, per matrix: the blocks' f16 factors (m,
+    // or d for Q4_0) of row n, blocks 8 (kq & 1) + i of the wave's K range
+    // (lanes kq >= 2 meet zeros in A; two named vectors, not an array, which
+    // was placed in LDS)
+    u32x4 P0 = {0u, 0u, 0u, 0u}, P1 = P0;
+    uint32_t fprev0 = 0u, fprev1 = 0u;
+    const bool upper = (kq & 1) != 0;
 #pragma unroll
     for (int j = 0; j < KQ; j++) {
       const int jb = wave * KQ + j;
-      const float4 sx4 = *reinterpret_cast<const float4 *>(&asum[wave][j][4 * kq]);
-      const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
 #pragma unroll
       for (int m = 0; m < 2; m++) {
         float d, mo;
         const half8 q = QStaged<QT>::frag(&bst[m][n][0], 0, jb, kq, d, mo);
+        const uint32_t fw = QFactor<QT>::word(&bst[m][n][0], jb);
+        uint32_t &fprev = m ? fprev1 : fprev0;
+        u32x4 &Pv = m ? P1 : P0;
+        const bool mine = ((j >> 3) != 0) == upper;  // (j >> 3: compile time)
+        if (j & 1) Pv[(j & 7) >> 1] = mine ? QFactor<QT>::pair(fw, fprev) : Pv[(j & 7) >> 1];
+        fprev = fw;
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[j], q, z, 0, 0, 0);
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[j], q, z, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[m][i] = __builtin_fmaf(d, z[i], __builtin_fmaf(mo, sx[i], acc[m][i]));
+        for (int i = 0; i < 4; i++) acc[m][i] = __builtin_fmaf(d, z[i], acc[m][i]);
+      }
+    }
+    {
+      // + the input-sum term sum_j f_j sum(x)_j on the matrix cores: acc is
+      // scaled by 1/S (exact: S = 2^6, or -2^9 for Q4_0's -8 d), the two MFMAs
+      // add 2^-6 sum(x) (hi, lo) times the factors, and the result is scaled back
+      constexpr float S = QT == MOE_Q4_1 ? 64.0f : -512.0f;
+      const half8 ah = amt[wave][0][lane], al = amt[wave][1][lane];
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        const half8 bq = __builtin_bit_cast(half8, m ? P1 : P0);
+        f32x4 t = acc[m] * (1.0f / S);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
+        acc[m] = t * S;
       }
     }
     *reinterpret_cast<f32x4 *>(red[wave][0][lane]) = acc[0];
@@ -789,6 +851,14 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   if ((lane & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, emax);
 }
 
+// N u32x4 registers indexed by a compile-time tile number (named members:
+// an array here was placed in LDS).
+template <int N> struct TileWords {
+  u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = w0, w2 = w0, w3 = w0;
+  static_assert(N >= 1 && N <= 4, "tiles per chunk");
+  __device__ __forceinline__ u32x4 &at(int t) { return t == 0 ? w0 : (t == 1 ? w1 : (t == 2 ? w2 : w3)); }
+};
+
 // LDS of one k_group_down_rows tile (bytes; every part a multiple of 16).
 template <int QT, int KQ>
 struct DownRowsLds {
@@ -796,7 +866,7 @@ struct DownRowsLds {
   static constexpr int PADW = KQ * QBlock<QT>::bytes + 4;     // staged row stride, dwords
   static constexpr size_t bst = 4 * 16 * TPC * PADW;          // staged chunk
   static constexpr size_t red = 4 * 4 * TPC * 64 * 4;         // waves' partial tiles
-  static constexpr size_t asum = 4 * 4 * KQ * 16;             // input sums per K block
+  static constexpr size_t asum = 4 * 2 * 64 * 16;             // input-sum MFMA operands (as in k_group_gateup_rows)
   static constexpr size_t bytes = bst + red + asum + 4 * 4 * 16;  // + rowid, outid, outw, rsh
 };
 
@@ -822,7 +892,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
   // LDS, carved from the kernel's buffer (16-byte aligned; every part a multiple of 16 bytes)
   auto &bst = *reinterpret_cast<uint32_t (*)[CR][PADW]>(smem);
   auto &red = *reinterpret_cast<float (*)[4][TPC][64][4]>(smem + DownRowsLds<QT, KQ>::bst);  // [wave][tile][lane][element]
-  auto &asum = *reinterpret_cast<float (*)[4][KQ][16]>(smem + DownRowsLds<QT, KQ>::bst + DownRowsLds<QT, KQ>::red);
+  auto &amt = *reinterpret_cast<half8 (*)[4][2][64]>(smem + DownRowsLds<QT, KQ>::bst + DownRowsLds<QT, KQ>::red);
   int *rowid = reinterpret_cast<int *>(smem + DownRowsLds<QT, KQ>::bst + DownRowsLds<QT, KQ>::red +
                                        DownRowsLds<QT, KQ>::asum);
   int *outid = rowid + 16;
@@ -866,10 +936,11 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
   const int n = lane & 15, kq = lane >> 4;
   __syncthreads();  // rowid
 
-  // this wave's A fragments (as in k_group_gateup_rows)
+  // this wave's A fragments and input-sum MFMA operand (as in k_group_gateup_rows)
   half8 xh[KQ], xl[KQ];
   {
     const int arow = rowid[n], ash = rsh[n];
+    float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     u32x4 v0[2][2], v1[2][2];
     auto load_group = [&](int g, u32x4 (&a0)[2], u32x4 (&a1)[2]) {
 #pragma unroll
@@ -902,9 +973,19 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
         }
         sum += __shfl_xor(sum, 16, 64);
         sum += __shfl_xor(sum, 32, 64);
-        if (kq == 0) asum[wave][j][n] = sum;
+        if ((j >> 3) == kq) am[j & 7] = sum;
       }
     }
+    half8 ah, al;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float v = __builtin_ldexpf(am[i], -6);
+      const _Float16 h = (_Float16)v;
+      ah[i] = h;
+      al[i] = (_Float16)(v - (float)h);
+    }
+    amt[wave][0][lane] = ah;
+    amt[wave][1][lane] = al;
   }
 
   // staged chunk: CR whole rows, row i at bst[i]
@@ -941,20 +1022,46 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     f32x4 acc[TPC];
 #pragma unroll
     for (int t = 0; t < TPC; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the input-sum MFMA's B operand per tile (as in k_group_gateup_rows;
+    // with KQ <= 8 every block sits in the lanes kq & 1 == 0, and the others
+    // meet zeros in A, so no lane selects)
+    TileWords<TPC> P;
+    uint32_t fprev[TPC];
+    const bool upper = (kq & 1) != 0;
 #pragma unroll
     for (int j = 0; j < KQ; j++) {
       const int jb = wave * KQ + j;
-      const float4 sx4 = *reinterpret_cast<const float4 *>(&asum[wave][j][4 * kq]);
-      const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
 #pragma unroll
       for (int t = 0; t < TPC; t++) {
         float d, mo;
         const half8 q = QStaged<QT>::frag(&bst[16 * t + n][0], 0, jb, kq, d, mo);
+        const uint32_t fw = QFactor<QT>::word(&bst[16 * t + n][0], jb);
+        if (j & 1) {
+          const uint32_t pw = QFactor<QT>::pair(fw, fprev[t]);
+          u32x4 &Pv = P.at(t);
+          if constexpr (KQ > 8)
+            Pv[(j & 7) >> 1] = (((j >> 3) != 0) == upper) ? pw : Pv[(j & 7) >> 1];
+          else
+            Pv[(j & 7) >> 1] = pw;
+        }
+        fprev[t] = fw;
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[j], q, z, 0, 0, 0);
         z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[j], q, z, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[t][i] = __builtin_fmaf(d, z[i], __builtin_fmaf(mo, sx[i], acc[t][i]));
+        for (int i = 0; i < 4; i++) acc[t][i] = __builtin_fmaf(d, z[i], acc[t][i]);
+      }
+    }
+    {
+      constexpr float S = QT == MOE_Q4_1 ? 64.0f : -512.0f;  // (as in k_group_gateup_rows)
+      const half8 ah = amt[wave][0][lane], al = amt[wave][1][lane];
+#pragma unroll
+      for (int t = 0; t < TPC; t++) {
+        const half8 bq = __builtin_bit_cast(half8, P.at(t));
+        f32x4 u = acc[t] * (1.0f / S);
+        u = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, u, 0, 0, 0);
+        u = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, u, 0, 0, 0);
+        acc[t] = u * S;
       }
     }
 #pragma unroll
