@@ -392,6 +392,54 @@ template <> struct QFactor<MOE_Q4_0> {
   }
 };
 
+// 8 nibbles of 8 bytes (the low halves, or the high halves with sh = 4) as
+// exact f16 q in the natural order of the bytes: each nibble is moved into a
+// byte of its own, read as an OCP E4M3 byte -- whose value is q 2^-9 for every
+// q in 0..15 (subnormal below 8, exponent 1 from 8) -- and scaled by 2^9 by
+// the conversion (two values per instruction).
+__device__ __forceinline__ half8 nibbles_e4m3(u32x2 nb, uint32_t sh) {
+  const uint32_t a = (nb.x >> sh) & 0x0F0F0F0Fu, b = (nb.y >> sh) & 0x0F0F0F0Fu;
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 512.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 512.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 512.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 512.0f, true);
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+                    __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(half8, v);
+}
+// As QStaged, with the nibbles in the natural order (nibbles_e4m3): the A
+// operand that meets them is in the same order.
+template <int QT> struct QStagedNat;
+template <> struct QStagedNat<MOE_Q4_1> {
+  static __device__ __forceinline__ half8 frag(const uint32_t *w, int jb, int kq, float &d) {
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[5 * jb] & 0xffffu));
+    const int half = kq & 1;
+    u32x2 nb;
+    nb.x = w[5 * jb + 1 + 2 * half];
+    nb.y = w[5 * jb + 2 + 2 * half];
+    return nibbles_e4m3(nb, (uint32_t)(kq & 2) << 1);
+  }
+};
+template <> struct QStagedNat<MOE_Q4_0> {
+  static __device__ __forceinline__ half8 frag(const uint32_t *w, int jb, int kq, float &d) {
+    const int o = 18 * jb;  // even
+    const uint32_t dw = w[o >> 2];
+    d = (float)__builtin_bit_cast(_Float16, (uint16_t)((o & 2) ? (dw >> 16) : (dw & 0xffffu)));
+    const int s = o + 2 + 8 * (kq & 1), a = s >> 2;
+    const uint32_t w0 = w[a], w1 = w[a + 1], w2 = w[a + 2];
+    u32x2 nb;
+    if (s & 2) {
+      nb.x = __builtin_amdgcn_alignbyte(w1, w0, 2);
+      nb.y = __builtin_amdgcn_alignbyte(w2, w1, 2);
+    } else {
+      nb.x = w0;
+      nb.y = w1;
+    }
+    return nibbles_e4m3(nb, (uint32_t)(kq & 2) << 1);
+  }
+};
+
 // grid.x: routed tiles (16 tokens of one expert) then shared tiles (16 tokens);
 // grid.y: slices of 256 output rows; 4 waves x 64 rows (4 MFMA tiles of 16).
 // Each chunk: registers -> LDS, barrier, issue the next chunk's loads, MFMAs
@@ -683,8 +731,8 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   const int n = lane & 15, kq = lane >> 4;
   __syncthreads();  // rowid
 
-  // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in the
-  // slot order kperm() gives, as f16 hi + lo; the block sums of its tokens
+  // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in slot
+  // i (the order of QStagedNat), as f16 hi + lo; the block sums of its tokens
   // (KQ is a compile-time count, so nothing splits the unrolled loops; the
   // loads go out in groups of 4 blocks, the next group in flight while the
   // current one is converted)
@@ -718,8 +766,8 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
         for (int i = 0; i < 8; i++) {
           const float v = __builtin_ldexpf(xv[i], ash);
           const _Float16 h = (_Float16)v;
-          xh[j][kperm(i)] = h;
-          xl[j][kperm(i)] = (_Float16)(v - (float)h);
+          xh[j][i] = h;
+          xl[j][i] = (_Float16)(v - (float)h);
           sum += v;
         }
         sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
@@ -787,8 +835,8 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
       const int jb = wave * KQ + j;
 #pragma unroll
       for (int m = 0; m < 2; m++) {
-        float d, mo;
-        const half8 q = QStaged<QT>::frag(&bst[m][n][0], 0, jb, kq, d, mo);
+        float d;
+        const half8 q = QStagedNat<QT>::frag(&bst[m][n][0], jb, kq, d);
         const uint32_t fw = QFactor<QT>::word(&bst[m][n][0], jb);
         uint32_t &fprev = m ? fprev1 : fprev0;
         u32x4 &Pv = m ? P1 : P0;
@@ -967,8 +1015,8 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
         for (int i = 0; i < 8; i++) {
           const float v = __builtin_ldexpf(xv[i], ash);
           const _Float16 h = (_Float16)v;
-          xh[j][kperm(i)] = h;
-          xl[j][kperm(i)] = (_Float16)(v - (float)h);
+          xh[j][i] = h;
+          xl[j][i] = (_Float16)(v - (float)h);
           sum += v;
         }
         sum += __shfl_xor(sum, 16, 64);
@@ -1033,8 +1081,8 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
       const int jb = wave * KQ + j;
 #pragma unroll
       for (int t = 0; t < TPC; t++) {
-        float d, mo;
-        const half8 q = QStaged<QT>::frag(&bst[16 * t + n][0], 0, jb, kq, d, mo);
+        float d;
+        const half8 q = QStagedNat<QT>::frag(&bst[16 * t + n][0], jb, kq, d);
         const uint32_t fw = QFactor<QT>::word(&bst[16 * t + n][0], jb);
         if (j & 1) {
           const uint32_t pw = QFactor<QT>::pair(fw, fprev[t]);
