@@ -118,23 +118,26 @@ template <> struct QBlock<MOE_Q8_0> {
 };
 
 // sum over one nibble word's 8 elements of q*x: low nibbles pair with
-// x[4k..4k+3], high nibbles with x[16+4k..16+4k+3].  The high nibbles are
-// masked in place (value 16q) and their partial is scaled by 1/16 at the end.
+// x[4k..4k+3], high nibbles with x[16+4k..16+4k+3].  Each nibble is moved into
+// a byte of its own and the bytes are read as OCP E4M3 values -- q 2^-9 for
+// every q in 0..15 -- and scaled by 2^9 by the conversion, two per instruction,
+// as exact f16 q; each product q*x is then one mixed f16 x f32 fma (exact
+// product, one rounding, as an f32 fma of the converted value).
 __device__ __forceinline__ void nib_word_dot(uint32_t w, const float4 &xl, const float4 &xh, float &lo,
                                              float &hi) {
-  uint32_t l = w & 0x0F0F0F0Fu, h = w & 0xF0F0F0F0u;
-  // hide the masks' known bits from the compiler so that each byte converts
-  // with one v_cvt_f32_ubyteN (it otherwise extracts with v_bfe first)
-  asm("" : "+v"(l));
-  asm("" : "+v"(h));
-  lo = __builtin_fmaf((float)(l & 0xff), xl.x, lo);
-  lo = __builtin_fmaf((float)((l >> 8) & 0xff), xl.y, lo);
-  lo = __builtin_fmaf((float)((l >> 16) & 0xff), xl.z, lo);
-  lo = __builtin_fmaf((float)(l >> 24), xl.w, lo);
-  hi = __builtin_fmaf((float)(h & 0xff), xh.x, hi);
-  hi = __builtin_fmaf((float)((h >> 8) & 0xff), xh.y, hi);
-  hi = __builtin_fmaf((float)((h >> 16) & 0xff), xh.z, hi);
-  hi = __builtin_fmaf((float)(h >> 24), xh.w, hi);
+  const uint32_t l = w & 0x0F0F0F0Fu, h = (w >> 4) & 0x0F0F0F0Fu;
+  const auto l01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l, 512.0f, false);
+  const auto l23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l, 512.0f, true);
+  const auto h01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h, 512.0f, false);
+  const auto h23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h, 512.0f, true);
+  lo = __builtin_fmaf((float)l01[0], xl.x, lo);
+  lo = __builtin_fmaf((float)l01[1], xl.y, lo);
+  lo = __builtin_fmaf((float)l23[0], xl.z, lo);
+  lo = __builtin_fmaf((float)l23[1], xl.w, lo);
+  hi = __builtin_fmaf((float)h01[0], xh.x, hi);
+  hi = __builtin_fmaf((float)h01[1], xh.y, hi);
+  hi = __builtin_fmaf((float)h23[0], xh.z, hi);
+  hi = __builtin_fmaf((float)h23[1], xh.w, hi);
 }
 
 // Q4 block dot with its 32 inputs xb (LDS) and their sum sx.
@@ -149,7 +152,7 @@ __device__ __forceinline__ float block_dot_q4(const Raw5 &b, uint32_t off, const
     float4 xh = *reinterpret_cast<const float4 *>(xb + 16 + 4 * k);
     nib_word_dot(QBlock<QT>::nib(b, off, k), xl, xh, lo, hi);
   }
-  float q = __builtin_fmaf(hi, 0.0625f, lo);
+  float q = lo + hi;
   return __builtin_fmaf(d, q, m * sx);
 }
 
