@@ -29,6 +29,9 @@ namespace moe {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   // Sizes are rounded up to whole dwords: a dword holding the last byte of an
@@ -116,6 +119,22 @@ template <> struct QBlock<MOE_Q8_0> {
     return w ^ 0x80808080u;
   }
 };
+
+// 8 nibbles of 8 bytes (the low halves, or the high halves with sh = 4) as
+// exact f16 q in the natural order of the bytes: each nibble is moved into a
+// byte of its own, read as an OCP E4M3 byte -- whose value is q 2^-9 for every
+// q in 0..15 (subnormal below 8, exponent 1 from 8) -- and scaled by 2^9 by
+// the conversion (two values per instruction).
+__device__ __forceinline__ half8 nibbles_e4m3(u32x2 nb, uint32_t sh) {
+  const uint32_t a = (nb.x >> sh) & 0x0F0F0F0Fu, b = (nb.y >> sh) & 0x0F0F0F0Fu;
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 512.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 512.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 512.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 512.0f, true);
+  const u32x4 v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+                   __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(half8, v);
+}
 
 // sum over one nibble word's 8 elements of q*x: low nibbles pair with
 // x[4k..4k+3], high nibbles with x[16+4k..16+4k+3].  Each nibble is moved into
