@@ -12,8 +12,10 @@
 //    block count) owns one output row; lane i reads blocks i, i+LPR, ... with
 //    one 16-byte and one 4-byte buffer load per 20-byte block, so a group's
 //    loads cover consecutive bytes of the row and rows stay whole per group;
-//  * nibbles are unpacked in registers (mask, v_cvt_f32_ubyte*, FMA) against
-//    the input block staged in LDS; the Q4_1 offset term m*sum(x) uses the
+//  * nibbles are unpacked in registers against the input block staged in
+//    LDS: each goes to a byte of its own, two bytes convert to exact f16 q in
+//    one E4M3 conversion, and each product is a mixed f16 x f32 fma (Q8_0
+//    bytes: v_cvt_f32_ubyte*, FMA); the Q4_1 offset term m*sum(x) uses the
 //    per-block input sums staged beside it;
 //  * gate and up rows of the same f are streamed by the same lanes so the
 //    SwiGLU is applied in registers and act is written once;

@@ -28,8 +28,10 @@
 // is split as x = hi + lo (two f16, about 22 significant bits); the block's
 // f32 scale d and offset term m * sum_k x_k are applied per block in f32
 // (value d*q + m; Q4_0 is m = -8d).  The nibbles enter the MFMA as exact f16
-// values: a mask-or builds the f16 1024 + q, a packed f16 subtract removes
-// the 1024.
+// values: in the row-streaming kernels through the E4M3 conversion
+// (nibbles_e4m3), in k_group_gemm by a mask-or that builds the f16 1024 + q
+// and a packed f16 subtract that removes the 1024.  The row-streaming kernels
+// add the offset term on the matrix cores too (two MFMAs per tile and chunk).
 //
 // f16 has a narrow exponent range, so every input row (a token's x, a pair's
 // or a token's act) is first scaled by a power of two that puts its largest
