@@ -58,10 +58,15 @@ KERNEL_SYMBOLS = {"gateup_swiglu": "k_gateup_swiglu", "group_gateup": "k_group_g
 
 
 def kernel_source_hash(kernel):
+    """Hash of the code (comments and blank space removed) of the sources a kernel is built from."""
+    import re
     h = hashlib.sha256()
     for fn in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "sparse_moe_ffn_topk_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_moe_ffn_topk_amd", "csrc", fn)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -134,9 +139,9 @@ def write_traffic(args):
                 f"{wscale}.\n\n")
         f.write("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes per launch |\n|---|---|---|---|---|\n")
         f.write(f"| {rec['kernel']} | {nd} | {fetch:.1f} | {write:.1f} | {nbytes:,} |\n\n")
-        f.write(f"Kernel source hash {rec['kernel_source_sha']} (the bench reports this traffic only while the "
-                f"sources are unchanged).  Written by `python bench.py --workload {args.workload} --write-traffic "
-                f"...`.\n")
+        f.write(f"Kernel source hash {rec['kernel_source_sha']} (of the code with comments removed; the bench reports "
+                f"this traffic only while that code is unchanged).  Written by `python bench.py --workload "
+                f"{args.workload} --write-traffic ...`.\n")
     print(json.dumps(rec))
 
 
