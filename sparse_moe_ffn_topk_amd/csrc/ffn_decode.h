@@ -31,9 +31,14 @@
 namespace moe {
 
 // Blocks per lane held in registers per chunk, two chunks in flight: 2 in the
-// gate||up kernel (whose blocks then fit two to a CU), 4 in the down kernel.
+// gate||up kernel (whose blocks then fit two to a CU); in the down kernel 4
+// where a row's task list is split over waves (one token), and 2 where it is
+// not (several tokens: about 110 registers, so four waves per SIMD keep a
+// launch of a thousand blocks resident at once, against two at 4 per chunk
+// and 204 registers).
 constexpr int NCH = 2;
 constexpr int NCHD = 4;
+constexpr int NCHD_UNSPLIT = 2;
 // Offset past every buffer resource's range: loads there return zeros without
 // touching memory, and an all-zero block contributes exactly 0 to a dot.
 constexpr uint32_t OOB = 0x7ffffff0u;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256) void k_decode_prelude(
 // LDS in split order (fixed: bitwise reproducible).  A block is (NT/64)/S row
 // groups of 64/LPR rows (SPLIT == false: S is 1).  The token's ids and
 // weights are fetched into lanes 0..k-1 ahead of everything else.
-template <int QT, int LPR, int XR, int NT, bool SPLIT>
+template <int QT, int LPR, int XR, int NT, bool SPLIT, int CH>
 __global__ __launch_bounds__(NT) void k_down_accum(
     const float *__restrict__ act, const int32_t *__restrict__ ids, const float *__restrict__ wts, int H, int k,
     int F, int SF, const uint8_t *__restrict__ down_exps, const uint8_t *__restrict__ down_sh,
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(NT) void k_down_accum(
   const int bplF = nbF / LPR, bplS = nbS / LPR;  // LPR divides both
   const int nq = bplS + k * bplF;
   const int nqw = (nq - ws + S - 1) / S;  // this wave's tasks: q = ws + S * i
-  const int nch = (nqw + NCHD - 1) / NCHD;
+  const int nch = (nqw + CH - 1) / CH;
   const size_t mat = (size_t)H * nbF * BS;
   const uint32_t rowF = (uint32_t)h * nbF * BS;
   const uint32_t rowS = (uint32_t)h * nbS * BS;
@@ -373,19 +378,19 @@ __global__ __launch_bounds__(NT) void k_down_accum(
     return (live && q < nq) ? (j < k ? rowF : rowS) + (uint32_t)block(q, j) * BS : OOB;
   };
   typedef typename QBlock<QT>::Raw Raw;
-  Raw A[NCHD], B[NCHD];
+  Raw A[CH], B[CH];
   auto load = [&](Raw *W, int c) {
 #pragma unroll
-    for (int i = 0; i < NCHD; i++) {
-      const int q = ws + S * (c * NCHD + i), j = min(pick(q), k);
+    for (int i = 0; i < CH; i++) {
+      const int q = ws + S * (c * CH + i), j = min(pick(q), k);
       W[i] = QBlock<QT>::load(rsrc_for(j), offset(q, j));
     }
   };
   float acc = 0.f;
   auto compute = [&](const Raw *W, int c) {
 #pragma unroll
-    for (int i = 0; i < NCHD; i++) {
-      const int q = ws + S * (c * NCHD + i), j = min(pick(q), k);
+    for (int i = 0; i < CH; i++) {
+      const int q = ws + S * (c * CH + i), j = min(pick(q), k);
       const int ab = min(j * nbF + block(q, j), nbAll - 1);  // staged act block (shared row after routed)
       const float d = block_dot<QT>(W[i], offset(q, j), xs + ab * XSTRIDE, sx[ab]);
       const int wbits = j < k ? __builtin_amdgcn_readlane(__float_as_int(wt_v), j) : __float_as_int(1.0f);
@@ -440,7 +445,8 @@ static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_
 }
 template <int QT, int LPR, int XR, int NT, bool SPLIT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT, SPLIT>), grid, dim3(NT), (uint32_t)lds, st, (const float *)a.act,
+  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT, SPLIT, SPLIT ? NCHD : NCHD_UNSPLIT>), grid, dim3(NT), (uint32_t)lds, st,
+             (const float *)a.act,
              (const int32_t *)a.ids, (const float *)a.wts, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid,
              a.down_split);
 }
