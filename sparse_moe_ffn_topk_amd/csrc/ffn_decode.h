@@ -30,13 +30,16 @@
 
 namespace moe {
 
-// Blocks per lane held in registers per chunk, two chunks in flight: 2 in the
-// gate||up kernel (whose blocks then fit two to a CU); in the down kernel 4
+// Blocks per lane held in registers per chunk, two chunks in flight: in the
+// gate||up kernel 2 for one token (whose blocks then fit two to a CU) and 1
+// for several (95 registers against 138: five waves per SIMD instead of
+// three, for launches of a thousand blocks and more); in the down kernel 4
 // where a row's task list is split over waves (one token), and 2 where it is
 // not (several tokens: about 110 registers, so four waves per SIMD keep a
 // launch of a thousand blocks resident at once, against two at 4 per chunk
 // and 204 registers).
 constexpr int NCH = 2;
+constexpr int NCH_MULTI = 1;
 constexpr int NCHD = 4;
 constexpr int NCHD_UNSPLIT = 2;
 // Offset past every buffer resource's range: loads there return zeros without
@@ -98,7 +101,7 @@ __device__ __forceinline__ float silu_mul(float g, float u, float L) {
 // act row of token t: its k routed rows of F, then the shared row of SF.
 // With logits != NULL every block routes its token (select_load/select_rank)
 // and block (0, t) writes the token's ids and weights; otherwise ids are read.
-template <int QT, int LPR, int XR>
+template <int QT, int LPR, int XR, int CH>
 __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
     const float *__restrict__ x, int32_t *__restrict__ ids, float *__restrict__ wts,
     const float *__restrict__ logits, const float *__restrict__ bias, SelParams P, int H, int k, int F, int SF,
@@ -135,12 +138,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   else if (!is_sh && wlive)
     e = ids[(size_t)t * k + j];
 
-  const int nch = (nbH / LPR + NCH - 1) / NCH;  // LPR divides nbH
+  const int nch = (nbH / LPR + CH - 1) / CH;  // LPR divides nbH
   typedef typename QBlock<QT>::Raw Raw;
-  Raw ga[NCH], ua[NCH], gb[NCH], ub[NCH];
+  Raw ga[CH], ua[CH], gb[CH], ub[CH];
   rsrc_t rg = make_rsrc(gate_sh, (uint32_t)SF * rowbytes), ru = make_rsrc(up_sh, (uint32_t)SF * rowbytes);
   auto offset = [&](int c, int i) {
-    const int b = li + LPR * (c * NCH + i);
+    const int b = li + LPR * (c * CH + i);
     return (live && b < nbH) ? rowoff + (uint32_t)b * BS : OOB;
   };
   // early: every wave issues the same loads (routed waves at the out-of-range
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   // routing waits for exactly its own inputs
   auto load = [&](Raw *G, Raw *U, int c, bool early) {
 #pragma unroll
-    for (int i = 0; i < NCH; i++) {
+    for (int i = 0; i < CH; i++) {
       const uint32_t off = (early && !is_sh) ? OOB : offset(c, i);
       G[i] = QBlock<QT>::load(rg, off);
       U[i] = QBlock<QT>::load(ru, off);
@@ -176,9 +179,9 @@ __global__ __launch_bounds__(256, 2) void k_gateup_swiglu(
   float g = 0.f, v = 0.f;
   auto compute = [&](const Raw *G, const Raw *U, int c) {
 #pragma unroll
-    for (int i = 0; i < NCH; i++) {
+    for (int i = 0; i < CH; i++) {
       const uint32_t off = offset(c, i);
-      const int b = min(li + LPR * (c * NCH + i), nbH - 1);
+      const int b = min(li + LPR * (c * CH + i), nbH - 1);
       const float *xb = xs + b * XSTRIDE;
       const float s = sx[b];
       g += block_dot<QT>(G[i], off, xb, s);
@@ -436,12 +439,18 @@ static inline int xr_for(int n, int nt) {  // float4s per thread to stage n floa
   return xr;
 }
 
+template <int QT, int LPR, int XR, int CH>
+static void gateup_launch_ch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR, CH>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
+             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.sf_tasks, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim,
+             a.lim_sh, a.act);
+}
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  MOE_LAUNCH(3, (k_gateup_swiglu<QT, LPR, XR>), grid, dim3(256), (uint32_t)lds, st, a.x, a.ids, a.wts, a.logits,
-             a.bias, a.sel, a.H, a.k, a.F, a.SF, a.sf_tasks, a.gate_exps, a.up_exps, a.gate_sh, a.up_sh, a.lim,
-             a.lim_sh,
-             a.act);
+  if (a.T > 1)
+    gateup_launch_ch<QT, LPR, XR, NCH_MULTI>(a, grid, lds, st);
+  else
+    gateup_launch_ch<QT, LPR, XR, NCH>(a, grid, lds, st);
 }
 template <int QT, int LPR, int XR, int NT, bool SPLIT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
