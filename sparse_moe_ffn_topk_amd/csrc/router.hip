@@ -39,7 +39,7 @@ constexpr uint32_t ROUTER_OOB = 0x7ffffff0u;
 // xn = f32(x * s * g), s = 1/sqrt(ss/H + eps), before the dot; block 0 writes
 // xn for the FFN kernels.  Every block computes the same xn the same way.
 template <int TPW, int NC>
-__global__ __launch_bounds__(256) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
+__global__ __launch_bounds__(512) void k_router_rows(const float *__restrict__ W, const float *__restrict__ x,
                                                      int H, int E, int T, float *__restrict__ logits,
                                                      const float *__restrict__ gnorm, float eps,
                                                      float *__restrict__ xn_out) {
@@ -335,7 +335,7 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
     // Chunks per lane and pass: the whole row in one pass up to H = 4096.
     const int n16 = (H + 3) / 4;
     const int nc = (n16 + 63) / 64;
-    const dim3 grid(E), block(64 * (T < 4 ? T : 4));
+    const dim3 grid(E), block(64 * T);  // one wave per token
 #define MOE_ROUTER_ROWS(TPW)                                                                             \
   do {                                                                                                   \
     if (nc <= 2)                                                                                         \
@@ -349,10 +349,7 @@ hipError_t launch_router_logits(const float *W, const float *x, int H, int E, in
     else                                                                                                 \
       MOE_LAUNCH(1, (k_router_rows<TPW, 16>), grid, block, 0u, st, W, x, H, E, T, logits, gnorm, eps, xn);\
   } while (0)
-    if (T <= 4)
-      MOE_ROUTER_ROWS(1);
-    else
-      MOE_ROUTER_ROWS(2);
+    MOE_ROUTER_ROWS(1);
 #undef MOE_ROUTER_ROWS
   } else {
     const dim3 grid((E + 15) / 16, (T + 31) / 32);
