@@ -632,8 +632,10 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // The grid is one-dimensional: the shared expert's tiles x row slices come
 // first, then the routed tiles x the routed row slices, so no block is
 // launched for a slice past a matrix's rows.  Within each part, work is
-// ordered slice-major and dealt to the XCDs in runs (xcd_run): one XCD
-// takes every tile of a shared slice, and an expert's tiles share an L2.
+// dealt to the XCDs in runs (xcd_run).  The shared part is ordered
+// slice-major, so one XCD takes every tile of a shared slice; the routed part
+// tile-major, so one XCD takes every slice of a routed tile (its token rows
+// are fetched into one L2, once) and an expert's tiles share that L2.
 constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
 constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
@@ -675,8 +677,9 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     const int v = nt * ((a.F + RS_GU_RB - 1) / RS_GU_RB);
     if (b - ns >= v) return;
     const int l = xcd_run(b - ns, v);
-    bx = l % nt;
-    by = l / nt;
+    const int nsl = (a.F + RS_GU_RB - 1) / RS_GU_RB;
+    bx = l / nsl;
+    by = l % nsl;
   }
   int e = 0, first = 0, ntok, R;
   const uint8_t *g0, *u0;
@@ -1119,7 +1122,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
 // their longer blocks start first and overlap the routed ones (K = F, KQF
 // blocks per wave, RS_RB rows each) that follow.  KQF or KQS is 0 where the
 // layer has no routed or no shared expert.  Each part is dealt to the XCDs
-// in slice-major runs, as in k_group_gateup_rows.
+// in runs as in k_group_gateup_rows (shared slice-major, routed tile-major).
 template <int QT, int KQF, int KQS>
 __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles, int rbs) {
   constexpr size_t lf = KQF > 0 ? DownRowsLds<QT, KQF>::bytes : 0, ls = KQS > 0 ? DownRowsLds<QT, KQS>::bytes : 0;
@@ -1138,7 +1141,8 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shti
       const int v = nt * ((a.H + RS_RB - 1) / RS_RB);
       if (b - ns >= v) return;
       const int l = xcd_run(b - ns, v);
-      down_rows_tile<QT, KQF>(a, l % nt, l / nt, RS_RB, smem);
+      const int nsl = (a.H + RS_RB - 1) / RS_RB;
+      down_rows_tile<QT, KQF>(a, l / nsl, l % nsl, RS_RB, smem);
     }
   }
 }
