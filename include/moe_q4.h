@@ -227,14 +227,16 @@ enum {
   MOE_KERNEL_SELECT = 2,  /* scores, group limit, top-k, weights         */
   MOE_KERNEL_GATEUP = 3,  /* gate||up GEMV + SwiGLU (decode)             */
   MOE_KERNEL_DOWN = 4,    /* down GEMV + weighted accumulate (decode)    */
-  MOE_KERNEL_SORT = 5,    /* pairs grouped by expert (grouped path)      */
+  MOE_KERNEL_SORT = 5,    /* pairs grouped by expert (grouped path); the
+                             same launch takes the input rows' scales     */
   MOE_KERNEL_GROUP_GATEUP = 6, /* grouped gate||up MFMA GEMM + SwiGLU     */
   MOE_KERNEL_GROUP_DOWN = 7,   /* grouped down MFMA GEMM, weighted        */
   MOE_KERNEL_COMBINE = 8,      /* per-token sum into the residual         */
   MOE_KERNEL_RMSNORM = 9,      /* pre-FFN RMSNorm (when ffn_norm is given) */
   MOE_KERNEL_PRELUDE = 10,     /* decode of 2+ tokens: per-token select and
                                   the shared expert's gate||up for all tokens */
-  MOE_KERNEL_ROW_SCALE = 11    /* grouped path: the input rows' power-of-two
+  MOE_KERNEL_ROW_SCALE = 11    /* grouped path of a layer without routed
+                                  experts: the input rows' power-of-two
                                   scales for the f16 MFMA operands           */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);

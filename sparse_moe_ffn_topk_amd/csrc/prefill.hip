@@ -11,10 +11,12 @@
 // are read once per chunk.
 //
 // Steps:
-//  1. k_sort_by_expert (one block): a stable counting sort of the pairs by
+//  1. k_sort_by_expert (block 0): a stable counting sort of the pairs by
 //     expert, pair order (tokens ascending) within an expert: per-expert
 //     token bit sets, popcount prefixes, an exclusive scan (wave shuffles) -> offsets, pos[p],
-//     perm[pos], and the list of 16-token tiles of every expert.
+//     perm[pos], and the list of 16-token tiles of every expert.  Its other
+//     blocks take the input rows' largest exponents (below), which do not
+//     depend on the sort, so both share one launch.
 //  2. k_group_gemm<GATEUP>: per (tile, 256-row slice): g and u for 16 tokens
 //     x 256 rows, SwiGLU in registers, act rows written in sorted order; the
 //     shared expert runs as extra tiles over all tokens.
@@ -46,6 +48,28 @@
 namespace moe {
 
 
+// Biased f32 exponent field of v.
+__device__ __forceinline__ int bexp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
+
+// Largest biased f32 exponent of each of nrows rows of K floats (one wave per
+// row: rows r = wpb * b + wave of block b of nb), and nzero ints zeroed.
+__device__ __forceinline__ void row_exp_part(const float *__restrict__ rows, int nrows, int K, int32_t *__restrict__ eb,
+                                             int32_t *__restrict__ zero, int nzero, int b, int nb) {
+  const int nt = (int)blockDim.x, wpb = nt >> 6;
+  for (int i = b * nt + (int)threadIdx.x; i < nzero; i += nb * nt) zero[i] = 0;
+  const int r = b * wpb + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= nrows) return;
+  const float4 *p = reinterpret_cast<const float4 *>(rows + (size_t)r * K);
+  int m = 0;
+  for (int i = lane; i < K / 4; i += 64) {
+    const float4 v = p[i];
+    m = max(m, max(max(bexp(v.x), bexp(v.y)), max(bexp(v.z), bexp(v.w))));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
+  if (lane == 0) eb[r] = m;
+}
+
 // ------------------------------------------------------------------ sort --
 
 // One block of 1024 threads; T <= PREFILL_CHUNK, E <= 512.  The rank of pair
@@ -65,11 +89,19 @@ __device__ __forceinline__ int earlier_picks(P ids, int t, int k, int j, int e) 
 }
 
 // STAGE: the ids are first copied to LDS (after bits and pre) and read there.
+// Block 0 sorts; blocks 1.. take the T input rows' largest exponents (H floats
+// each, into xexp) and zero nzero words at aexp, as k_row_exp does.
 template <bool STAGE>
 __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ gids, int T, int k, int E,
                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ tiles,
-                                                         int32_t *__restrict__ ntiles) {
+                                                         int32_t *__restrict__ ntiles, const float *__restrict__ x,
+                                                         int H, int32_t *__restrict__ xexp,
+                                                         int32_t *__restrict__ aexp, int nzero) {
+  if (blockIdx.x > 0) {
+    row_exp_part(x, T, H, xexp, aexp, nzero, (int)blockIdx.x - 1, (int)gridDim.x - 1);
+    return;
+  }
   extern __shared__ uint32_t lds[];
   const int W = (T + 31) >> 5;
   uint32_t *bits = lds;                       // [E][W]
@@ -230,29 +262,17 @@ struct GemmArgs {
                              // GATEUP raises them with atomicMax, DOWN reads them
 };
 
-// Biased f32 exponent of |v|, and the power-of-two shift that puts a row
-// whose largest biased exponent is eb in [2^14, 2^15) (2^(eb - 127) <= max
-// < 2^(eb - 126)).
-__device__ __forceinline__ int bexp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
+// The power-of-two shift that puts a row whose largest biased exponent is eb
+// in [2^14, 2^15) (2^(eb - 127) <= max < 2^(eb - 126)).
 __device__ __forceinline__ int row_shift(int eb) { return 141 - eb; }
 
 // Largest biased exponent of |x| over each of nrows rows of K floats (one
 // wave per row); the grid also zeroes nzero words at zero (the act rows'
-// exponents, raised later by atomicMax).
+// exponents, raised later by atomicMax).  For a layer with no routed pairs;
+// otherwise the sort's launch does this in its blocks past the first.
 __global__ __launch_bounds__(256) void k_row_exp(const float *__restrict__ rows, int nrows, int K,
                                                  int32_t *__restrict__ eb, int32_t *__restrict__ zero, int nzero) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < nzero; i += gridDim.x * 256) zero[i] = 0;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= nrows) return;
-  const float4 *p = reinterpret_cast<const float4 *>(rows + (size_t)r * K);
-  int m = 0;
-  for (int i = lane; i < K / 4; i += 64) {
-    const float4 v = p[i];
-    m = max(m, max(max(bexp(v.x), bexp(v.y)), max(bexp(v.z), bexp(v.w))));
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
-  if (lane == 0) eb[r] = m;
+  row_exp_part(rows, nrows, K, eb, zero, nzero, blockIdx.x, gridDim.x);
 }
 
 // K is walked in chunks of KB blocks.  Per chunk a block stages, in LDS, the
@@ -1211,22 +1231,23 @@ static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, i
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
   hipError_t err;
+  // the sort, and the rows' power-of-two scales: x now, the act rows' exponents
+  // zeroed for the gate||up epilogue (in the sort's launch, blocks past the first)
+  const int nzero = T * (k + 1);
   if (k > 0) {  // (a dense layer, k == 0, has no routed pairs to sort)
+    const int nexp = max((T + 15) / 16, (nzero + 1023) / 1024);
     if (sort_stages_ids(T, k, E))
-      MOE_LAUNCH(5, k_sort_by_expert<true>, dim3(1), dim3(1024), (uint32_t)(prefill_sort_lds_bytes(T, E) + T * k * 4),
-                 st, p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
+      MOE_LAUNCH(5, k_sort_by_expert<true>, dim3(1 + nexp), dim3(1024),
+                 (uint32_t)(prefill_sort_lds_bytes(T, E) + T * k * 4), st, p.ids, T, k, E, p.offsets, p.pos, p.perm,
+                 p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero);
     else
-      MOE_LAUNCH(5, k_sort_by_expert<false>, dim3(1), dim3(1024), (uint32_t)prefill_sort_lds_bytes(T, E), st,
-                 p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  // the rows' power-of-two scales: x now, the act rows' exponents zeroed for the gate||up epilogue
-  {
-    const int nzero = T * (k + 1);
+      MOE_LAUNCH(5, k_sort_by_expert<false>, dim3(1 + nexp), dim3(1024), (uint32_t)prefill_sort_lds_bytes(T, E), st,
+                 p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero);
+  } else {
     const int nblk = max((T + 3) / 4, (nzero + 255) / 256);
     MOE_LAUNCH(11, k_row_exp, dim3(nblk), dim3(256), 0u, st, p.x, T, p.H, p.xexp, p.aexp, nzero);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   GemmArgs g{};
   g.T = T;
   g.k = k;
