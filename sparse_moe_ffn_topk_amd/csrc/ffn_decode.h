@@ -30,16 +30,18 @@
 
 namespace moe {
 
-// Blocks per lane held in registers per chunk, two chunks in flight: in the
-// gate||up kernel 2 for one token (whose blocks then fit two to a CU) and 1
-// for several (95 registers against 138: five waves per SIMD instead of
-// three, for launches of a thousand blocks and more); in the down kernel 4
-// where a row's task list is split over waves (one token), and 2 where it is
-// not (several tokens: about 110 registers, so four waves per SIMD keep a
-// launch of a thousand blocks resident at once, against two at 4 per chunk
-// and 204 registers).
-constexpr int NCH = 2;
-constexpr int NCH_MULTI = 1;
+// Blocks per lane held in registers per chunk, two chunks in flight.  In the
+// gate||up kernel 1 (95 registers against 138 at 2: five waves per SIMD
+// instead of three for launches of a thousand blocks and more, and for one
+// token a lane's two blocks of a 32-lane row go out as two chunks, so the
+// first is computed while the second arrives), except 2 for one token of
+// Q4_0 blocks and for one token of a dense layer, where 2 measured faster.  In
+// the down kernel 4 where a row's task list is split over waves (one token),
+// and 2 where it is not (several tokens: about 110 registers, so four waves
+// per SIMD keep a launch of a thousand blocks resident at once, against two at
+// 4 per chunk and 204 registers).
+constexpr int NCH_GU = 1;
+constexpr int NCH_GU_ONE_Q40 = 2;
 constexpr int NCHD = 4;
 constexpr int NCHD_UNSPLIT = 2;
 // Offset past every buffer resource's range: loads there return zeros without
@@ -447,10 +449,10 @@ static void gateup_launch_ch(const DecodeArgs &a, dim3 grid, size_t lds, hipStre
 }
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.T > 1)
-    gateup_launch_ch<QT, LPR, XR, NCH_MULTI>(a, grid, lds, st);
+  if (a.T == 1 && (QT == MOE_Q4_0 || a.k == 0))
+    gateup_launch_ch<QT, LPR, XR, NCH_GU_ONE_Q40>(a, grid, lds, st);
   else
-    gateup_launch_ch<QT, LPR, XR, NCH>(a, grid, lds, st);
+    gateup_launch_ch<QT, LPR, XR, NCH_GU>(a, grid, lds, st);
 }
 template <int QT, int LPR, int XR, int NT, bool SPLIT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
@@ -539,10 +541,11 @@ template <int QT>
 static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
   const int nbH = a.H / 32;
   int lpr = lanes_for(nbH);
-  // one token, Q4 blocks: 32 lanes per row where they divide the row (each
-  // lane's blocks then fit one register chunk, and the launch has twice the
-  // blocks; measured slower for Q8_0's 34-byte blocks, which stay at 16)
-  if (QT != MOE_Q8_0 && a.T == 1 && lpr == 16 && nbH % 32 == 0 && nbH / 32 <= NCH) lpr = 32;
+  // one token, Q4 blocks: 32 lanes per row where they divide the row and
+  // leave a lane at most two blocks (all in flight at once, and the launch has
+  // twice the blocks; measured slower for Q8_0's 34-byte blocks, which stay at
+  // 16)
+  if (QT != MOE_Q8_0 && a.T == 1 && lpr == 16 && nbH % 32 == 0 && nbH / 32 <= 2) lpr = 32;
   const int rw = 64 / lpr;  // rows per wave task
   const int tasks = (a.sf_tasks + rw - 1) / rw + a.k * ((a.F + rw - 1) / rw);
   if (tasks == 0) return hipSuccess;  // (a dense layer whose rows the prelude computed)
