@@ -39,7 +39,8 @@ namespace moe {
 // the down kernel 4 where a row's task list is split over waves (one token),
 // and 2 where it is not (several tokens: about 110 registers, so four waves
 // per SIMD keep a launch of a thousand blocks resident at once, against two at
-// 4 per chunk and 204 registers).
+// 4 per chunk and 204 registers); a split list whose waves' task counts are
+// not a multiple of 4 takes one block per chunk (down_launch_nt).
 constexpr int NCH_GU = 1;
 constexpr int NCH_GU_ONE_Q40 = 2;
 constexpr int NCHD = 4;
@@ -454,12 +455,29 @@ static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_
   else
     gateup_launch_ch<QT, LPR, XR, NCH_GU>(a, grid, lds, st);
 }
-template <int QT, int LPR, int XR, int NT, bool SPLIT>
-static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
-  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT, SPLIT, SPLIT ? NCHD : NCHD_UNSPLIT>), grid, dim3(NT), (uint32_t)lds, st,
-             (const float *)a.act,
+template <int QT, int LPR, int XR, int NT, bool SPLIT, int CH>
+static void down_launch_ch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  MOE_LAUNCH(4, (k_down_accum<QT, LPR, XR, NT, SPLIT, CH>), grid, dim3(NT), (uint32_t)lds, st, (const float *)a.act,
              (const int32_t *)a.ids, (const float *)a.wts, a.H, a.k, a.F, a.SF, a.down_exps, a.down_sh, a.resid,
              a.down_split);
+}
+// Split task lists: NCHD blocks per chunk when a wave's task count is a
+// multiple of it (every chunk full), else one (chunks then follow each other
+// two in flight).  Measured per layer step against NCHD throughout: LFM2.5
+// (3 tasks a wave) 17.2 -> 16.3 us, with Q8_0 experts 22.6 -> 20.2, Ling (7)
+// 24.0-24.4 -> 23.8; Flint (4) keeps NCHD (one block per chunk: 14.8 against
+// 14.3).
+template <int QT, int LPR, int XR, int NT, bool SPLIT>
+static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  if constexpr (SPLIT) {
+    const int nq = a.k * ((a.F / 32) / LPR) + (a.SF / 32) / LPR;
+    const int per_wave = (nq + a.down_split - 1) / a.down_split;
+    if (per_wave % NCHD != 0) {
+      down_launch_ch<QT, LPR, XR, NT, true, 1>(a, grid, lds, st);
+      return;
+    }
+  }
+  down_launch_ch<QT, LPR, XR, NT, SPLIT, SPLIT ? NCHD : NCHD_UNSPLIT>(a, grid, lds, st);
 }
 template <int QT, int LPR, int XR>
 static void down_launch_128(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
