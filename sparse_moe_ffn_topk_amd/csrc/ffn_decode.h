@@ -37,14 +37,15 @@ namespace moe {
 // first is computed while the second arrives), except 2 for one token of
 // Q4_0 blocks and for one token of a dense layer, where 2 measured faster.  In
 // the down kernel 4 where a row's task list is split over waves (one token),
-// and 2 where it is not (several tokens: about 110 registers, so four waves
-// per SIMD keep a launch of a thousand blocks resident at once, against two at
-// 4 per chunk and 204 registers); a split list whose waves' task counts are
-// not a multiple of 4 takes one block per chunk (down_launch_nt).
+// and 1 where it is not (several tokens: a launch of a thousand blocks then
+// stays resident at once, which at 4 per chunk and 204 registers took two
+// rounds; 2 per chunk measured 1 % slower at eight tokens); a split list whose
+// waves' task counts are not a multiple of 4 takes one block per chunk
+// (down_launch_nt).
 constexpr int NCH_GU = 1;
 constexpr int NCH_GU_ONE_Q40 = 2;
 constexpr int NCHD = 4;
-constexpr int NCHD_UNSPLIT = 2;
+constexpr int NCHD_UNSPLIT = 1;
 // Offset past every buffer resource's range: loads there return zeros without
 // touching memory, and an all-zero block contributes exactly 0 to a dot.
 constexpr uint32_t OOB = 0x7ffffff0u;
