@@ -19,9 +19,11 @@
 // 16-lane row already beat -- and keeps them as candidates; the candidates
 // (at most 4k) are then ranked against each other.  Every global top-k expert
 // is a candidate of its segment, and every expert that beats it is one too,
-// so the candidate ranks are the exact pick positions.  Experts are compared
-// through 64-bit keys (sel_key) whose unsigned order is the beats order, so a
-// comparison is one integer compare.  Kept groups use the same rank rule.
+// so the candidate ranks are the exact pick positions.  With E <= 64 only
+// wave 0 holds experts, so its segment ranks are already the pick positions
+// and stage 2 is skipped.  Experts are compared through 64-bit keys (sel_key)
+// whose unsigned order is the beats order, so a comparison is one integer
+// compare.  Kept groups use the same rank rule.
 //
 // The sigmoid of the f32 logit is evaluated in double and rounded once to
 // f32, so equal f32 logits always give equal scores.
@@ -244,7 +246,17 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
     ns += __popcll(m);
   }
   if (lane < 8 && ns + lane < ((ns + 7) & ~7)) sh.sk[wave][ns + lane] = 0ull;  // pad to 8
-  __syncthreads();
+  // with E <= 64 every expert is in wave 0, so its segment ranks are the pick
+  // positions: wave 0 writes the picks itself, and neither the block barrier
+  // here nor stage 2 is needed (its own LDS writes are ordered by a wave fence)
+  const bool one_wave = P.E <= 64;  // (uniform)
+  if (one_wave) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
 #pragma unroll
   for (int r = 0; r < 2; r++) {
     if (surv[r]) {
@@ -256,7 +268,15 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
         rank += (v0.x > mine) + (v0.y > mine) + (v1.x > mine) + (v1.y > mine) + (v2.x > mine) + (v2.y > mine) +
                 (v3.x > mine) + (v3.y > mine);
       }
-      if (rank < P.k) sh.ck[wave * P.k + rank] = mine;
+      if (rank < P.k) {
+        if (one_wave) {
+          const int e = (int)~(uint32_t)mine;
+          sh.pick[rank] = e;
+          sh.pp[rank] = sh.p[e];
+        } else {
+          sh.ck[wave * P.k + rank] = mine;
+        }
+      }
     }
   }
   __syncthreads();
@@ -264,7 +284,7 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
   // stage 2: rank among the candidates (4k slots; a dropped expert's key and
   // an empty slot are 0 and are never picked: k <= the kept experts)
   const int C = 4 * P.k;
-  if (tid < C) {
+  if (!one_wave && tid < C) {
     const unsigned long long mine = sh.ck[tid];
     if (mine != 0ull) {
       int rank = 0;
@@ -281,7 +301,7 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
       }
     }
   }
-  __syncthreads();
+  if (!one_wave) __syncthreads();
   if (w_out && tid < P.k) {
     float wsum = 0.f;
 #pragma unroll 8
