@@ -43,7 +43,7 @@ namespace moe {
 // waves' task counts are not a multiple of 4 takes one block per chunk
 // (down_launch_nt).
 constexpr int NCH_GU = 1;
-constexpr int NCH_GU_ONE_Q40 = 2;
+constexpr int NCH_GU_PAIR = 2;
 constexpr int NCHD = 4;
 constexpr int NCHD_UNSPLIT = 1;
 // Offset past every buffer resource's range: loads there return zeros without
@@ -452,7 +452,7 @@ static void gateup_launch_ch(const DecodeArgs &a, dim3 grid, size_t lds, hipStre
 template <int QT, int LPR, int XR>
 static void gateup_launch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   if (a.T == 1 && (QT == MOE_Q4_0 || a.k == 0))
-    gateup_launch_ch<QT, LPR, XR, NCH_GU_ONE_Q40>(a, grid, lds, st);
+    gateup_launch_ch<QT, LPR, XR, NCH_GU_PAIR>(a, grid, lds, st);
   else
     gateup_launch_ch<QT, LPR, XR, NCH_GU>(a, grid, lds, st);
 }
