@@ -43,6 +43,7 @@ SEL_CASES = {
     "groups_all_used": dict(E=128, k=8, G=8, Gu=8),
     "max": dict(E=512, k=32, G=64, Gu=7, bias=True),
     "odd_E": dict(E=97, k=5),
+    "small_E_groups": dict(E=64, k=6, G=8, Gu=3, bias=True),  # one wave holds every expert, with a group limit
 }
 
 
@@ -502,6 +503,7 @@ TIE_CASES = {
     "odd_E": dict(E=100, k=5, G=1, Gu=1, bias=False),
     "k32": dict(E=64, k=32, G=1, Gu=1, bias=False),
     "groups_small": dict(E=128, k=6, G=16, Gu=5, bias=True),  # groups of 8: the block router
+    "e64_groups": dict(E=64, k=5, G=4, Gu=2, bias=True),  # one wave holds every expert, groups of 16
 }
 
 
