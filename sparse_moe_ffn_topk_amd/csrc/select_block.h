@@ -21,7 +21,9 @@
 // is a candidate of its segment, and every expert that beats it is one too,
 // so the candidate ranks are the exact pick positions.  With E <= 64 only
 // wave 0 holds experts, so its segment ranks are already the pick positions
-// and stage 2 is skipped.  Experts are compared through 64-bit keys (sel_key)
+// and stage 2 is skipped.  With two experts a thread (E > 256) a wave's k best
+// are found instead by a bitwise search for its k-th largest score word (one
+// ballot count per bit), which costs less than ranking the many survivors.  Experts are compared through 64-bit keys (sel_key)
 // whose unsigned order is the beats order, so a comparison is one integer
 // compare.  Kept groups use the same rank rule.
 //
@@ -152,7 +154,7 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
       sh.p[e] = p;
     }
   }
-  if (tid < 4 * SEL_MAX_K) sh.ck[tid] = 0ull;
+  if (R == 1 && tid < 4 * SEL_MAX_K) sh.ck[tid] = 0ull;  // (two experts a thread: each wave clears its own slots)
 
   const int PG = P.G > 1 ? P.E / P.G : P.E;  // experts per group
   const int pg_shift = (PG & (PG - 1)) == 0 ? __builtin_ctz(PG) : -1;  // (uniform)
@@ -219,67 +221,98 @@ __device__ __forceinline__ void select_rank(const SelIn &in, const SelParams &P,
     kr[r] = real ? sel_key(sv[r], e) : 0ull;
   }
 
-  // stage 1: the k best of the wave's segment {64*wave + i + 256*r}.
-  // (a) an expert with k or more strictly larger score words in its 16-lane
-  // row has k experts beating it and is dropped; (b) the survivors' keys are
-  // compacted per wave; (c) each survivor is ranked among them.  Everything
-  // that beats a top-k expert of the segment survives (a), so the survivor
-  // ranks below k are its exact ranks in the segment.
   const int lane = tid & 63;
-  bool surv[2];
+  const bool one_wave = P.E <= 64;  // (uniform) every expert is in wave 0
+  if (R == 1) {
+    // stage 1: the k best of the wave's segment {64*wave + i + 256*r}.
+    // (a) an expert with k or more strictly larger score words in its 16-lane
+    // row has k experts beating it and is dropped; (b) the survivors' keys are
+    // compacted per wave; (c) each survivor is ranked among them.  Everything
+    // that beats a top-k expert of the segment survives (a), so the survivor
+    // ranks below k are its exact ranks in the segment.
+    bool surv[2];
 #pragma unroll
-  for (int r = 0; r < 2; r++) {
-    surv[r] = false;
-    if (r < R) {  // (uniform) every lane takes part in the row moves
-      const int above = row_count_above<15>((uint32_t)(kr[r] >> 32));
-      surv[r] = kr[r] != 0ull && above < P.k;
-    }
-  }
-  int ns = 0;
-#pragma unroll
-  for (int r = 0; r < 2; r++) {
-    const unsigned long long m = __ballot(surv[r]);
-    if (surv[r]) {
-      const int pos = ns + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      sh.sk[wave][pos] = kr[r];
-    }
-    ns += __popcll(m);
-  }
-  if (lane < 8 && ns + lane < ((ns + 7) & ~7)) sh.sk[wave][ns + lane] = 0ull;  // pad to 8
-  // with E <= 64 every expert is in wave 0, so its segment ranks are the pick
-  // positions: wave 0 writes the picks itself, and neither the block barrier
-  // here nor stage 2 is needed (its own LDS writes are ordered by a wave fence)
-  const bool one_wave = P.E <= 64;  // (uniform)
-  if (one_wave) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
-    __syncthreads();
-  }
-#pragma unroll
-  for (int r = 0; r < 2; r++) {
-    if (surv[r]) {
-      const unsigned long long mine = kr[r];
-      int rank = 0;
-      for (int c = 0; c < ns; c += 8) {  // four reads in flight per step
-        const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(&sh.sk[wave][c]);
-        const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
-        rank += (v0.x > mine) + (v0.y > mine) + (v1.x > mine) + (v1.y > mine) + (v2.x > mine) + (v2.y > mine) +
-                (v3.x > mine) + (v3.y > mine);
+    for (int r = 0; r < 2; r++) {
+      surv[r] = false;
+      if (r < R) {  // (uniform) every lane takes part in the row moves
+        const int above = row_count_above<15>((uint32_t)(kr[r] >> 32));
+        surv[r] = kr[r] != 0ull && above < P.k;
       }
-      if (rank < P.k) {
-        if (one_wave) {
-          const int e = (int)~(uint32_t)mine;
-          sh.pick[rank] = e;
-          sh.pp[rank] = sh.p[e];
-        } else {
-          sh.ck[wave * P.k + rank] = mine;
+    }
+    int ns = 0;
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      const unsigned long long m = __ballot(surv[r]);
+      if (surv[r]) {
+        const int pos = ns + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        sh.sk[wave][pos] = kr[r];
+      }
+      ns += __popcll(m);
+    }
+    if (lane < 8 && ns + lane < ((ns + 7) & ~7)) sh.sk[wave][ns + lane] = 0ull;  // pad to 8
+    // with E <= 64 every expert is in wave 0, so its segment ranks are the pick
+    // positions: wave 0 writes the picks itself, and neither the block barrier
+    // here nor stage 2 is needed (its own LDS writes are ordered by a wave fence)
+    if (one_wave) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      if (surv[r]) {
+        const unsigned long long mine = kr[r];
+        int rank = 0;
+        for (int c = 0; c < ns; c += 8) {  // four reads in flight per step
+          const ulonglong2 *q = reinterpret_cast<const ulonglong2 *>(&sh.sk[wave][c]);
+          const ulonglong2 v0 = q[0], v1 = q[1], v2 = q[2], v3 = q[3];
+          rank += (v0.x > mine) + (v0.y > mine) + (v1.x > mine) + (v1.y > mine) + (v2.x > mine) + (v2.y > mine) +
+                  (v3.x > mine) + (v3.y > mine);
+        }
+        if (rank < P.k) {
+          if (one_wave) {
+            const int e = (int)~(uint32_t)mine;
+            sh.pick[rank] = e;
+            sh.pp[rank] = sh.p[e];
+          } else {
+            sh.ck[wave * P.k + rank] = mine;
+          }
         }
       }
     }
+    __syncthreads();
+  } else {
+    // stage 1 with two experts a thread (E > 256): t = the k-th largest score
+    // word of the wave's segment (the largest t with at least k words >= t),
+    // found bit by bit from the top with ballots; the segment's k best are the
+    // keys whose word is above t and, of those equal to t, the lowest-index
+    // ones (lane order, experts tid before tid + 256).  Their keys go to the
+    // wave's k candidate slots, unranked: stage 2 ranks them.
+    const uint32_t hw0 = (uint32_t)(kr[0] >> 32), hw1 = (uint32_t)(kr[1] >> 32);
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = 31; b >= 0; b--) {
+      const uint32_t trial = t | (1u << b);
+      const int c = __popcll(__ballot(hw0 >= trial)) + __popcll(__ballot(hw1 >= trial));
+      t = c >= P.k ? trial : t;
+    }
+    const unsigned long long gt0 = __ballot(hw0 > t), gt1 = __ballot(hw1 > t);
+    const unsigned long long eq0 = __ballot(hw0 == t && kr[0] != 0ull), eq1 = __ballot(hw1 == t && kr[1] != 0ull);
+    const int m = P.k - (__popcll(gt0) + __popcll(gt1));  // ties to take, lowest index first
+    auto below = [&](unsigned long long msk) {
+      return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+    };
+    const bool sel0 = ((gt0 >> lane) & 1ull) || (((eq0 >> lane) & 1ull) && below(eq0) < m);
+    const bool sel1 = ((gt1 >> lane) & 1ull) || (((eq1 >> lane) & 1ull) && __popcll(eq0) + below(eq1) < m);
+    const unsigned long long s0 = __ballot(sel0), s1 = __ballot(sel1);
+    if (lane < P.k) sh.ck[wave * P.k + lane] = 0ull;  // (then the selected keys over them: one wave, in order)
+    if (sel0) sh.ck[wave * P.k + below(s0)] = kr[0];
+    if (sel1) sh.ck[wave * P.k + __popcll(s0) + below(s1)] = kr[1];
+    if (tid >= 4 * P.k && tid < ((4 * P.k + 7) & ~7)) sh.ck[tid] = 0ull;  // stage 2 reads in steps of 8
+    __syncthreads();
   }
-  __syncthreads();
 
   // stage 2: rank among the candidates (4k slots; a dropped expert's key and
   // an empty slot are 0 and are never picked: k <= the kept experts)
