@@ -463,17 +463,18 @@ static void down_launch_ch(const DecodeArgs &a, dim3 grid, size_t lds, hipStream
              a.down_split);
 }
 // Split task lists: NCHD blocks per chunk when a wave's task count is a
-// multiple of it (every chunk full), else one (chunks then follow each other
-// two in flight).  Measured per layer step against NCHD throughout: LFM2.5
-// (3 tasks a wave) 17.2 -> 16.3 us, with Q8_0 experts 22.6 -> 20.2, Ling (7)
-// 24.0-24.4 -> 23.8; Flint (4) keeps NCHD (one block per chunk: 14.8 against
-// 14.3).
+// multiple of it (every chunk full) in a 256-thread block, else one (chunks
+// then follow each other two in flight; 512-thread blocks always take one, so
+// that two of them fit a CU).  Measured per layer step against NCHD
+// throughout: LFM2.5 (3 tasks a wave) 17.2 -> 16.3 us, with Q8_0 experts
+// 22.6 -> 20.2, Ling (7) 24.0-24.4 -> 23.8; Flint (4) keeps NCHD (one block
+// per chunk: 14.8 against 14.3).
 template <int QT, int LPR, int XR, int NT, bool SPLIT>
 static void down_launch_nt(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   if constexpr (SPLIT) {
     const int nq = a.k * ((a.F / 32) / LPR) + (a.SF / 32) / LPR;
     const int per_wave = (nq + a.down_split - 1) / a.down_split;
-    if (per_wave % NCHD != 0) {
+    if (NT == 512 || per_wave % NCHD != 0) {
       down_launch_ch<QT, LPR, XR, NT, true, 1>(a, grid, lds, st);
       return;
     }
@@ -491,6 +492,10 @@ static void down_launch_256(const DecodeArgs &a, dim3 grid, size_t lds, hipStrea
 template <int QT, int LPR, int XR>
 static void down_launch_split(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
   down_launch_nt<QT, LPR, XR, 256, true>(a, grid, lds, st);
+}
+template <int QT, int LPR, int XR>
+static void down_launch_split512(const DecodeArgs &a, dim3 grid, size_t lds, hipStream_t st) {
+  down_launch_nt<QT, LPR, XR, 512, true>(a, grid, lds, st);
 }
 
 #define MOE_XR_SWITCH(FN, QT, LPR)                  \
@@ -578,10 +583,13 @@ static hipError_t gateup_q(const DecodeArgs &a, hipStream_t st) {
 // of two <= 4 that leaves each lane at most one register chunk of blocks, as
 // long as the launch stays within 512 blocks (two per CU: more waves and
 // shorter serial chains); beyond that, at most two chunks (more blocks would
-// each stage the act row again).  S > 1 runs 256-thread blocks.  Unsplit
-// blocks are 256 threads, or 128 where 256 would leave fewer than 256 blocks
-// (so the launch covers the 256 CUs) and the act row still stages in 16
-// float4 per thread.
+// each stage the act row again).  S > 1 runs 256-thread blocks, except that a
+// split of 4 that still leaves a wave more than two tasks becomes a split of
+// 8 in 512-thread blocks (as many blocks, each wave half the tasks: Ling 23.0-
+// 23.3 -> 22.9 us per layer step, LFM2.5 16.0-16.2 -> 15.9, dense LFM2.5
+// layers 22.0 -> 20.8).  Unsplit blocks are 256 threads, or 128 where 256
+// would leave fewer than 256 blocks (so the launch covers the 256 CUs) and the
+// act row still stages in 16 float4 per thread.
 static inline int down_split(int nq, int per_lane) {
   int S = 1;
   while (S < 4 && (nq + S - 1) / S > per_lane) S <<= 1;
@@ -598,13 +606,17 @@ static hipError_t down_q(DecodeArgs a, hipStream_t st) {
   int S = down_split(nq, NCHD);
   if (S > 1 && (size_t)((a.H + (4 / S) * (64 / lpr) - 1) / ((4 / S) * (64 / lpr))) * a.T > 512)
     S = down_split(nq, 2 * NCHD);
+  const bool split8 = S == 4 && (nq + 3) / 4 > 2;
+  if (split8) S = 8;
   auto rows_for = [&](int nt) { return (nt / 64 / S) * (64 / lpr); };
   const bool wide = S > 1 || (size_t)((a.H + rows_for(256) - 1) / rows_for(256)) * a.T >= 256 || n > 4 * 128 * 16;
-  const int nt = wide ? 256 : 128;
+  const int nt = split8 ? 512 : (wide ? 256 : 128);
   const dim3 grid((a.H + rows_for(nt) - 1) / rows_for(nt), a.T);
   const int xr = xr_for(n, nt);
   a.down_split = S;
-  if (S > 1) {
+  if (split8) {
+    MOE_LPR_SWITCH(down_launch_split512, QT)
+  } else if (S > 1) {
     MOE_LPR_SWITCH(down_launch_split, QT)
   } else if (wide) {
     MOE_LPR_SWITCH(down_launch_256, QT)
