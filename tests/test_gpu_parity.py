@@ -101,6 +101,18 @@ def test_layer_step_parity(gpu, name, composed):
     _ok(err, f"{name} composed={composed} near_ties={ties}")
 
 
+@pytest.mark.parametrize("name,T", [("ling", 5), ("ling", 40), ("lfm25", 5), ("lfm25", 40)])
+def test_layer_several_tokens_full_shapes(gpu, name, T):
+    # the Ling (512 experts in groups: each selection thread holds two experts) and LFM2.5 (64 experts: one
+    # wave holds them all) layers at several tokens: the decode prelude's selection (T = 5) and the grouped
+    # path's (T = 40), every token row against the oracle
+    wl = S.WORKLOADS[name]
+    _say("layer", name, f"T={T}")
+    w, x = _layer(wl, seed=11 + T, tokens=T)
+    err, ties = run_layer_parity(wl, to_device(w), x.cuda(), wnp=S.to_numpy(w))
+    _ok(err, f"{name} T={T} near_ties={ties}")
+
+
 def test_layer_prefill_chunk(gpu):
     # 512 tokens through one Flint-shaped layer (grouped MFMA path), every
     # token row against the oracle, and the sort of the pairs bit-exact
