@@ -25,7 +25,10 @@ synchronisations give the headline.  A second timed region of eager native
 steps measures kernel durations: the library attaches HIP start/stop events to
 every dispatch of the kernel under test, on its stream; the dominant kernel
 (gate||up + SwiGLU) gives the roofline line.  The CPU baseline times the f64
-oracle on a bounded sample.
+oracle over one whole step on one thread and on N threads at once (median of
+3 each; a token sample, scaled, where a whole step would exceed the time
+budget), and recomputes every layer from the GPU's own input for the parity
+figures.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
