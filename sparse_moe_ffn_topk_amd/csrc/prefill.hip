@@ -639,25 +639,25 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 }
 
 // Grouped gate||up, row-streaming form (Q4 blocks; K <= 64 blocks, rows a
-// multiple of 16 bytes): a block takes one 16-token tile x 256 rows of gate
-// and of up, and walks them in chunks of 16 whole rows per matrix, so every
-// chunk is one contiguous run of each matrix (the column-chunk form above
-// reads 80 bytes from each of 512 rows per chunk, a pattern that a stream
-// probe ran at 3.5 TB/s against 5.7 TB/s for these runs).  Wave w takes K
-// blocks [w KQ, (w+1) KQ): its tokens' inputs for those blocks are held as
-// MFMA A fragments (f16 hi + lo) in registers for the whole block.  The four
-// waves' partial tiles of a chunk are added in wave order (fixed:
+// multiple of 16 bytes): a block walks a run of 16-token tiles' rows of gate
+// and of up in chunks of 16 whole rows per matrix, so every chunk is one
+// contiguous run of each matrix (the column-chunk form above reads 80 bytes
+// from each of 512 rows per chunk, a pattern that a stream probe ran at
+// 3.5 TB/s against 5.7 TB/s for these runs).  Wave w takes K blocks
+// [w KQ, (w+1) KQ): its tokens' inputs for those blocks are held as MFMA A
+// fragments (f16 hi + lo) in registers while the block stays on one tile.
+// The four waves' partial tiles of a chunk are added in wave order (fixed:
 // reproducible), each wave finishing a quarter of the tile's values (SwiGLU
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
-// The grid is one-dimensional: the shared expert's tiles x row slices come
-// first, then the routed tiles x the routed row slices, so no block is
-// launched for a slice past a matrix's rows.  Within each part, work is
-// dealt to the XCDs in runs (xcd_run).  The shared part is ordered
-// slice-major, so one XCD takes every tile of a shared slice; the routed part
-// tile-major, so one XCD takes every slice of a routed tile (its token rows
-// are fetched into one L2, once) and an expert's tiles share that L2.
+// The grid is resident (two blocks per CU) and splits the sequence of (tile,
+// chunk) pairs -- the shared expert's tiles first, then the routed tiles the
+// sort produced, each tile's chunks in row order -- into equal runs, one per
+// block, so every block streams the same number of chunks and reloads its
+// inputs only where its run crosses into another tile.  The runs are dealt to
+// the XCDs in order (xcd_run): an XCD's blocks take one contiguous part of the
+// sequence, so a tile's token rows and an expert's rows are fetched into one
+// L2.
 constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
-constexpr int RS_GU_RB = 128;  // rows per block, per matrix (gate||up): more, shorter blocks balance the CUs
 constexpr int RS_KQM = 16;   // max K blocks per wave
 
 // Blocks are dealt to the chip's eight XCDs (each with its own L2) in turn:
@@ -675,6 +675,11 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   constexpr int BS = QBlock<QT>::bytes;
   constexpr int MAXDW = KQ * 4 * BS / 4;       // dwords of a row
   constexpr int PADW = MAXDW + 4;              // staged row stride (a 16-byte pad spreads the banks)
+  constexpr int nbK = 4 * KQ;
+  constexpr uint32_t rowbytes = (uint32_t)nbK * BS;
+  constexpr int ppr = (int)(rowbytes / 16u);  // 16-byte pieces per row
+  constexpr int np = 16 * ppr;                // pieces per matrix and chunk
+  constexpr int PMAX = (2 * np + 255) / 256;  // pieces per thread
   __shared__ __attribute__((aligned(16))) uint32_t bst[2][16][PADW];
   __shared__ __attribute__((aligned(16))) float red[4][2][64][4];  // [wave][gate, up][lane][element]
   // the input-sum MFMA operand of each wave, 2^-6 sum(x) of token lane % 16 over
@@ -682,227 +687,246 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) half8 amt[4][2][64];
   __shared__ int rowid[16], outid[16], rsh[16];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0, b = (int)blockIdx.x;
-  const int ns = shtiles * ((a.SF + RS_GU_RB - 1) / RS_GU_RB);
-  const bool shared = b < ns;
-  int bx, by;
-  if (shared) {
-    const int l = xcd_run(b, ns);
-    bx = a.max_routed_tiles + l % shtiles;
-    by = l / shtiles;
-  } else {
-    // routed: only the ntiles tiles the sort produced, times the F slices
-    const int nt = __builtin_amdgcn_readfirstlane(*a.ntiles);
-    const int v = nt * ((a.F + RS_GU_RB - 1) / RS_GU_RB);
-    if (b - ns >= v) return;
-    const int l = xcd_run(b - ns, v);
-    const int nsl = (a.F + RS_GU_RB - 1) / RS_GU_RB;
-    bx = l / nsl;
-    by = l % nsl;
-  }
-  int e = 0, first = 0, ntok, R;
-  const uint8_t *g0, *u0;
-  if (!shared) {
-    if (bx >= __builtin_amdgcn_readfirstlane(*a.ntiles)) return;
-    e = __builtin_amdgcn_readfirstlane(a.tiles[2 * bx]);
-    first = __builtin_amdgcn_readfirstlane(a.offsets[e] + a.tiles[2 * bx + 1]);
-    ntok = min(16, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - first);
-    R = a.F;
-    const size_t mat = (size_t)R * (a.H / 32) * BS;
-    g0 = a.w0 + (size_t)e * mat;
-    u0 = a.w1 + (size_t)e * mat;
-  } else {
-    first = 16 * (bx - a.max_routed_tiles);
-    ntok = min(16, a.T - first);
-    R = a.SF;
-    g0 = a.s0;
-    u0 = a.s1;
-  }
-  if (tid < 16) {
-    const bool ok = tid < ntok;
-    const int q = first + tid;
-    const int ar = ok ? (shared ? q : a.perm[q] / a.k) : -1;
-    rowid[tid] = ar;
-    outid[tid] = ok ? q : -1;
-    rsh[tid] = ar >= 0 ? row_shift(a.xexp[ar]) : 0;
-  }
-  const int r0 = by * RS_GU_RB;
-  if (r0 >= R) return;
-  const int K = a.H, nbK = 4 * KQ;
-  const uint32_t rowbytes = (uint32_t)nbK * BS;
-  const uint32_t mbytes = (uint32_t)((size_t)R * rowbytes);
-  const rsrc_t rg = make_rsrc(g0, mbytes), ru = make_rsrc(u0, mbytes);
+  // this block's run [c, c1) of the (tile, chunk) sequence: the shared tiles'
+  // nchS chunks each, then the nt routed tiles' nchR chunks each.  The runs
+  // are equal in cost units: a chunk counts UC, a tile's input prologue UP
+  // (its units come before the tile's chunks).  Almost every run starts inside
+  // a tile, so every block pays one prologue the units do not count, and a run
+  // that crosses into another tile is that much shorter in chunks.  (Measured
+  // per block: a prologue and its first chunk's wait about 10 us, a chunk about
+  // 4 us; runs equal in chunks left the kernel 2.5 % slower.)
+  const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0;
+  const int nchS = (a.SF + 15) / 16, nchR = (a.F + 15) / 16;
+  const int nt = a.k > 0 && a.F > 0 ? __builtin_amdgcn_readfirstlane(*a.ntiles) : 0;
+  const int CS = shtiles * nchS;
+  constexpr int UC = 4, UP = 10;
+  const int US = shtiles * (UP + UC * nchS), U = US + nt * (UP + UC * nchR);
+  const int W = (int)gridDim.x, wk = xcd_run((int)blockIdx.x, W);
+  auto chunk_of = [&](int u) {  // the number of chunks whose first unit lies below u
+    if (u < US) {
+      const int t = u / (UP + UC * nchS), o = u - t * (UP + UC * nchS);
+      return t * nchS + (max(0, o - UP) + UC - 1) / UC;
+    }
+    const int v = u - US, t = v / (UP + UC * nchR), o = v - t * (UP + UC * nchR);
+    return CS + t * nchR + (max(0, o - UP) + UC - 1) / UC;
+  };
+  const int uq = U / W, ur = U - uq * W;  // run wk: units [wk uq + min(wk, ur), ...), uq or uq + 1 of them
+  const int u0 = wk * uq + min(wk, ur), u1 = u0 + uq + (wk < ur ? 1 : 0);
+  int c = chunk_of(u0);
+  const int c1 = chunk_of(u1);
+  const int K = a.H;
   const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)K * 4u);
-  const int n = lane & 15, kq = lane >> 4;
-  __syncthreads();  // rowid
+  const int tid0 = threadIdx.x;
+  while (c < c1) {  // one pass per tile the run touches
+    // (the thread index passes through an empty asm each pass, so nothing
+    // derived from it is hoisted out of this loop and held live through the
+    // input prologue, which then spilled; its range is restated)
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    __builtin_assume(tid >= 0 && tid < 256);
+    const int lane = tid & 63, wave = tid >> 6, n = lane & 15, kq = lane >> 4;
+    const bool shared = c < CS;
+    int first, ntok, R, cc, tnch;
+    const uint8_t *g0, *u0;
+    if (shared) {
+      const int t = c / nchS;
+      cc = c - t * nchS;
+      tnch = nchS;
+      first = 16 * t;
+      ntok = min(16, a.T - first);
+      R = a.SF;
+      g0 = a.s0;
+      u0 = a.s1;
+    } else {
+      const int q = c - CS, t = q / nchR;
+      cc = q - t * nchR;
+      tnch = nchR;
+      const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * t]);
+      first = __builtin_amdgcn_readfirstlane(a.offsets[e] + a.tiles[2 * t + 1]);
+      ntok = min(16, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - first);
+      R = a.F;
+      const size_t mat = (size_t)R * (a.H / 32) * BS;
+      g0 = a.w0 + (size_t)e * mat;
+      u0 = a.w1 + (size_t)e * mat;
+    }
+    const int cend = cc + min(c1 - c, tnch - cc);  // this pass: the tile's chunks [cc, cend)
+    c += cend - cc;
+    __syncthreads();  // the previous pass's readers of rowid, outid, rsh
+    if (tid < 16) {
+      const bool ok = tid < ntok;
+      const int q = first + tid;
+      const int ar = ok ? (shared ? q : a.perm[q] / a.k) : -1;
+      rowid[tid] = ar;
+      outid[tid] = ok ? q : -1;
+      rsh[tid] = ar >= 0 ? row_shift(a.xexp[ar]) : 0;
+    }
+    const uint32_t mbytes = (uint32_t)((size_t)R * rowbytes);
+    const rsrc_t rg = make_rsrc(g0, mbytes), ru = make_rsrc(u0, mbytes);
+    __syncthreads();  // rowid
 
-  // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in slot
-  // i (the order of QStagedNat), as f16 hi + lo; the block sums of its tokens
-  // (KQ is a compile-time count, so nothing splits the unrolled loops; the
-  // loads go out in groups of 4 blocks, the next group in flight while the
-  // current one is converted)
-  half8 xh[KQ], xl[KQ];
-  {
-    const int arow = rowid[n], ash = rsh[n];
-    float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // this lane's A operand of the input-sum MFMA
-    u32x4 v0[2][4], v1[2][4];
-    auto load_group = [&](int g, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
+    // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in slot
+    // i (the order of QStagedNat), as f16 hi + lo; the block sums of its tokens
+    // (KQ is a compile-time count, so nothing splits the unrolled loops; the
+    // loads go out in groups of 4 blocks, the next group in flight while the
+    // current one is converted)
+    half8 xh[KQ], xl[KQ];
+    {
+      const int arow = rowid[n], ash = rsh[n];
+      float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // this lane's A operand of the input-sum MFMA
+      u32x4 v0[2][4], v1[2][4];
+      auto load_group = [&](int g, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const uint32_t k0 = (uint32_t)((wave * KQ + 4 * g + jj) * 32 + 8 * kq);
-        const uint32_t off = arow >= 0 ? ((uint32_t)arow * (uint32_t)K + k0) * 4u : 0x7ffffff0u;
-        a0[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-        a1[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(arow >= 0 ? off + 16u : off), 0, 0);
+        for (int jj = 0; jj < 4; jj++) {
+          const uint32_t k0 = (uint32_t)((wave * KQ + 4 * g + jj) * 32 + 8 * kq);
+          const uint32_t off = arow >= 0 ? ((uint32_t)arow * (uint32_t)K + k0) * 4u : 0x7ffffff0u;
+          a0[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+          a1[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(arow >= 0 ? off + 16u : off), 0, 0);
+        }
+      };
+      load_group(0, v0[0], v1[0]);
+#pragma unroll
+      for (int g = 0; g < KQ / 4; g++) {
+        if (g + 1 < KQ / 4) load_group(g + 1, v0[(g + 1) & 1], v1[(g + 1) & 1]);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = 4 * g + jj;
+          float xv[8];
+          const u32x4 a0 = v0[g & 1][jj], a1 = v1[g & 1][jj];
+          xv[0] = __uint_as_float(a0.x); xv[1] = __uint_as_float(a0.y); xv[2] = __uint_as_float(a0.z); xv[3] = __uint_as_float(a0.w);
+          xv[4] = __uint_as_float(a1.x); xv[5] = __uint_as_float(a1.y); xv[6] = __uint_as_float(a1.z); xv[7] = __uint_as_float(a1.w);
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; i++) {
+            const float v = __builtin_ldexpf(xv[i], ash);
+            const _Float16 h = (_Float16)v;
+            xh[j][i] = h;
+            xl[j][i] = (_Float16)(v - (float)h);
+            sum += v;
+          }
+          sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
+          sum += __shfl_xor(sum, 32, 64);
+          if ((j >> 3) == kq) am[j & 7] = sum;
+        }
+      }
+      // |sum| < 32 * 2^15 (the row shift puts |x| below 2^15): 2^-6 sum fits f16;
+      // hi + lo carry 22 of its bits
+      half8 ah, al;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float v = __builtin_ldexpf(am[i], -6);
+        const _Float16 h = (_Float16)v;
+        ah[i] = h;
+        al[i] = (_Float16)(v - (float)h);
+      }
+      amt[wave][0][lane] = ah;
+      amt[wave][1][lane] = al;
+    }
+
+    // staged chunk ch: 16 rows of gate (m = 0) and of up (m = 1), row i at bst[m][i]
+    u32x4 breg[PMAX];
+    auto issue = [&](int ch) {
+#pragma unroll
+      for (int i = 0; i < PMAX; i++) {
+        const int q = tid + 256 * i, m = q >= np, qq = q - m * np;  // (q < 2 np)
+        const uint32_t off = (q < 2 * np && 16 * ch + qq / ppr < R)
+                                 ? (uint32_t)(16 * ch) * rowbytes + 16u * (uint32_t)qq
+                                 : 0x7ffffff0u;
+        breg[i] = __builtin_amdgcn_raw_buffer_load_b128(m ? ru : rg, (int)off, 0, 0);
       }
     };
-    load_group(0, v0[0], v1[0]);
+    auto stage = [&]() {
 #pragma unroll
-    for (int g = 0; g < KQ / 4; g++) {
-      if (g + 1 < KQ / 4) load_group(g + 1, v0[(g + 1) & 1], v1[(g + 1) & 1]);
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int j = 4 * g + jj;
-        float xv[8];
-        const u32x4 a0 = v0[g & 1][jj], a1 = v1[g & 1][jj];
-        xv[0] = __uint_as_float(a0.x); xv[1] = __uint_as_float(a0.y); xv[2] = __uint_as_float(a0.z); xv[3] = __uint_as_float(a0.w);
-        xv[4] = __uint_as_float(a1.x); xv[5] = __uint_as_float(a1.y); xv[6] = __uint_as_float(a1.z); xv[7] = __uint_as_float(a1.w);
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-          const float v = __builtin_ldexpf(xv[i], ash);
-          const _Float16 h = (_Float16)v;
-          xh[j][i] = h;
-          xl[j][i] = (_Float16)(v - (float)h);
-          sum += v;
+      for (int i = 0; i < PMAX; i++) {
+        const int q = tid + 256 * i, m = q >= np, qq = q - m * np;
+        if (q < 2 * np) {
+          const int row = qq / ppr, pc = qq - row * ppr;
+          *reinterpret_cast<u32x4 *>(&bst[m][row][4 * pc]) = breg[i];
         }
-        sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
-        sum += __shfl_xor(sum, 32, 64);
-        if ((j >> 3) == kq) am[j & 7] = sum;
       }
-    }
-    // |sum| < 32 * 2^15 (the row shift puts |x| below 2^15): 2^-6 sum fits f16;
-    // hi + lo carry 22 of its bits
-    half8 ah, al;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const float v = __builtin_ldexpf(am[i], -6);
-      const _Float16 h = (_Float16)v;
-      ah[i] = h;
-      al[i] = (_Float16)(v - (float)h);
-    }
-    amt[wave][0][lane] = ah;
-    amt[wave][1][lane] = al;
-  }
+    };
 
-  // staged chunk: 16 rows of gate (m = 0) and of up (m = 1), row i at bst[m][i]
-  constexpr int PMAX = (2 * 16 * (KQ * 4 * BS / 4) / 4 + 255) / 256;  // 16-byte pieces per thread
-  const int ppr = (int)(rowbytes / 16u);           // pieces per row
-  const int np = 16 * ppr;                          // pieces per matrix and chunk
-  u32x4 breg[PMAX];
-  auto issue = [&](int c) {
+    int emax = 0;  // largest exponent of the act values this lane writes (one token slot, every chunk)
+    issue(cc);
+    for (int ch = cc; ch < cend; ch++) {
+      stage();
+      __syncthreads();
+      if (ch + 1 < cend) issue(ch + 1);
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // B operand of the input-sum MFMA, per matrix: the blocks' f16 factors (m,
+      // or d for Q4_0) of row n, blocks 8 (kq & 1) + i of the wave's K range
+      // (lanes kq >= 2 meet zeros in A; two named vectors, not an array, which
+      // was placed in LDS)
+      u32x4 P0 = {0u, 0u, 0u, 0u}, P1 = P0;
+      uint32_t fprev0 = 0u, fprev1 = 0u;
+      const bool upper = (kq & 1) != 0;
 #pragma unroll
-    for (int i = 0; i < PMAX; i++) {
-      const int q = tid + 256 * i, m = q >= np, qq = q - m * np;  // (q < 2 np)
-      const uint32_t off = (q < 2 * np && r0 + 16 * c + qq / ppr < R)
-                               ? (uint32_t)(r0 + 16 * c) * rowbytes + 16u * (uint32_t)qq
-                               : 0x7ffffff0u;
-      breg[i] = __builtin_amdgcn_raw_buffer_load_b128(m ? ru : rg, (int)off, 0, 0);
-    }
-  };
-  auto stage = [&]() {
+      for (int j = 0; j < KQ; j++) {
+        const int jb = wave * KQ + j;
 #pragma unroll
-    for (int i = 0; i < PMAX; i++) {
-      const int q = tid + 256 * i, m = q >= np, qq = q - m * np;
-      if (q < 2 * np) {
-        const int row = qq / ppr, pc = qq - row * ppr;
-        *reinterpret_cast<u32x4 *>(&bst[m][row][4 * pc]) = breg[i];
-      }
-    }
-  };
-
-  const int nch = min(RS_GU_RB, R - r0 + 15) / 16;
-  int emax = 0;  // largest exponent of the act values this lane writes (one token slot, every chunk)
-  issue(0);
-  for (int c = 0; c < nch; c++) {
-    stage();
-    __syncthreads();
-    if (c + 1 < nch) issue(c + 1);
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    // B operand of the input-sum MFMA, per matrix: the blocks' f16 factors (m,
-    // or d for Q4_0) of row n, blocks 8 (kq & 1) + i of the wave's K range
-    // (lanes kq >= 2 meet zeros in A; two named vectors, not an array, which
-    // was placed in LDS)
-    u32x4 P0 = {0u, 0u, 0u, 0u}, P1 = P0;
-    uint32_t fprev0 = 0u, fprev1 = 0u;
-    const bool upper = (kq & 1) != 0;
+        for (int m = 0; m < 2; m++) {
+          float d;
+          const half8 q = QStagedNat<QT>::frag(&bst[m][n][0], jb, kq, d);
+          const uint32_t fw = QFactor<QT>::word(&bst[m][n][0], jb);
+          uint32_t &fprev = m ? fprev1 : fprev0;
+          u32x4 &Pv = m ? P1 : P0;
+          const bool mine = ((j >> 3) != 0) == upper;  // (j >> 3: compile time)
+          if (j & 1) Pv[(j & 7) >> 1] = mine ? QFactor<QT>::pair(fw, fprev) : Pv[(j & 7) >> 1];
+          fprev = fw;
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[j], q, z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[j], q, z, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < KQ; j++) {
-      const int jb = wave * KQ + j;
-#pragma unroll
-      for (int m = 0; m < 2; m++) {
-        float d;
-        const half8 q = QStagedNat<QT>::frag(&bst[m][n][0], jb, kq, d);
-        const uint32_t fw = QFactor<QT>::word(&bst[m][n][0], jb);
-        uint32_t &fprev = m ? fprev1 : fprev0;
-        u32x4 &Pv = m ? P1 : P0;
-        const bool mine = ((j >> 3) != 0) == upper;  // (j >> 3: compile time)
-        if (j & 1) Pv[(j & 7) >> 1] = mine ? QFactor<QT>::pair(fw, fprev) : Pv[(j & 7) >> 1];
-        fprev = fw;
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh[j], q, z, 0, 0, 0);
-        z = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl[j], q, z, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; i++) acc[m][i] = __builtin_fmaf(d, z[i], acc[m][i]);
-      }
-    }
-    {
-      // + the input-sum term sum_j f_j sum(x)_j on the matrix cores: acc is
-      // scaled by 1/S (exact: S = 2^6, or -2^9 for Q4_0's -8 d), the two MFMAs
-      // add 2^-6 sum(x) (hi, lo) times the factors, and the result is scaled back
-      constexpr float S = QT == MOE_Q4_1 ? 64.0f : -512.0f;
-      const half8 ah = amt[wave][0][lane], al = amt[wave][1][lane];
-#pragma unroll
-      for (int m = 0; m < 2; m++) {
-        const half8 bq = __builtin_bit_cast(half8, m ? P1 : P0);
-        f32x4 t = acc[m] * (1.0f / S);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
-        acc[m] = t * S;
-      }
-    }
-    *reinterpret_cast<f32x4 *>(red[wave][0][lane]) = acc[0];
-    *reinterpret_cast<f32x4 *>(red[wave][1][lane]) = acc[1];
-    __syncthreads();
-    {
-      // wave w finishes element w of every lane's tile values: D[token 4 (l/16) + w][row r0 + 16 c + l%16],
-      // the waves' partials added in order 0..3
-      // (the tile values are scaled by 2^rsh[token]: scaled back first)
-      const int l = lane, i = wave, slot = 4 * (l >> 4) + i;
-      const int sh = rsh[slot];
-      const float g = __builtin_ldexpf(((red[0][0][l][i] + red[1][0][l][i]) + red[2][0][l][i]) + red[3][0][l][i], -sh);
-      const float u = __builtin_ldexpf(((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i], -sh);
-      const int row = r0 + 16 * c + (l & 15);
-      const int o = outid[slot];
-      if (o >= 0 && row < R) {
-        const float L = shared ? a.lim_sh : a.lim;
-        float sg = g / (1.0f + __expf(-g)), uu = u;
-        if (L > 0.f) {
-          uu = fminf(fmaxf(uu, -L), L);
-          sg = fminf(sg, L);
+          for (int i = 0; i < 4; i++) acc[m][i] = __builtin_fmaf(d, z[i], acc[m][i]);
         }
-        const float v = sg * uu;
-        (shared ? a.out_sh : a.out)[(size_t)o * R + row] = v;
-        emax = max(emax, bexp(v));
+      }
+      {
+        // + the input-sum term sum_j f_j sum(x)_j on the matrix cores: acc is
+        // scaled by 1/S (exact: S = 2^6, or -2^9 for Q4_0's -8 d), the two MFMAs
+        // add 2^-6 sum(x) (hi, lo) times the factors, and the result is scaled back
+        constexpr float S = QT == MOE_Q4_1 ? 64.0f : -512.0f;
+        const half8 ah = amt[wave][0][lane], al = amt[wave][1][lane];
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+          const half8 bq = __builtin_bit_cast(half8, m ? P1 : P0);
+          f32x4 t = acc[m] * (1.0f / S);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bq, t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bq, t, 0, 0, 0);
+          acc[m] = t * S;
+        }
+      }
+      *reinterpret_cast<f32x4 *>(red[wave][0][lane]) = acc[0];
+      *reinterpret_cast<f32x4 *>(red[wave][1][lane]) = acc[1];
+      __syncthreads();
+      {
+        // wave w finishes element w of every lane's tile values: D[token 4 (l/16) + w][row 16 ch + l%16],
+        // the waves' partials added in order 0..3
+        // (the tile values are scaled by 2^rsh[token]: scaled back first)
+        const int l = lane, i = wave, slot = 4 * (l >> 4) + i;
+        const int sh = rsh[slot];
+        const float g = __builtin_ldexpf(((red[0][0][l][i] + red[1][0][l][i]) + red[2][0][l][i]) + red[3][0][l][i], -sh);
+        const float u = __builtin_ldexpf(((red[0][1][l][i] + red[1][1][l][i]) + red[2][1][l][i]) + red[3][1][l][i], -sh);
+        const int row = 16 * ch + (l & 15);
+        const int o = outid[slot];
+        if (o >= 0 && row < R) {
+          const float L = shared ? a.lim_sh : a.lim;
+          float sg = g / (1.0f + __expf(-g)), uu = u;
+          if (L > 0.f) {
+            uu = fminf(fmaxf(uu, -L), L);
+            sg = fminf(sg, L);
+          }
+          const float v = sg * uu;
+          (shared ? a.out_sh : a.out)[(size_t)o * R + row] = v;
+          emax = max(emax, bexp(v));
+        }
       }
     }
-  }
-  // the act row's exponent: lane l served token slot 4 (l / 16) + wave in
-  // every chunk; the 16 lanes of l / 16 share it
+    // the act row's exponent: lane l served token slot 4 (l / 16) + wave in
+    // every chunk; the 16 lanes of l / 16 share it
 #pragma unroll
-  for (int d = 8; d >= 1; d >>= 1) emax = max(emax, __shfl_xor(emax, d, 64));
-  const int o = outid[4 * (lane >> 4) + wave];
-  if ((lane & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, emax);
+    for (int d = 8; d >= 1; d >>= 1) emax = max(emax, __shfl_xor(emax, d, 64));
+    const int o = outid[4 * (lane >> 4) + wave];
+    if ((lane & 15) == 0 && o >= 0) atomicMax(shared ? a.aexp + (size_t)a.T * a.k + o : a.aexp + o, emax);
+  }
 }
 
 // N u32x4 registers indexed by a compile-time tile number (named members:
@@ -1142,7 +1166,10 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
 // their longer blocks start first and overlap the routed ones (K = F, KQF
 // blocks per wave, RS_RB rows each) that follow.  KQF or KQS is 0 where the
 // layer has no routed or no shared expert.  Each part is dealt to the XCDs
-// in runs as in k_group_gateup_rows (shared slice-major, routed tile-major).
+// in runs (xcd_run): the shared part slice-major, so one XCD reads a shared
+// slice for every tile; the routed part tile-major, so one XCD takes every
+// slice of a routed tile (its act rows are fetched into one L2, once) and an
+// expert's tiles share that L2.
 template <int QT, int KQF, int KQS>
 __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles, int rbs) {
   constexpr size_t lf = KQF > 0 ? DownRowsLds<QT, KQF>::bytes : 0, ls = KQS > 0 ? DownRowsLds<QT, KQS>::bytes : 0;
@@ -1228,6 +1255,18 @@ static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, i
   }
 }
 
+// Compute units of the current device, looked up once per device.
+static int cu_count() {
+  static int counts[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] <= 0) {
+    int n = 0;
+    counts[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return counts[dev];
+}
+
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
   hipError_t err;
@@ -1282,9 +1321,11 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     const int nbH = p.H / 32;
     // row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks (whole 16-byte pieces)
     const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
-    if (rowform)  // (shared tiles x slices, then routed tiles x slices)
-      grid = dim3(shtiles * ((p.SF + RS_GU_RB - 1) / RS_GU_RB) +
-                  (k > 0 && p.F > 0 ? g.max_routed_tiles * ((p.F + RS_GU_RB - 1) / RS_GU_RB) : 0));
+    if (rowform) {  // resident blocks (two per CU), or one per chunk where there are fewer chunks
+      const long long cmax = (long long)shtiles * ((p.SF + 15) / 16) +
+                             (k > 0 && p.F > 0 ? (long long)g.max_routed_tiles * ((p.F + 15) / 16) : 0);
+      grid = dim3((unsigned)std::max(1LL, std::min(cmax, 2LL * cu_count())));
+    }
 #define MOE_RS_LAUNCH(QT)                                                                                \
   switch (nbH / 4) {                                                                                     \
     case 4: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 4>), grid, dim3(256), 0u, st, g); break;             \
