@@ -657,7 +657,6 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // the XCDs in order (xcd_run): an XCD's blocks take one contiguous part of the
 // sequence, so a tile's token rows and an expert's rows are fetched into one
 // L2.
-constexpr int RS_RB = 256;   // rows per block (down, routed tiles)
 constexpr int RS_KQM = 16;   // max K blocks per wave
 
 // Blocks are dealt to the chip's eight XCDs (each with its own L2) in turn:
@@ -954,12 +953,12 @@ struct DownRowsLds {
 // whole rows (about 20 KB, one contiguous run); wave w takes K blocks
 // [w KQ, (w+1) KQ) of every tile, with its tokens' act rows held as MFMA A
 // fragments.  The waves' partial tiles are added in wave order and weighted
-// by the pair's routing weight.  One block runs tile bx (routed tiles first,
-// then shared ones) over rows [by rb, (by + 1) rb); rb is a multiple of the
-// chunk's rows.
+// by the pair's routing weight.  One pass runs tile bx (routed tiles first,
+// then shared ones) over its chunks [cc, cend), rows [CR cc, CR cend); tid is
+// the thread's index.
 
 template <int QT, int KQ>
-__device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by, int rb, char *smem) {
+__device__ __forceinline__ void down_rows_pass(const GemmArgs &a, int bx, int cc, int cend, char *smem, int tid) {
   static_assert(KQ <= RS_KQM, "K blocks per wave");
   constexpr int BS = QBlock<QT>::bytes;
   constexpr int TPC = DownRowsLds<QT, KQ>::TPC;  // 16-row tiles per chunk
@@ -978,13 +977,12 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
   int *rsh = rowid + 48;
   static_assert(DownRowsLds<QT, KQ>::bst % 16 == 0 && DownRowsLds<QT, KQ>::red % 16 == 0, "alignment");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const bool shared = bx >= a.max_routed_tiles;
   int e = 0, first = 0, ntok, K;
   const int R = a.H;
   const uint8_t *m0p;
   if (!shared) {
-    if (bx >= __builtin_amdgcn_readfirstlane(*a.ntiles)) return;
     e = __builtin_amdgcn_readfirstlane(a.tiles[2 * bx]);
     first = __builtin_amdgcn_readfirstlane(a.offsets[e] + a.tiles[2 * bx + 1]);
     ntok = min(16, __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - first);
@@ -996,6 +994,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     K = a.SF;
     m0p = a.s0;
   }
+  __syncthreads();  // the previous pass's readers of this LDS (its parts may lie elsewhere)
   if (tid < 16) {
     const bool ok = tid < ntok;
     const int q = first + tid;
@@ -1004,8 +1003,6 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     outw[tid] = ok && !shared ? a.wts[a.perm[q]] : 1.f;
     rsh[tid] = ok ? row_shift((shared ? a.aexp + (size_t)a.T * a.k : a.aexp)[q]) : 0;
   }
-  const int r0 = by * rb;
-  if (r0 >= R) return;
   const uint32_t rowbytes = (uint32_t)(4 * KQ) * BS;
   const rsrc_t rw = make_rsrc(m0p, (uint32_t)((size_t)R * rowbytes));
   const float *arows = shared ? a.act_sh : a.act;
@@ -1074,8 +1071,8 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
 #pragma unroll
     for (int i = 0; i < PMAX; i++) {
       const int q = tid + 256 * i;
-      const uint32_t off = (q < CR * PPR && r0 + CR * c + q / PPR < R)
-                               ? (uint32_t)(r0 + CR * c) * rowbytes + 16u * (uint32_t)q
+      const uint32_t off = (q < CR * PPR && CR * c + q / PPR < R)
+                               ? (uint32_t)(CR * c) * rowbytes + 16u * (uint32_t)q
                                : 0x7ffffff0u;
       breg[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0);
     }
@@ -1091,12 +1088,11 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     }
   };
 
-  const int nch = (min(rb, R - r0) + CR - 1) / CR;
-  issue(0);
-  for (int c = 0; c < nch; c++) {
+  issue(cc);
+  for (int c = cc; c < cend; c++) {
     stage();
     __syncthreads();
-    if (c + 1 < nch) issue(c + 1);
+    if (c + 1 < cend) issue(c + 1);
     f32x4 acc[TPC];
 #pragma unroll
     for (int t = 0; t < TPC; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1146,7 +1142,7 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
     for (int t = 0; t < TPC; t++) *reinterpret_cast<f32x4 *>(red[wave][t][lane]) = acc[t];
     __syncthreads();
     {
-      // wave w finishes element w: D[token 4 (l/16) + w][row r0 + CR c + 16 t + l%16], waves added in order
+      // wave w finishes element w: D[token 4 (l/16) + w][row CR c + 16 t + l%16], waves added in order
       const int l = lane, i = wave;
       const int slot = 4 * (l >> 4) + i, o = outid[slot], sh = rsh[slot];
       const float wgt = outw[slot];
@@ -1154,42 +1150,62 @@ __device__ __forceinline__ void down_rows_tile(const GemmArgs &a, int bx, int by
 #pragma unroll
       for (int t = 0; t < TPC; t++) {
         const float v = __builtin_ldexpf(((red[0][t][l][i] + red[1][t][l][i]) + red[2][t][l][i]) + red[3][t][l][i], -sh);
-        const int row = r0 + CR * c + 16 * t + (l & 15);
+        const int row = CR * c + 16 * t + (l & 15);
         if (o >= 0 && row < R) dst[(size_t)o * R + row] = wgt * v;
       }
     }
   }
 }
 
-// Grouped down, both kinds of tile in one launch: the first ns blocks take
-// the shared tiles (K = SF, KQS blocks per wave, rbs rows each), so that
-// their longer blocks start first and overlap the routed ones (K = F, KQF
-// blocks per wave, RS_RB rows each) that follow.  KQF or KQS is 0 where the
-// layer has no routed or no shared expert.  Each part is dealt to the XCDs
-// in runs (xcd_run): the shared part slice-major, so one XCD reads a shared
-// slice for every tile; the routed part tile-major, so one XCD takes every
-// slice of a routed tile (its act rows are fetched into one L2, once) and an
-// expert's tiles share that L2.
+// Grouped down, both kinds of tile in one launch: K = SF for the shared
+// tiles (KQS blocks per wave), K = F for the routed ones (KQF); KQF or KQS is 0
+// where the layer has no routed or no shared expert.  As in
+// k_group_gateup_rows the grid is resident and splits the sequence of (tile,
+// chunk) pairs -- the shared tiles first, then the routed tiles the sort
+// produced -- into runs equal in cost units (a chunk UC, a tile's act prologue
+// UP), dealt to the XCDs in order (xcd_run), so a tile's act rows and an
+// expert's rows are fetched into one L2.  A chunk of either kind is about
+// 20 KB of weights and the same MFMA work (TPC 16-row tiles of K / 32 blocks).
 template <int QT, int KQF, int KQS>
-__global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles, int rbs) {
+__global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shtiles) {
   constexpr size_t lf = KQF > 0 ? DownRowsLds<QT, KQF>::bytes : 0, ls = KQS > 0 ? DownRowsLds<QT, KQS>::bytes : 0;
   __shared__ __attribute__((aligned(16))) char smem[lf > ls ? lf : (ls > 0 ? ls : 16)];  // one tile's LDS, either kind
-  const int b = (int)blockIdx.x;
-  const int ns = KQS > 0 ? shtiles * ((a.H + rbs - 1) / rbs) : 0;
-  if (b < ns) {
-    if constexpr (KQS > 0) {
-      const int l = xcd_run(b, ns);
-      down_rows_tile<QT, KQS>(a, a.max_routed_tiles + l % shtiles, l / shtiles, rbs, smem);
+  constexpr int CRS = KQS > 0 ? 16 * DownRowsLds<QT, KQS>::TPC : 16;  // rows per chunk, shared tiles
+  constexpr int CRF = KQF > 0 ? 16 * DownRowsLds<QT, KQF>::TPC : 16;  // rows per chunk, routed tiles
+  constexpr int UC = 4, UP = 6;
+  const int nchS = (a.H + CRS - 1) / CRS, nchR = (a.H + CRF - 1) / CRF;
+  const int nts = KQS > 0 ? shtiles : 0;
+  const int nt = KQF > 0 ? __builtin_amdgcn_readfirstlane(*a.ntiles) : 0;
+  const int CS = nts * nchS;
+  const int US = nts * (UP + UC * nchS), U = US + nt * (UP + UC * nchR);
+  const int W = (int)gridDim.x, wk = xcd_run((int)blockIdx.x, W);
+  auto chunk_of = [&](int u) {  // the number of chunks whose first unit lies below u
+    if (u < US) {
+      const int t = u / (UP + UC * nchS), o = u - t * (UP + UC * nchS);
+      return t * nchS + (max(0, o - UP) + UC - 1) / UC;
     }
-  } else {
-    if constexpr (KQF > 0) {
-      // routed: only the ntiles tiles the sort produced, times the H slices
-      const int nt = __builtin_amdgcn_readfirstlane(*a.ntiles);
-      const int v = nt * ((a.H + RS_RB - 1) / RS_RB);
-      if (b - ns >= v) return;
-      const int l = xcd_run(b - ns, v);
-      const int nsl = (a.H + RS_RB - 1) / RS_RB;
-      down_rows_tile<QT, KQF>(a, l / nsl, l % nsl, RS_RB, smem);
+    const int v = u - US, t = v / (UP + UC * nchR), o = v - t * (UP + UC * nchR);
+    return CS + t * nchR + (max(0, o - UP) + UC - 1) / UC;
+  };
+  const int uq = U / W, ur = U - uq * W;
+  const int u0 = wk * uq + min(wk, ur), u1 = u0 + uq + (wk < ur ? 1 : 0);
+  int c = chunk_of(u0);
+  const int c1 = chunk_of(u1);
+  const int tid0 = threadIdx.x;
+  while (c < c1) {  // one pass per tile the run touches
+    // (the thread index passes through an empty asm each pass, as in
+    // k_group_gateup_rows, so nothing derived from it is hoisted out of this loop)
+    int tid = tid0;
+    asm volatile("" : "+v"(tid));
+    __builtin_assume(tid >= 0 && tid < 256);
+    if (c < CS) {
+      const int t = c / nchS, cc = c - t * nchS, cend = cc + min(c1 - c, nchS - cc);
+      c += cend - cc;
+      if constexpr (KQS > 0) down_rows_pass<QT, KQS>(a, a.max_routed_tiles + t, cc, cend, smem, tid);
+    } else {
+      const int q = c - CS, t = q / nchR, cc = q - t * nchR, cend = cc + min(c1 - c, nchR - cc);
+      c += cend - cc;
+      if constexpr (KQF > 0) down_rows_pass<QT, KQF>(a, t, cc, cend, smem, tid);
     }
   }
 }
@@ -1231,30 +1247,6 @@ size_t prefill_sort_lds_bytes(int T, int E) { return (size_t)E * ((T + 31) / 32)
 // The sort stages the ids in LDS while the whole stays within 56 KB.
 static bool sort_stages_ids(int T, int k, int E) { return prefill_sort_lds_bytes(T, E) + (size_t)T * k * 4 <= 56 * 1024; }
 
-template <int QT, int KQF>
-static void launch_down_rows_s(int kqs, const GemmArgs &g, int shtiles, int rbs, int nblk, hipStream_t st) {
-  switch (kqs) {
-    case 0: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 0>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
-    case 4: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 4>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
-    case 8: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 8>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
-    case 12: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 12>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
-    default: MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, 16>), dim3(nblk), dim3(256), 0u, st, g, shtiles, rbs); break;
-  }
-}
-
-// K blocks per wave of the routed (kqf) and shared (kqs) down matrices: 0
-// (none), 4, 8, 12 or 16.
-template <int QT>
-static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, int rbs, int nblk, hipStream_t st) {
-  switch (kqf) {
-    case 0: launch_down_rows_s<QT, 0>(kqs, g, shtiles, rbs, nblk, st); break;
-    case 4: launch_down_rows_s<QT, 4>(kqs, g, shtiles, rbs, nblk, st); break;
-    case 8: launch_down_rows_s<QT, 8>(kqs, g, shtiles, rbs, nblk, st); break;
-    case 12: launch_down_rows_s<QT, 12>(kqs, g, shtiles, rbs, nblk, st); break;
-    default: launch_down_rows_s<QT, 16>(kqs, g, shtiles, rbs, nblk, st); break;
-  }
-}
-
 // Compute units of the current device, looked up once per device.
 static int cu_count() {
   static int counts[64];
@@ -1265,6 +1257,53 @@ static int cu_count() {
     counts[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
   }
   return counts[dev];
+}
+
+// Grid of a resident launch of a 256-thread kernel without dynamic LDS: its
+// blocks per CU (occ caches them) times the CUs, at most cap and at least 1.
+template <typename Kern>
+static unsigned resident_grid(Kern kernel, int &occ, long long cap) {
+  if (occ <= 0) {
+    int nb = 0;
+    occ = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) == hipSuccess && nb > 0 ? nb : 1;
+  }
+  return (unsigned)std::max(1LL, std::min(cap, (long long)occ * cu_count()));
+}
+
+// The down launch for routed and shared K blocks per wave KQF and KQS: one
+// block per chunk of the layer at most, else resident.
+template <int QT, int KQF, int KQS>
+static void launch_down_rows_k(const GemmArgs &g, int shtiles, hipStream_t st) {
+  static int occ = 0;
+  constexpr int crs = 16 * DownRowsLds<QT, KQS>::TPC, crf = 16 * DownRowsLds<QT, KQF>::TPC;
+  const long long cap = (KQS > 0 ? (long long)shtiles * ((g.H + crs - 1) / crs) : 0) +
+                        (KQF > 0 ? (long long)g.max_routed_tiles * ((g.H + crf - 1) / crf) : 0);
+  const unsigned grid = resident_grid(k_group_down_rows<QT, KQF, KQS>, occ, cap);
+  MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, KQS>), dim3(grid), dim3(256), 0u, st, g, shtiles);
+}
+
+template <int QT, int KQF>
+static void launch_down_rows_s(int kqs, const GemmArgs &g, int shtiles, hipStream_t st) {
+  switch (kqs) {
+    case 0: launch_down_rows_k<QT, KQF, 0>(g, shtiles, st); break;
+    case 4: launch_down_rows_k<QT, KQF, 4>(g, shtiles, st); break;
+    case 8: launch_down_rows_k<QT, KQF, 8>(g, shtiles, st); break;
+    case 12: launch_down_rows_k<QT, KQF, 12>(g, shtiles, st); break;
+    default: launch_down_rows_k<QT, KQF, 16>(g, shtiles, st); break;
+  }
+}
+
+// K blocks per wave of the routed (kqf) and shared (kqs) down matrices: 0
+// (none), 4, 8, 12 or 16.
+template <int QT>
+static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, hipStream_t st) {
+  switch (kqf) {
+    case 0: launch_down_rows_s<QT, 0>(kqs, g, shtiles, st); break;
+    case 4: launch_down_rows_s<QT, 4>(kqs, g, shtiles, st); break;
+    case 8: launch_down_rows_s<QT, 8>(kqs, g, shtiles, st); break;
+    case 12: launch_down_rows_s<QT, 12>(kqs, g, shtiles, st); break;
+    default: launch_down_rows_s<QT, 16>(kqs, g, shtiles, st); break;
+  }
 }
 
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
@@ -1321,17 +1360,21 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     const int nbH = p.H / 32;
     // row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks (whole 16-byte pieces)
     const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
-    if (rowform) {  // resident blocks (two per CU), or one per chunk where there are fewer chunks
-      const long long cmax = (long long)shtiles * ((p.SF + 15) / 16) +
-                             (k > 0 && p.F > 0 ? (long long)g.max_routed_tiles * ((p.F + 15) / 16) : 0);
-      grid = dim3((unsigned)std::max(1LL, std::min(cmax, 2LL * cu_count())));
-    }
+    // (its grid: resident blocks, or one per chunk where the layer has fewer chunks)
+    const long long cmax = (long long)shtiles * ((p.SF + 15) / 16) +
+                           (k > 0 && p.F > 0 ? (long long)g.max_routed_tiles * ((p.F + 15) / 16) : 0);
+#define MOE_RS_CASE(QT, KQ)                                                                              \
+  {                                                                                                      \
+    static int occ_ = 0;                                                                                 \
+    MOE_LAUNCH(6, (k_group_gateup_rows<QT, KQ>), dim3(resident_grid(k_group_gateup_rows<QT, KQ>, occ_, cmax)), \
+               dim3(256), 0u, st, g);                                                                    \
+  }
 #define MOE_RS_LAUNCH(QT)                                                                                \
   switch (nbH / 4) {                                                                                     \
-    case 4: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 4>), grid, dim3(256), 0u, st, g); break;             \
-    case 8: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 8>), grid, dim3(256), 0u, st, g); break;             \
-    case 12: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 12>), grid, dim3(256), 0u, st, g); break;           \
-    default: MOE_LAUNCH(6, (k_group_gateup_rows<QT, 16>), grid, dim3(256), 0u, st, g); break;           \
+    case 4: MOE_RS_CASE(QT, 4) break;                                                                    \
+    case 8: MOE_RS_CASE(QT, 8) break;                                                                    \
+    case 12: MOE_RS_CASE(QT, 12) break;                                                                  \
+    default: MOE_RS_CASE(QT, 16) break;                                                                  \
   }
     if (rowform && p.qtype == MOE_Q4_1) {
       MOE_RS_LAUNCH(MOE_Q4_1)
@@ -1344,6 +1387,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
     else
       MOE_LAUNCH(6, (k_group_gemm<MOE_Q4_0, GG_GATEUP>), grid, dim3(256), 0u, st, g);
 #undef MOE_RS_LAUNCH
+#undef MOE_RS_CASE
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // down, weighted
@@ -1356,14 +1400,12 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int nbF = k > 0 ? p.F / 32 : 0, nbS = p.SF / 32;
   auto rowable = [](int nb) { return nb % 16 == 0 && nb <= 4 * RS_KQM; };
   if (p.qtype != MOE_Q8_0 && (nbF == 0 || rowable(nbF)) && (nbS == 0 || rowable(nbS))) {
-    // row-streaming form: shared tiles (128 rows a block), then routed tiles, in one launch
-    const int rbs = 128;
-    const int nblk = (shtiles > 0 ? shtiles * ((p.H + rbs - 1) / rbs) : 0) +
-                     (nbF > 0 ? g.max_routed_tiles * ((p.H + RS_RB - 1) / RS_RB) : 0);
-    if (nblk > 0 && p.qtype == MOE_Q4_1)
-      launch_down_rows<MOE_Q4_1>(nbF / 4, nbS / 4, g, shtiles, rbs, nblk, st);
-    else if (nblk > 0)
-      launch_down_rows<MOE_Q4_0>(nbF / 4, nbS / 4, g, shtiles, rbs, nblk, st);
+    // row-streaming form: shared tiles, then routed tiles, in one resident launch
+    const bool any = shtiles > 0 || nbF > 0;
+    if (any && p.qtype == MOE_Q4_1)
+      launch_down_rows<MOE_Q4_1>(nbF / 4, nbS / 4, g, shtiles, st);
+    else if (any)
+      launch_down_rows<MOE_Q4_0>(nbF / 4, nbS / 4, g, shtiles, st);
   } else {
     dim3 grid(g.max_routed_tiles + shtiles, (p.H + 255) / 256);
     if (p.qtype == MOE_Q4_1)
