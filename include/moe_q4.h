@@ -162,8 +162,8 @@ int moe_layer_step(const moe_config *cfg, const moe_layer_weights *w, const floa
  * of MOE_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends;
  * the call allocates nothing.  A T whose moe_workspace_bytes(cfg, T) exceeds
  * it is rejected with MOE_EWORKSPACE (16 MiB covers decode at every shape
- * and the grouped path up to about 128 tokens at the Flint and LFM2.5
- * shapes, about 100 at the Ling shape).  Every call on one GPU uses that
+ * and the grouped path up to 155 tokens at the Flint shape, 156 at the
+ * LFM2.5 shape and 98 at the Ling shape).  Every call on one GPU uses that
  * GPU's one array, so calls that overlap on a GPU (other streams, other
  * threads) race and must be ordered by the caller.  No kernel needs the
  * array zeroed.  Otherwise as moe_layer_step. */
@@ -228,7 +228,8 @@ enum {
   MOE_KERNEL_GATEUP = 3,  /* gate||up GEMV + SwiGLU (decode)             */
   MOE_KERNEL_DOWN = 4,    /* down GEMV + weighted accumulate (decode)    */
   MOE_KERNEL_SORT = 5,    /* pairs grouped by expert (grouped path); the
-                             same launch takes the input rows' scales     */
+                             same launch takes the input rows' scales and
+                             their f16 hi + lo form                       */
   MOE_KERNEL_GROUP_GATEUP = 6, /* grouped gate||up MFMA GEMM + SwiGLU     */
   MOE_KERNEL_GROUP_DOWN = 7,   /* grouped down MFMA GEMM, weighted        */
   MOE_KERNEL_COMBINE = 8,      /* per-token sum into the residual         */
@@ -237,7 +238,8 @@ enum {
                                   the shared expert's gate||up for all tokens */
   MOE_KERNEL_ROW_SCALE = 11    /* grouped path of a layer without routed
                                   experts: the input rows' power-of-two
-                                  scales for the f16 MFMA operands           */
+                                  scales and f16 hi + lo form for the MFMA
+                                  operands                                  */
 };
 int moe_kernel_timer_begin(int32_t kernel, int32_t capacity);
 /* Timer mode (before moe_kernel_timer_begin; kept until changed): drain 1

@@ -44,7 +44,7 @@ size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 // uses logits/ids/wts/act; the grouped path works on chunks of at most
 // PREFILL_CHUNK tokens and adds the sort results and its act and Y rows.
 struct Layout {
-  size_t logits, ids, wts, act, xn, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, xexp, aexp, total;
+  size_t logits, ids, wts, act, xn, offsets, pos, perm, tiles, ntiles, pact, pact_sh, Y, Ysh, xexp, aexp, xhl, xsum, total;
 };
 
 Layout layout(const moe_config &c, int32_t T) {
@@ -76,8 +76,11 @@ Layout layout(const moe_config &c, int32_t T) {
     L.Ysh = take(Tc * H * 4);
     L.xexp = take(Tc * 4);
     L.aexp = take(Tc * (k + 1) * 4);
+    L.xhl = take(Tc * H * 4);          // the input rows as f16 hi + lo pairs
+    L.xsum = take(Tc * (H / 32) * 4);  // and their 32-value block sums
   } else {
     L.offsets = L.pos = L.perm = L.tiles = L.ntiles = L.pact = L.pact_sh = L.Y = L.Ysh = L.xexp = L.aexp = 0;
+    L.xhl = L.xsum = 0;
   }
   L.total = o;
   return L;
@@ -241,6 +244,8 @@ int prefill_ffn_impl(const moe_config &c, const moe_layer_weights *w, const floa
     p.resid = resid + (size_t)t0 * c.hidden;
     p.xexp = (int32_t *)(b + L.xexp);
     p.aexp = (int32_t *)(b + L.aexp);
+    p.xhl = (uint16_t *)(b + L.xhl);
+    p.xsum = (float *)(b + L.xsum);
     p.lim = c.swiglu_limit;
     p.lim_sh = c.swiglu_limit_shared;
     int rc = launched(moe::launch_prefill_ffn(p, st), "grouped expert FFN");

@@ -68,6 +68,8 @@ struct PrefillArgs {
   float *resid;            // [T][H] in/out
   float lim, lim_sh;       // SwiGLU clamp of the routed and of the shared experts (0: none)
   int32_t *xexp, *aexp;    // [T], [T*k + T]: the rows' largest f32 exponents (scales of the f16 MFMA inputs)
+  uint16_t *xhl;           // [T][H/8][16]: each octet of x, scaled by its row's power of two, as 8 f16 hi then 8 f16 lo parts
+  float *xsum;             // [T][H/32]: the scaled values' sum over each 32-value block
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st);
 size_t prefill_sort_lds_bytes(int T, int E);

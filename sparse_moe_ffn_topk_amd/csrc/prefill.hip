@@ -51,10 +51,20 @@ namespace moe {
 // Biased f32 exponent field of v.
 __device__ __forceinline__ int bexp(float v) { return (int)((__float_as_uint(v) >> 23) & 0xffu); }
 
+// The power-of-two shift that puts a row whose largest biased exponent is eb
+// in [2^14, 2^15) (2^(eb - 127) <= max < 2^(eb - 126)).
+__device__ __forceinline__ int row_shift(int eb) { return 141 - eb; }
+
 // Largest biased f32 exponent of each of nrows rows of K floats (one wave per
 // row: rows r = wpb * b + wave of block b of nb), and nzero ints zeroed.
+// Where xhl is not NULL the row is also written scaled by 2^row_shift: each
+// octet of values as its 8 f16 hi parts, then the 8 f16 lo parts (v - hi),
+// 32 bytes, and each 32-value block's sum into xsum, added in the order the
+// grouped gate||up kernel needs (each octet in order, then (octet 0 + octet 1)
+// + (octet 2 + octet 3)).
 __device__ __forceinline__ void row_exp_part(const float *__restrict__ rows, int nrows, int K, int32_t *__restrict__ eb,
-                                             int32_t *__restrict__ zero, int nzero, int b, int nb) {
+                                             int32_t *__restrict__ zero, int nzero, int b, int nb,
+                                             uint16_t *__restrict__ xhl, float *__restrict__ xsum) {
   const int nt = (int)blockDim.x, wpb = nt >> 6;
   for (int i = b * nt + (int)threadIdx.x; i < nzero; i += nb * nt) zero[i] = 0;
   const int r = b * wpb + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -68,6 +78,29 @@ __device__ __forceinline__ void row_exp_part(const float *__restrict__ rows, int
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
   if (lane == 0) eb[r] = m;
+  if (xhl == nullptr) return;
+  const int sh = row_shift(m);
+  // (K / 8 octets, a multiple of 4: the lanes that take a last, partial round
+  // hold whole blocks, so the shuffles stay within active lanes)
+  for (int o = lane; o < K / 8; o += 64) {
+    const float4 v0 = p[2 * o], v1 = p[2 * o + 1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    half8 h, l;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float s = __builtin_ldexpf(v[i], sh);
+      h[i] = (_Float16)s;
+      l[i] = (_Float16)(s - (float)h[i]);
+      sum += s;
+    }
+    half8 *dst = reinterpret_cast<half8 *>(xhl + ((size_t)r * K + 8 * (size_t)o) * 2);
+    dst[0] = h;
+    dst[1] = l;
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if ((o & 3) == 0) xsum[(size_t)r * (K / 32) + (o >> 2)] = sum;
+  }
 }
 
 // ------------------------------------------------------------------ sort --
@@ -90,16 +123,18 @@ __device__ __forceinline__ int earlier_picks(P ids, int t, int k, int j, int e) 
 
 // STAGE: the ids are first copied to LDS (after bits and pre) and read there.
 // Block 0 sorts; blocks 1.. take the T input rows' largest exponents (H floats
-// each, into xexp) and zero nzero words at aexp, as k_row_exp does.
+// each, into xexp), their f16 hi + lo form and block sums (xhl, xsum; where
+// xhl is not NULL), and zero nzero words at aexp, as k_row_exp does.
 template <bool STAGE>
 __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restrict__ gids, int T, int k, int E,
                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ pos,
                                                          int32_t *__restrict__ perm, int32_t *__restrict__ tiles,
                                                          int32_t *__restrict__ ntiles, const float *__restrict__ x,
                                                          int H, int32_t *__restrict__ xexp,
-                                                         int32_t *__restrict__ aexp, int nzero) {
+                                                         int32_t *__restrict__ aexp, int nzero,
+                                                         uint16_t *__restrict__ xhl, float *__restrict__ xsum) {
   if (blockIdx.x > 0) {
-    row_exp_part(x, T, H, xexp, aexp, nzero, (int)blockIdx.x - 1, (int)gridDim.x - 1);
+    row_exp_part(x, T, H, xexp, aexp, nzero, (int)blockIdx.x - 1, (int)gridDim.x - 1, xhl, xsum);
     return;
   }
   extern __shared__ uint32_t lds[];
@@ -258,21 +293,21 @@ struct GemmArgs {
   int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
   float lim, lim_sh;         // GATEUP: SwiGLU clamp of routed / shared experts (0: none)
   const int32_t *xexp;       // [T] largest biased f32 exponent of |x| per token (k_row_exp)
+  const uint16_t *xhl;       // [T][H/8][16]: x scaled by 2^row_shift(xexp), f16 hi + lo per octet (row-streaming form)
+  const float *xsum;         // [T][H/32]: the scaled values' block sums
   int32_t *aexp;             // [T*k] then [T]: the same for the act rows (sorted, then shared);
                              // GATEUP raises them with atomicMax, DOWN reads them
 };
 
-// The power-of-two shift that puts a row whose largest biased exponent is eb
-// in [2^14, 2^15) (2^(eb - 127) <= max < 2^(eb - 126)).
-__device__ __forceinline__ int row_shift(int eb) { return 141 - eb; }
-
 // Largest biased exponent of |x| over each of nrows rows of K floats (one
-// wave per row); the grid also zeroes nzero words at zero (the act rows'
+// wave per row), with the rows' f16 hi + lo form and block sums where xhl is
+// not NULL; the grid also zeroes nzero words at zero (the act rows'
 // exponents, raised later by atomicMax).  For a layer with no routed pairs;
 // otherwise the sort's launch does this in its blocks past the first.
 __global__ __launch_bounds__(256) void k_row_exp(const float *__restrict__ rows, int nrows, int K,
-                                                 int32_t *__restrict__ eb, int32_t *__restrict__ zero, int nzero) {
-  row_exp_part(rows, nrows, K, eb, zero, nzero, blockIdx.x, gridDim.x);
+                                                 int32_t *__restrict__ eb, int32_t *__restrict__ zero, int nzero,
+                                                 uint16_t *__restrict__ xhl, float *__restrict__ xsum) {
+  row_exp_part(rows, nrows, K, eb, zero, nzero, blockIdx.x, gridDim.x, xhl, xsum);
 }
 
 // K is walked in chunks of KB blocks.  Per chunk a block stages, in LDS, the
@@ -691,9 +726,9 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   // are equal in cost units: a chunk counts UC, a tile's input prologue UP
   // (its units come before the tile's chunks).  Almost every run starts inside
   // a tile, so every block pays one prologue the units do not count, and a run
-  // that crosses into another tile is that much shorter in chunks.  (Measured
-  // per block: a prologue and its first chunk's wait about 10 us, a chunk about
-  // 4 us; runs equal in chunks left the kernel 2.5 % slower.)
+  // that crosses into another tile is that much shorter in chunks.  (Measured:
+  // runs equal in chunks left the kernel 2.5 % slower; a prologue of 10 units
+  // beat 4 and 6.)
   const int shtiles = a.SF > 0 ? (a.T + 15) / 16 : 0;
   const int nchS = (a.SF + 15) / 16, nchR = (a.F + 15) / 16;
   const int nt = a.k > 0 && a.F > 0 ? __builtin_amdgcn_readfirstlane(*a.ntiles) : 0;
@@ -714,7 +749,8 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
   int c = chunk_of(u0);
   const int c1 = chunk_of(u1);
   const int K = a.H;
-  const rsrc_t ra = make_rsrc(a.x, (uint32_t)a.T * (uint32_t)K * 4u);
+  const rsrc_t rx = make_rsrc(a.xhl, (uint32_t)a.T * (uint32_t)K * 4u);
+  const rsrc_t rs = make_rsrc(a.xsum, (uint32_t)a.T * (uint32_t)(K / 32) * 4u);
   const int tid0 = threadIdx.x;
   while (c < c1) {  // one pass per tile the run touches
     // (the thread index passes through an empty asm each pass, so nothing
@@ -763,64 +799,6 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     const rsrc_t rg = make_rsrc(g0, mbytes), ru = make_rsrc(u0, mbytes);
     __syncthreads();  // rowid
 
-    // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in slot
-    // i (the order of QStagedNat), as f16 hi + lo; the block sums of its tokens
-    // (KQ is a compile-time count, so nothing splits the unrolled loops; the
-    // loads go out in groups of 4 blocks, the next group in flight while the
-    // current one is converted)
-    half8 xh[KQ], xl[KQ];
-    {
-      const int arow = rowid[n], ash = rsh[n];
-      float am[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // this lane's A operand of the input-sum MFMA
-      u32x4 v0[2][4], v1[2][4];
-      auto load_group = [&](int g, u32x4 (&a0)[4], u32x4 (&a1)[4]) {
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const uint32_t k0 = (uint32_t)((wave * KQ + 4 * g + jj) * 32 + 8 * kq);
-          const uint32_t off = arow >= 0 ? ((uint32_t)arow * (uint32_t)K + k0) * 4u : 0x7ffffff0u;
-          a0[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-          a1[jj] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)(arow >= 0 ? off + 16u : off), 0, 0);
-        }
-      };
-      load_group(0, v0[0], v1[0]);
-#pragma unroll
-      for (int g = 0; g < KQ / 4; g++) {
-        if (g + 1 < KQ / 4) load_group(g + 1, v0[(g + 1) & 1], v1[(g + 1) & 1]);
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int j = 4 * g + jj;
-          float xv[8];
-          const u32x4 a0 = v0[g & 1][jj], a1 = v1[g & 1][jj];
-          xv[0] = __uint_as_float(a0.x); xv[1] = __uint_as_float(a0.y); xv[2] = __uint_as_float(a0.z); xv[3] = __uint_as_float(a0.w);
-          xv[4] = __uint_as_float(a1.x); xv[5] = __uint_as_float(a1.y); xv[6] = __uint_as_float(a1.z); xv[7] = __uint_as_float(a1.w);
-          float sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; i++) {
-            const float v = __builtin_ldexpf(xv[i], ash);
-            const _Float16 h = (_Float16)v;
-            xh[j][i] = h;
-            xl[j][i] = (_Float16)(v - (float)h);
-            sum += v;
-          }
-          sum += __shfl_xor(sum, 16, 64);  // the four k-octets of token n
-          sum += __shfl_xor(sum, 32, 64);
-          if ((j >> 3) == kq) am[j & 7] = sum;
-        }
-      }
-      // |sum| < 32 * 2^15 (the row shift puts |x| below 2^15): 2^-6 sum fits f16;
-      // hi + lo carry 22 of its bits
-      half8 ah, al;
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float v = __builtin_ldexpf(am[i], -6);
-        const _Float16 h = (_Float16)v;
-        ah[i] = h;
-        al[i] = (_Float16)(v - (float)h);
-      }
-      amt[wave][0][lane] = ah;
-      amt[wave][1][lane] = al;
-    }
-
     // staged chunk ch: 16 rows of gate (m = 0) and of up (m = 1), row i at bst[m][i]
     u32x4 breg[PMAX];
     auto issue = [&](int ch) {
@@ -844,8 +822,42 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
       }
     };
 
+    // this wave's A fragments: token n, k = (wave KQ + j) 32 + 8 kq + i in slot
+    // i (the order of QStagedNat), as f16 hi + lo, loaded as the sort's launch
+    // wrote them; and the input-sum MFMA's A operand: lanes kq < 2 hold the
+    // sums of the wave's blocks 8 kq + i, i < 8 (zero past KQ, and in lanes
+    // kq >= 2), an invalid token's loads fall outside the buffer and read zero
+    half8 xh[KQ], xl[KQ];
+    {
+      const int arow = rowid[n];
+#pragma unroll
+      for (int j = 0; j < KQ; j++) {
+        const uint32_t k0 = (uint32_t)((wave * KQ + j) * 32 + 8 * kq);
+        const uint32_t off = arow >= 0 ? ((uint32_t)arow * (uint32_t)K + k0) * 4u : 0x7ffffff0u;
+        xh[j] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0));
+        xl[j] = __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(arow >= 0 ? off + 16u : off), 0, 0));
+      }
+      issue(cc);  // (after the input loads: the prologue waits for those alone)
+      const uint32_t so = ((uint32_t)arow * (uint32_t)(K / 32) + (uint32_t)(wave * KQ + 8 * kq)) * 4u;
+      const u32x4 s0 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(arow >= 0 && 8 * kq < KQ ? so : 0x7ffffff0u), 0, 0);
+      const u32x4 s1 = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(arow >= 0 && 8 * kq + 4 < KQ ? so + 16u : 0x7ffffff0u), 0, 0);
+      const float am[8] = {__uint_as_float(s0.x), __uint_as_float(s0.y), __uint_as_float(s0.z), __uint_as_float(s0.w),
+                           __uint_as_float(s1.x), __uint_as_float(s1.y), __uint_as_float(s1.z), __uint_as_float(s1.w)};
+      // |sum| < 32 * 2^15 (the row shift puts |x| below 2^15): 2^-6 sum fits f16;
+      // hi + lo carry 22 of its bits
+      half8 ah, al;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float v = __builtin_ldexpf(am[i], -6);
+        const _Float16 h = (_Float16)v;
+        ah[i] = h;
+        al[i] = (_Float16)(v - (float)h);
+      }
+      amt[wave][0][lane] = ah;
+      amt[wave][1][lane] = al;
+    }
+
     int emax = 0;  // largest exponent of the act values this lane writes (one token slot, every chunk)
-    issue(cc);
     for (int ch = cc; ch < cend; ch++) {
       stage();
       __syncthreads();
@@ -1309,21 +1321,28 @@ static void launch_down_rows(int kqf, int kqs, const GemmArgs &g, int shtiles, h
 hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   const int T = p.T, k = p.k, E = p.E;
   hipError_t err;
-  // the sort, and the rows' power-of-two scales: x now, the act rows' exponents
-  // zeroed for the gate||up epilogue (in the sort's launch, blocks past the first)
+  // gate||up in the row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks
+  // (whole 16-byte pieces); it reads x as the f16 hi + lo pairs made below
+  const int nbH = p.H / 32;
+  const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
+  uint16_t *xhl = rowform ? p.xhl : nullptr;
+  // the sort, and the rows' power-of-two scales: x now (with its f16 form),
+  // the act rows' exponents zeroed for the gate||up epilogue (in the sort's
+  // launch, blocks past the first)
   const int nzero = T * (k + 1);
   if (k > 0) {  // (a dense layer, k == 0, has no routed pairs to sort)
     const int nexp = max((T + 15) / 16, (nzero + 1023) / 1024);
     if (sort_stages_ids(T, k, E))
       MOE_LAUNCH(5, k_sort_by_expert<true>, dim3(1 + nexp), dim3(1024),
                  (uint32_t)(prefill_sort_lds_bytes(T, E) + T * k * 4), st, p.ids, T, k, E, p.offsets, p.pos, p.perm,
-                 p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero);
+                 p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero, xhl, p.xsum);
     else
       MOE_LAUNCH(5, k_sort_by_expert<false>, dim3(1 + nexp), dim3(1024), (uint32_t)prefill_sort_lds_bytes(T, E), st,
-                 p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero);
+                 p.ids, T, k, E, p.offsets, p.pos, p.perm, p.tiles, p.ntiles, p.x, p.H, p.xexp, p.aexp, nzero, xhl,
+                 p.xsum);
   } else {
     const int nblk = max((T + 3) / 4, (nzero + 255) / 256);
-    MOE_LAUNCH(11, k_row_exp, dim3(nblk), dim3(256), 0u, st, p.x, T, p.H, p.xexp, p.aexp, nzero);
+    MOE_LAUNCH(11, k_row_exp, dim3(nblk), dim3(256), 0u, st, p.x, T, p.H, p.xexp, p.aexp, nzero, xhl, p.xsum);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   GemmArgs g{};
@@ -1331,6 +1350,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   g.k = k;
   g.H = p.H;
   g.xexp = p.xexp;
+  g.xhl = p.xhl;
+  g.xsum = p.xsum;
   g.aexp = p.aexp;
   g.F = p.F;
   g.SF = p.SF;
@@ -1357,9 +1378,6 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   {
     const int rows = p.F > p.SF ? p.F : p.SF;
     dim3 grid(g.max_routed_tiles + shtiles, (rows + 255) / 256);
-    const int nbH = p.H / 32;
-    // row-streaming form: Q4 rows of 16, 32, 48 or 64 blocks (whole 16-byte pieces)
-    const bool rowform = p.qtype != MOE_Q8_0 && nbH % 16 == 0 && nbH <= 4 * RS_KQM;
     // (its grid: resident blocks, or one per chunk where the layer has fewer chunks)
     const long long cmax = (long long)shtiles * ((p.SF + 15) / 16) +
                            (k > 0 && p.F > 0 ? (long long)g.max_routed_tiles * ((p.F + 15) / 16) : 0);
