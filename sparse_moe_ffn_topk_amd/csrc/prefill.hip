@@ -1023,6 +1023,31 @@ __device__ __forceinline__ void down_rows_pass(const GemmArgs &a, int bx, int cc
   const int n = lane & 15, kq = lane >> 4;
   __syncthreads();  // rowid
 
+  // staged chunk: CR whole rows, row i at bst[i]
+  constexpr int PMAX = (CR * ROWDW / 4 + 255) / 256;
+  constexpr int PPR = ROWDW / 4;  // 16-byte pieces per row
+  u32x4 breg[PMAX];
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PMAX; i++) {
+      const int q = tid + 256 * i;
+      const uint32_t off = (q < CR * PPR && CR * c + q / PPR < R)
+                               ? (uint32_t)(CR * c) * rowbytes + 16u * (uint32_t)q
+                               : 0x7ffffff0u;
+      breg[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < PMAX; i++) {
+      const int q = tid + 256 * i;
+      if (q < CR * PPR) {
+        const int row = q / PPR, pc = q - row * PPR;
+        *reinterpret_cast<u32x4 *>(&bst[row][4 * pc]) = breg[i];
+      }
+    }
+  };
+
   // this wave's A fragments and input-sum MFMA operand (as in k_group_gateup_rows)
   half8 xh[KQ], xl[KQ];
   {
@@ -1042,6 +1067,7 @@ __device__ __forceinline__ void down_rows_pass(const GemmArgs &a, int bx, int cc
 #pragma unroll
     for (int g = 0; g < KQ / 2; g++) {
       if (g + 1 < KQ / 2) load_group(g + 1, v0[(g + 1) & 1], v1[(g + 1) & 1]);
+      if (g + 2 == KQ / 2) issue(cc);  // (after the last act loads: loads complete in order)
 #pragma unroll
       for (int jj = 0; jj < 2; jj++) {
         const int j = 2 * g + jj;
@@ -1075,32 +1101,6 @@ __device__ __forceinline__ void down_rows_pass(const GemmArgs &a, int bx, int cc
     amt[wave][1][lane] = al;
   }
 
-  // staged chunk: CR whole rows, row i at bst[i]
-  constexpr int PMAX = (CR * ROWDW / 4 + 255) / 256;
-  constexpr int PPR = ROWDW / 4;  // 16-byte pieces per row
-  u32x4 breg[PMAX];
-  auto issue = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < PMAX; i++) {
-      const int q = tid + 256 * i;
-      const uint32_t off = (q < CR * PPR && CR * c + q / PPR < R)
-                               ? (uint32_t)(CR * c) * rowbytes + 16u * (uint32_t)q
-                               : 0x7ffffff0u;
-      breg[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < PMAX; i++) {
-      const int q = tid + 256 * i;
-      if (q < CR * PPR) {
-        const int row = q / PPR, pc = q - row * PPR;
-        *reinterpret_cast<u32x4 *>(&bst[row][4 * pc]) = breg[i];
-      }
-    }
-  };
-
-  issue(cc);
   for (int c = cc; c < cend; c++) {
     stage();
     __syncthreads();
