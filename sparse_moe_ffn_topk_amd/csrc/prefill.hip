@@ -70,20 +70,11 @@ __device__ __forceinline__ void row_exp_part(const float *__restrict__ rows, int
   const int r = b * wpb + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= nrows) return;
   const float4 *p = reinterpret_cast<const float4 *>(rows + (size_t)r * K);
-  int m = 0;
-  for (int i = lane; i < K / 4; i += 64) {
-    const float4 v = p[i];
-    m = max(m, max(max(bexp(v.x), bexp(v.y)), max(bexp(v.z), bexp(v.w))));
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
-  if (lane == 0) eb[r] = m;
-  if (xhl == nullptr) return;
-  const int sh = row_shift(m);
-  // (K / 8 octets, a multiple of 4: the lanes that take a last, partial round
-  // hold whole blocks, so the shuffles stay within active lanes)
-  for (int o = lane; o < K / 8; o += 64) {
-    const float4 v0 = p[2 * o], v1 = p[2 * o + 1];
+  // octet o of the row (values 8 o .. 8 o + 7) scaled by 2^sh: its f16 hi and
+  // lo parts, and its block's sum from the four octets' lanes (K / 8 octets,
+  // a multiple of 4: the lanes that take a last, partial round hold whole
+  // blocks, so the shuffles stay within active lanes)
+  auto convert = [&](int o, int sh, float4 v0, float4 v1) {
     const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     half8 h, l;
     float sum = 0.f;
@@ -100,7 +91,44 @@ __device__ __forceinline__ void row_exp_part(const float *__restrict__ rows, int
     sum += __shfl_xor(sum, 1, 64);
     sum += __shfl_xor(sum, 2, 64);
     if ((o & 3) == 0) xsum[(size_t)r * (K / 32) + (o >> 2)] = sum;
+  };
+  constexpr int RC = 8;  // octet rounds a lane holds in registers: rows of up to 4096 values
+  if (xhl != nullptr && K <= 512 * RC) {
+    float4 v[RC][2];
+    int m = 0;
+#pragma unroll
+    for (int it = 0; it < RC; it++) {
+      const int o = lane + 64 * it;
+      if (o < K / 8) {
+        v[it][0] = p[2 * o];
+        v[it][1] = p[2 * o + 1];
+        const float4 a = v[it][0], c = v[it][1];
+        m = max(m, max(max(max(bexp(a.x), bexp(a.y)), max(bexp(a.z), bexp(a.w))),
+                       max(max(bexp(c.x), bexp(c.y)), max(bexp(c.z), bexp(c.w)))));
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
+    if (lane == 0) eb[r] = m;
+    const int sh = row_shift(m);
+#pragma unroll
+    for (int it = 0; it < RC; it++) {
+      const int o = lane + 64 * it;
+      if (o < K / 8) convert(o, sh, v[it][0], v[it][1]);
+    }
+    return;
   }
+  int m = 0;
+  for (int i = lane; i < K / 4; i += 64) {
+    const float4 v = p[i];
+    m = max(m, max(max(bexp(v.x), bexp(v.y)), max(bexp(v.z), bexp(v.w))));
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, 64));
+  if (lane == 0) eb[r] = m;
+  if (xhl == nullptr) return;
+  const int sh = row_shift(m);
+  for (int o = lane; o < K / 8; o += 64) convert(o, sh, p[2 * o], p[2 * o + 1]);
 }
 
 // ------------------------------------------------------------------ sort --
@@ -152,23 +180,59 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
   if (tid == 0) repeats = 0;
   __syncthreads();
   const int32_t *ids = STAGE ? sids : gids;
-  for (int p = tid; p < np; p += 1024) {
-    const int e = ids[p], t = p / k;
-    if (earlier_picks(ids, t, k, p - t * k, e) == 0)
-      atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
-    else
-      repeats = 1;
+  // (k <= SORT_KR: one thread per token with its ids in registers, so the
+  // duplicate checks and the ranks below need no reloads)
+  constexpr int SORT_KR = 8;
+  const bool by_token = k <= SORT_KR;
+  int te[SORT_KR];
+  if (by_token) {
+    if (tid < T) {
+#pragma unroll
+      for (int j = 0; j < SORT_KR; j++) te[j] = j < k ? ids[tid * k + j] : -1;
+      bool dup = false;
+#pragma unroll
+      for (int j = 0; j < SORT_KR; j++) {
+        bool first = true;
+#pragma unroll
+        for (int i = 0; i < j; i++) first = first && te[i] != te[j];
+        if (j < k && first) atomicOr(&bits[te[j] * W + (tid >> 5)], 1u << (tid & 31));
+        dup = dup || (j < k && !first);
+      }
+      if (dup) repeats = 1;
+    }
+  } else {
+    for (int p = tid; p < np; p += 1024) {
+      const int e = ids[p], t = p / k;
+      if (earlier_picks(ids, t, k, p - t * k, e) == 0)
+        atomicOr(&bits[e * W + (t >> 5)], 1u << (t & 31));
+      else
+        repeats = 1;
+    }
   }
   __syncthreads();
   const bool rep = repeats != 0;
   if (tid < E) {
     int c = 0;
-    for (int w = 0; w < W; w++) {
-      pre[tid * W + w] = (uint16_t)c;
-      const uint32_t b = bits[tid * W + w];
-      c += __popc(b);
-      if (rep)
-        for (uint32_t m = b; m; m &= m - 1) c += earlier_picks(ids, 32 * w + __builtin_ctz(m), k, k, tid) - 1;
+    if (!rep && W <= 16) {
+      // all of the expert's words first (pre shares the LDS array, so a load
+      // after a store could not be moved ahead of it)
+      uint32_t bw[16];
+#pragma unroll
+      for (int w = 0; w < 16; w++) bw[w] = w < W ? bits[tid * W + w] : 0u;
+#pragma unroll
+      for (int w = 0; w < 16; w++)
+        if (w < W) {
+          pre[tid * W + w] = (uint16_t)c;
+          c += __popc(bw[w]);
+        }
+    } else {
+      for (int w = 0; w < W; w++) {
+        pre[tid * W + w] = (uint16_t)c;
+        const uint32_t b = bits[tid * W + w];
+        c += __popc(b);
+        if (rep)
+          for (uint32_t m = b; m; m &= m - 1) c += earlier_picks(ids, 32 * w + __builtin_ctz(m), k, k, tid) - 1;
+      }
     }
     cnt[tid] = c;
   }
@@ -221,6 +285,22 @@ __global__ __launch_bounds__(1024) void k_sort_by_expert(const int32_t *__restri
       tiles[2 * (toff[tid] + i)] = tid;
       tiles[2 * (toff[tid] + i) + 1] = 16 * i;
     }
+  }
+  if (by_token && !rep) {
+    // no token lists an expert twice: pair (t, j) of expert e ranks after the
+    // pairs of e of the tokens before t
+    if (tid < T) {
+#pragma unroll
+      for (int j = 0; j < SORT_KR; j++)
+        if (j < k) {
+          const int e = te[j];
+          const uint32_t below = bits[e * W + (tid >> 5)] & ((1u << (tid & 31)) - 1u);
+          const int q = off[e] + pre[e * W + (tid >> 5)] + __popc(below);
+          pos[tid * k + j] = q;
+          perm[q] = tid * k + j;
+        }
+    }
+    return;
   }
   for (int p = tid; p < np; p += 1024) {
     const int e = ids[p], t = p / k, j = p - t * k;

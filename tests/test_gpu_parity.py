@@ -506,6 +506,26 @@ def test_grouped_sort_with_repeated_ids_bit_exact(gpu):
     check_sort(cfg, ws, ids.numpy(), T)
 
 
+@pytest.mark.parametrize("T,E,k", [(512, 256, 6), (300, 64, 8), (45, 8, 1), (129, 40, 12)])
+def test_grouped_sort_bit_exact(gpu, T, E, k):
+    # the grouped path's sort of caller-given ids with k distinct experts per token (one thread per token holds
+    # its ids for k <= 8; k = 12 takes the per-pair form), read back from the workspace
+    from moe_testlib import check_sort
+    moe = gpu
+    wl = S.Workload("srt", 256, E, k, 96, 0, S.Q4_1)
+    _say("sort T", T, "E", E, "k", k)
+    w, x = _layer(wl, seed=61 + T, tokens=T)
+    g = torch.Generator().manual_seed(T + E + k)
+    ids = torch.argsort(torch.rand((T, E), generator=g), dim=1)[:, :k].to(torch.int32).contiguous()
+    cfg = moe.config_for(wl)
+    ws = moe.alloc_workspace(cfg, T)
+    out = torch.zeros((T, 256), device="cuda")
+    moe.expert_ffn_q4(cfg, to_device(w), x.cuda(), ids.cuda(), torch.ones((T, k), device="cuda"), out,
+                      workspace=ws)
+    torch.cuda.synchronize()
+    check_sort(cfg, ws, ids.numpy(), T)
+
+
 # ------------------------------------------------ one-token routing, exact ties --
 
 TIE_CASES = {
