@@ -764,11 +764,12 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // The four waves' partial tiles of a chunk are added in wave order (fixed:
 // reproducible), each wave finishing a quarter of the tile's values (SwiGLU
 // and store).  Its registers (about 250 per lane) allow two blocks per CU.
-// The grid is resident (two blocks per CU) and splits the sequence of (tile,
-// chunk) pairs -- the shared expert's tiles first, then the routed tiles the
-// sort produced, each tile's chunks in row order -- into equal runs, one per
-// block, so every block streams the same number of chunks and reloads its
-// inputs only where its run crosses into another tile.  The runs are dealt to
+// The grid is resident (the kernel's occupancy, two blocks per CU, times the
+// CUs) and splits the sequence of (tile, chunk) pairs -- the shared expert's
+// tiles first, then the routed tiles the sort produced, each tile's chunks in
+// row order -- into runs of equal cost, one per block (below), so the blocks
+// finish together and each loads its inputs again only where its run crosses
+// into another tile.  The runs are dealt to
 // the XCDs in order (xcd_run): an XCD's blocks take one contiguous part of the
 // sequence, so a tile's token rows and an expert's rows are fetched into one
 // L2.
