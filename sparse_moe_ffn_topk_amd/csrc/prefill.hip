@@ -868,13 +868,13 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     const int cend = cc + min(c1 - c, tnch - cc);  // this pass: the tile's chunks [cc, cend)
     c += cend - cc;
     __syncthreads();  // the previous pass's readers of rowid, outid, rsh
+    int ar = -1;  // (threads tid < 16: token slot tid's input row)
     if (tid < 16) {
       const bool ok = tid < ntok;
       const int q = first + tid;
-      const int ar = ok ? (shared ? q : a.perm[q] / a.k) : -1;
+      ar = ok ? (shared ? q : a.perm[q] / a.k) : -1;
       rowid[tid] = ar;
       outid[tid] = ok ? q : -1;
-      rsh[tid] = ar >= 0 ? row_shift(a.xexp[ar]) : 0;
     }
     const uint32_t mbytes = (uint32_t)((size_t)R * rowbytes);
     const rsrc_t rg = make_rsrc(g0, mbytes), ru = make_rsrc(u0, mbytes);
@@ -938,6 +938,9 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
       amt[wave][1][lane] = al;
     }
 
+    // the rows' shifts, needed only from the first chunk's output on (the input
+    // pairs come scaled), so their loads leave the chain before the input loads
+    if (tid < 16) rsh[tid] = ar >= 0 ? row_shift(a.xexp[ar]) : 0;
     int emax = 0;  // largest exponent of the act values this lane writes (one token slot, every chunk)
     for (int ch = cc; ch < cend; ch++) {
       stage();
