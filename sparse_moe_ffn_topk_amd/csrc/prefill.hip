@@ -371,6 +371,7 @@ struct GemmArgs {
   float *out;                // GATEUP: sorted act; DOWN: Y [T*k][H]
   float *out_sh;             // GATEUP: act_sh; DOWN: Ysh [T][H]
   int max_routed_tiles;      // grid.x = max_routed_tiles + shared tiles
+  int runw[4];               // row-streaming GEMMs: run weights by dispatch order on the CU (run_bounds; {0}: equal)
   float lim, lim_sh;         // GATEUP: SwiGLU clamp of routed / shared experts (0: none)
   const int32_t *xexp;       // [T] largest biased f32 exponent of |x| per token (k_row_exp)
   const uint16_t *xhl;       // [T][H/8][16]: x scaled by 2^row_shift(xexp), f16 hi + lo per octet (row-streaming form)
@@ -774,6 +775,40 @@ __global__ __launch_bounds__(256) void k_group_gemm(GemmArgs a) {
 // sequence, so a tile's token rows and an expert's rows are fetched into one
 // L2.
 constexpr int RS_KQM = 16;   // max K blocks per wave
+// Run weights of the row-streaming GEMMs' resident grids, by the order in
+// which a CU's blocks were dispatched.  A per-block timing of gate||up at two
+// blocks per CU showed the first block on each CU (the grid's first half)
+// ending about 15 % before the second (its older waves issue first), which
+// then finished alone on a half-idle CU; runs weighted 20 : 16 measured best
+// (layer 192.3 -> 189.8 us; 18 : 16 and 22 : 16 gave 190.8).  The down
+// kernel, at three blocks per CU, measured best with 20 : 16 : 12 (layer
+// 193.1 -> 191.3 us; 18 : 16 : 14 gave 192.2-194.8).
+constexpr int RS_RUNW2[2] = {20, 16};
+constexpr int RS_RUNW3[3] = {20, 16, 12};
+
+// Units [u0, u1) of run wk of the W runs (W blocks in XCD runs, xcd_run) over
+// U units.  Where w[0] > 0 and the grid is resident at nw blocks per CU (W a
+// multiple of 8 nw), block i was dispatched (i / (W / nw))-th to its CU and
+// its run's length is in the proportion w of that order; otherwise the runs
+// are equal.  The bounds are exact for the ends (0 and U) and the same
+// expression for a run's end and the next run's start.
+__device__ __forceinline__ void run_bounds(int U, int W, int wk, int nw, const int (&w)[4], int &u0, int &u1) {
+  if (w[0] > 0 && nw > 0 && nw <= 4 && W % (8 * nw) == 0) {
+    const int per = W >> 3, gp = per / nw, x = wk / per, j = wk - x * per, g = j / gp, jj = j - g * gp;
+    int tot = 0, pre = 0;
+    for (int h = 0; h < nw; h++) {
+      tot += gp * w[h];
+      if (h < g) pre += gp * w[h];
+    }
+    const int p0 = x * tot + pre + jj * w[g], p1 = p0 + w[g];
+    u0 = (int)((double)U * (double)p0 / (double)(8 * tot));
+    u1 = (int)((double)U * (double)p1 / (double)(8 * tot));
+  } else {
+    const int uq = U / W, ur = U - uq * W;  // run wk: units [wk uq + min(wk, ur), ...), uq or uq + 1 of them
+    u0 = wk * uq + min(wk, ur);
+    u1 = u0 + uq + (wk < ur ? 1 : 0);
+  }
+}
 
 // Blocks are dealt to the chip's eight XCDs (each with its own L2) in turn:
 // block i runs on XCD i % 8.  For i in [0, n) this returns a work index in
@@ -825,8 +860,8 @@ __global__ __launch_bounds__(256, 2) void k_group_gateup_rows(GemmArgs a) {
     const int v = u - US, t = v / (UP + UC * nchR), o = v - t * (UP + UC * nchR);
     return CS + t * nchR + (max(0, o - UP) + UC - 1) / UC;
   };
-  const int uq = U / W, ur = U - uq * W;  // run wk: units [wk uq + min(wk, ur), ...), uq or uq + 1 of them
-  const int u0 = wk * uq + min(wk, ur), u1 = u0 + uq + (wk < ur ? 1 : 0);
+  int u0, u1;
+  run_bounds(U, W, wk, 2, a.runw, u0, u1);
   int c = chunk_of(u0);
   const int c1 = chunk_of(u1);
   const int K = a.H;
@@ -1283,8 +1318,8 @@ __global__ __launch_bounds__(256, 2) void k_group_down_rows(GemmArgs a, int shti
     const int v = u - US, t = v / (UP + UC * nchR), o = v - t * (UP + UC * nchR);
     return CS + t * nchR + (max(0, o - UP) + UC - 1) / UC;
   };
-  const int uq = U / W, ur = U - uq * W;
-  const int u0 = wk * uq + min(wk, ur), u1 = u0 + uq + (wk < ur ? 1 : 0);
+  int u0, u1;
+  run_bounds(U, W, wk, 3, a.runw, u0, u1);
   int c = chunk_of(u0);
   const int c1 = chunk_of(u1);
   const int tid0 = threadIdx.x;
@@ -1375,7 +1410,10 @@ static void launch_down_rows_k(const GemmArgs &g, int shtiles, hipStream_t st) {
   const long long cap = (KQS > 0 ? (long long)shtiles * ((g.H + crs - 1) / crs) : 0) +
                         (KQF > 0 ? (long long)g.max_routed_tiles * ((g.H + crf - 1) / crf) : 0);
   const unsigned grid = resident_grid(k_group_down_rows<QT, KQF, KQS>, occ, cap);
-  MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, KQS>), dim3(grid), dim3(256), 0u, st, g, shtiles);
+  GemmArgs gr = g;
+  if (occ == 3 && grid == 3u * (unsigned)cu_count())
+    for (int i = 0; i < 3; i++) gr.runw[i] = RS_RUNW3[i];
+  MOE_LAUNCH(7, (k_group_down_rows<QT, KQF, KQS>), dim3(grid), dim3(256), 0u, st, gr, shtiles);
 }
 
 template <int QT, int KQF>
@@ -1451,6 +1489,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
   g.max_routed_tiles = (T * k + 15) / 16 + E;
   g.lim = p.lim;
   g.lim_sh = p.lim_sh;
+  // (runw stays {0}: equal runs, unless a launch below sets its weights)
   const int shtiles = p.SF > 0 ? (T + 15) / 16 : 0;
   // gate || up
   g.w0 = p.gate_exps;
@@ -1468,8 +1507,11 @@ hipError_t launch_prefill_ffn(const PrefillArgs &p, hipStream_t st) {
 #define MOE_RS_CASE(QT, KQ)                                                                              \
   {                                                                                                      \
     static int occ_ = 0;                                                                                 \
-    MOE_LAUNCH(6, (k_group_gateup_rows<QT, KQ>), dim3(resident_grid(k_group_gateup_rows<QT, KQ>, occ_, cmax)), \
-               dim3(256), 0u, st, g);                                                                    \
+    const unsigned grid_ = resident_grid(k_group_gateup_rows<QT, KQ>, occ_, cmax);                    \
+    GemmArgs gr_ = g;                                                                                    \
+    if (occ_ == 2 && grid_ == 2u * (unsigned)cu_count())                                                 \
+      for (int i_ = 0; i_ < 2; i_++) gr_.runw[i_] = RS_RUNW2[i_];                                        \
+    MOE_LAUNCH(6, (k_group_gateup_rows<QT, KQ>), dim3(grid_), dim3(256), 0u, st, gr_);                  \
   }
 #define MOE_RS_LAUNCH(QT)                                                                                \
   switch (nbH / 4) {                                                                                     \
